@@ -1,0 +1,583 @@
+"""Pins of the CPU oracle against what the DSpark pages and the mathematics fix.
+
+These run without a GPU.  Each test checks the oracle against something other
+than itself: a value the pages print for a worked example (tests/golden/), a
+closed form, an identity of the lossless-verification proof, a library routine
+the step reduces to, or brute force on tiny inputs.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats as sst
+from scipy.special import logsumexp
+from scipy.special import softmax as sp_softmax
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            rows.setdefault(key, []).append(vals)
+    return rows
+
+
+def bf16(x):
+    """Round float64 values to bf16 and return their uint16 bit patterns."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_val(bits):
+    return torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def chi2_ok(counts, probs, alpha):
+    counts = np.asarray(counts, np.float64)
+    n = counts.sum()
+    keep = probs * n > 0
+    res = sst.chisquare(counts[keep], probs[keep] * n / probs[keep].sum())
+    return res.pvalue > alpha, res.pvalue
+
+
+# ---------------------------------------------------------------------------
+# Philox4x32-10
+# ---------------------------------------------------------------------------
+
+def test_philox_known_answers(orc):
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    assert len(lines) == 3
+    for cols in lines:
+        ints = [int(c, 16) for c in cols]
+        out = orc.philox4x32_10(ints[:4], ints[4:6])
+        assert [int(x) for x in out] == ints[6:10]
+
+
+def test_philox_matches_rocrand_header(orc, tmp_path):
+    """Independent implementation: rocRAND's open-source Philox header, compiled
+    for the host.  Checks the counter/key word order the oracle relies on."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    hdr = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+    if not os.path.exists(hdr) or not os.path.exists(hipcc):
+        pytest.skip("rocRAND header or hipcc not available")
+    src = tmp_path / "p.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include <rocrand/rocrand_philox4x32_10.h>
+struct probe : rocrand_device::philox4x32_10_engine {
+  uint4 run(uint4 c, uint2 k) { return ten_rounds(c, k); }
+};
+int main() {
+  probe p; unsigned s = 12345u;
+  for (int i = 0; i < 64; ++i) {
+    uint4 c; uint2 k;
+    s = s * 1664525u + 1013904223u; c.x = s; s = s * 1664525u + 1013904223u; c.y = s;
+    s = s * 1664525u + 1013904223u; c.z = s; s = s * 1664525u + 1013904223u; c.w = s;
+    s = s * 1664525u + 1013904223u; k.x = s; s = s * 1664525u + 1013904223u; k.y = s;
+    uint4 o = p.run(c, k);
+    printf("%u %u %u %u %u %u %u %u %u %u\n", c.x, c.y, c.z, c.w, k.x, k.y, o.x, o.y, o.z, o.w);
+  }
+}
+''')
+    exe = tmp_path / "p"
+    r = subprocess.run([hipcc, "-x", "hip", "--offload-arch=gfx950", "-O1", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("rocRAND header did not compile for the host: " + r.stderr[-300:])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    n = 0
+    for line in out.strip().splitlines():
+        v = [int(x) for x in line.split()]
+        got = orc.philox4x32_10(v[:4], v[4:6])
+        assert [int(x) for x in got] == v[6:10]
+        n += 1
+    assert n == 64
+
+
+def test_uniform_mapping_and_ks(orc):
+    # u = top 24 bits of word 0 / 2^24, counter = (round, req, pos, purpose), key = seed
+    seed = 0x0123456789ABCDEF
+    w = orc.philox4x32_10([7, 3, 2, 1], [seed & 0xFFFFFFFF, seed >> 32])
+    assert orc.uniform(seed, 7, 3, 2, 1) == (int(w[0]) >> 8) / 2.0 ** 24
+    us = np.array([orc.uniform(0, rnd, req, pos, pur)
+                   for rnd in range(5) for req in range(40) for pos in range(10) for pur in range(3)])
+    assert us.min() >= 0.0 and us.max() < 1.0
+    assert sst.kstest(us, "uniform").pvalue > 1e-4
+    # distinct purposes give distinct streams
+    assert orc.uniform(0, 0, 0, 0, 0) != orc.uniform(0, 0, 0, 0, 1)
+
+
+# ---------------------------------------------------------------------------
+# Markov head: the pages' worked example (base 0, 0 plus ln 9: 50% -> 90%)
+# ---------------------------------------------------------------------------
+
+def _ln9_split():
+    g = _golden("markov_example.txt")
+    bias = float(g["bias"][0][0])
+    assert abs(bias - math.log(9.0)) < 1e-15
+    terms, rest = [], bias
+    for _ in range(3):
+        t = float(bf16_val(bf16([rest]))[0])
+        terms.append(t)
+        rest -= t
+    return bias, terms
+
+
+def test_markov_worked_example(orc):
+    g = _golden("markov_example.txt")
+    before = [float(x) for x in g["prob_before"][0]]
+    after = [float(x) for x in g["prob_after"][0]]
+    base = np.zeros(2, np.float32)
+    # rank-3 factorisation of "add ln 9 to token 0": E[prev] = (1, 1, 1),
+    # column 0 of W2 = a three-term bf16 expansion of ln 9, column 1 = 0.
+    _, terms = _ln9_split()
+    E = bf16([[1.0, 1.0, 1.0], [0.0, 0.0, 0.0]])
+    W2 = np.stack([bf16(terms), bf16([0.0, 0.0, 0.0])])
+    logit0, _ = orc.markov_logits(base, E, W2, prev=-1)
+    p0, _ = orc.softmax(logit0, 1.0)
+    np.testing.assert_allclose(p0, before, atol=1e-15)
+    logit1, _ = orc.markov_logits(base, E, W2, prev=0)
+    p1, _ = orc.softmax(logit1, 1.0)
+    np.testing.assert_allclose(p1, after, atol=1e-8)
+    # negative control: keeping only the leading bf16 term misses 90% by > 1e-4,
+    # so the check above sees every term of the rank-r contraction
+    W2c = np.stack([bf16([terms[0], 0.0, 0.0]), bf16([0.0, 0.0, 0.0])])
+    lc, _ = orc.markov_logits(base, E, W2c, prev=0)
+    pc, _ = orc.softmax(lc, 1.0)
+    assert abs(pc[0] - after[0]) > 1e-4
+    # greedy draft picks the favoured token
+    tok, q, _, fl = orc.draft(np.zeros((1, 1, 2), np.float32), E, W2, np.array([0]), np.array([0]),
+                              0.0, 0, 0)
+    assert tok[0, 0] == 0 and fl[0, 0] == 0
+
+
+def test_markov_example_sampling_frequency(orc):
+    """10^7 sampled drafts of the worked example: frequency 0.9 within 5 sigma."""
+    _, terms = _ln9_split()
+    E = bf16([[1.0, 1.0, 1.0], [0.0, 0.0, 0.0]])
+    W2 = np.stack([bf16(terms), bf16([0.0, 0.0, 0.0])])
+    n = 10_000_000
+    base = np.zeros((n, 1, 2), np.float32)
+    tok, q, _, _ = orc.draft(base, E, W2, np.zeros(n, np.int32), np.arange(n, dtype=np.int32),
+                             1.0, 0, 0)
+    freq = float((tok[:, 0] == 0).mean())
+    sigma = math.sqrt(0.9 * 0.1 / n)
+    assert abs(freq - 0.9) < 5 * sigma
+    np.testing.assert_allclose(q[tok[:, 0] == 0, 0][:10], 0.9, atol=1e-8)
+
+
+def test_markov_bias_is_rank_r_contraction(orc):
+    """bias_v = sum_i E[prev, i] W2(i, v): with one-hot E rows the bias is a single
+    W2 entry, which catches transposed or mis-indexed operands."""
+    rng = np.random.default_rng(1)
+    V, r = 7, 5
+    W2 = bf16(rng.normal(0, 0.5, (V, r)))
+    base = rng.normal(0, 1, V).astype(np.float32)
+    for i in range(r):
+        Erow = np.zeros((V, r))
+        Erow[3, i] = 1.0
+        E = bf16(Erow)
+        lg, _ = orc.markov_logits(base, E, W2, prev=3)
+        expect = (base.astype(np.float64) + bf16_val(W2)[:, i]).astype(np.float32)
+        np.testing.assert_array_equal(lg, expect)
+
+
+# ---------------------------------------------------------------------------
+# Token selection: reductions to library routines
+# ---------------------------------------------------------------------------
+
+def test_softmax_matches_scipy(orc):
+    rng = np.random.default_rng(2)
+    for T in (1.0, 0.7, 1.3):
+        x = (rng.normal(0, 3, 1000)).astype(np.float32)
+        p, st = orc.softmax(x, T)
+        ref = sp_softmax(x.astype(np.float64) / T)
+        np.testing.assert_allclose(p, ref, rtol=1e-13, atol=1e-300)
+        assert abs(st[1] - logsumexp(x.astype(np.float64) / T)) < 1e-12
+
+
+def test_inverse_cdf_matches_searchsorted(orc):
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        V = int(rng.integers(1, 50))
+        w = rng.random(V) * (rng.random(V) < 0.7)
+        if w.sum() == 0:
+            w[0] = 1.0
+        u = float(rng.integers(0, 2 ** 24)) / 2 ** 24
+        x, _ = orc.inverse_cdf(w, u)
+        ref = int(np.searchsorted(np.cumsum(w), u * w.sum(), side="right"))
+        assert x == min(ref, V - 1) or (ref == V and w[x] > 0)
+        assert w[x] > 0
+
+
+def test_plain_categorical_when_no_markov_bias(orc):
+    """W2 = 0 reduces the draft to categorical sampling from softmax(base / T)."""
+    rng = np.random.default_rng(4)
+    V, r, n, T = 8, 4, 2_000_000, 0.8
+    row = rng.normal(0, 1.0, V).astype(np.float32)
+    base = np.broadcast_to(row, (n, 1, V)).copy()
+    E = bf16(rng.normal(0, 1, (V, r)))
+    W2 = bf16(np.zeros((V, r)))
+    tok, q, st, _ = orc.draft(base, E, W2, np.zeros(n, np.int32), np.arange(n, dtype=np.int32), T, 5, 9)
+    p = sp_softmax(row.astype(np.float64) / T)
+    ok, pv = chi2_ok(np.bincount(tok[:, 0], minlength=V), p, 1e-4)
+    assert ok, pv
+    np.testing.assert_allclose(q[:, 0], p[tok[:, 0]], rtol=1e-12)
+
+
+def test_greedy_is_argmax_and_low_temperature_limit(orc):
+    rng = np.random.default_rng(5)
+    V, r, g = 64, 8, 5
+    n = 50
+    base = rng.normal(0, 2, (n, g, V)).astype(np.float32)
+    E = bf16(rng.normal(0, 0.1, (V, r)))
+    W2 = bf16(rng.normal(0, 0.1, (V, r)))
+    anchor = rng.integers(0, V, n).astype(np.int32)
+    tok, _, _, fl = orc.draft(base, E, W2, anchor, np.arange(n, dtype=np.int32), 0.0, 0, 0)
+    # recompute the chain with numpy argmax over the oracle's own logits
+    for i in range(n):
+        prev = anchor[i]
+        for k in range(g):
+            lg, _ = orc.markov_logits(base[i, k], E, W2, prev)
+            assert tok[i, k] == int(np.argmax(lg))
+            prev = tok[i, k]
+    # a very low temperature samples the argmax whenever the top gap is large
+    tok_c, _, _, _ = orc.draft(base, E, W2, anchor, np.arange(n, dtype=np.int32), 1e-4, 0, 0)
+    assert (tok_c == tok).mean() > 0.99
+
+
+# ---------------------------------------------------------------------------
+# Confidence head and sequential temperature scaling
+# ---------------------------------------------------------------------------
+
+def test_confidence_concatenation_and_temperature(orc):
+    rng = np.random.default_rng(6)
+    n, g, d, V, r = 5, 4, 12, 20, 6
+    h = bf16(rng.normal(0, 1, (n, g, d)))
+    E = bf16(rng.normal(0, 0.3, (V, r)))
+    w = rng.normal(0, 0.2, d + r).astype(np.float32)
+    T = np.array([1.0, 1.2, 0.8, 2.0], np.float32)
+    anchor = rng.integers(0, V, n).astype(np.int32)
+    tok = rng.integers(0, V, (n, g)).astype(np.int32)
+    c, _ = orc.confidence(h, E, anchor, tok, w, T)
+    # [h_k; E[x_{k-1}]] as one hidden vector of width d + r with no E term
+    prev = np.concatenate([anchor[:, None], tok[:, :-1]], axis=1)
+    h2 = np.concatenate([h, E[prev]], axis=2)
+    c2, _ = orc.confidence(h2, E, np.full(n, -1, np.int32), np.full((n, g), -1, np.int32), w, T)
+    np.testing.assert_allclose(c, c2, rtol=1e-14)
+    # T_k divides the logit: logit(c) * T_k is the same for every T
+    c1, _ = orc.confidence(h, E, anchor, tok, w, np.ones(g, np.float32))
+    lg = np.log(c / (1 - c)) * T[None, :]
+    lg1 = np.log(c1 / (1 - c1))
+    np.testing.assert_allclose(lg, lg1, rtol=1e-9, atol=1e-9)
+    # negating w mirrors the sigmoid; w = 0 gives exactly 1/2
+    cn, _ = orc.confidence(h, E, anchor, tok, -w, T)
+    np.testing.assert_allclose(cn, 1 - c, atol=1e-15)
+    c0, _ = orc.confidence(h, E, anchor, tok, 0 * w, T)
+    assert np.all(c0 == 0.5)
+    # a per-request offset shifts the logit before scaling
+    off = np.linspace(-2, 2, n).astype(np.float32)
+    co, _ = orc.confidence(h, E, anchor, tok, w, np.ones(g, np.float32), off)
+    np.testing.assert_allclose(np.log(co / (1 - co)), lg1 + off[:, None].astype(np.float64),
+                               rtol=1e-9, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Prefix scheduler
+# ---------------------------------------------------------------------------
+
+def test_survival_worked_example(orc):
+    g = _golden("survival_example.txt")
+    cond = [float(x) for x in g["conditional_after_first"][0]]
+    ratio = [float(x) for x in g["ratio"][0]]
+    for c1 in (1.0, 0.9, 0.5, 0.123):
+        c = np.array([[c1] + cond], np.float32)
+        length, a, B, _ = orc.schedule(c, np.ones(6, np.float32), 6, 0.0, 1)
+        expect = c1 * np.array(ratio)
+        ulp = np.spacing(np.abs(expect).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(a[0].astype(np.float64) - expect) <= 2 * ulp)
+        assert np.all(np.diff(a[0]) <= 0)
+        # with a constant SPS the objective rises with every positive a: all admitted
+        assert length[0] == 5 and B == 6
+
+
+def _prefix_curve(a, sps, R, tau0, B_max):
+    """Theta after admitting the n best candidates, n = 0..N (fp64, numpy sort)."""
+    Rg = a.shape
+    flat = a.ravel().astype(np.float64)
+    rr = np.repeat(np.arange(a.shape[0]), a.shape[1])
+    jj = np.tile(np.arange(a.shape[1]), a.shape[0])
+    order = np.lexsort((jj, rr, -flat))
+    theta = [tau0 * sps[R - 1]]
+    s = tau0
+    for n, idx in enumerate(order, start=1):
+        if R + n > B_max:
+            break
+        s += flat[idx]
+        theta.append(s * sps[R + n - 1])
+    return np.array(theta), order, rr, jj
+
+
+def test_scheduler_brute_force(orc):
+    """Exhaustive search over every length vector on tiny instances (R <= 3,
+    gamma <= 4): the best prefix of the global sort is the global optimum, and
+    the early stop gives the first local maximum of the prefix curve, which is the
+    global one whenever that curve is unimodal."""
+    rng = np.random.default_rng(7)
+    kinds = {"unimodal": 0, "multimodal": 0}
+    for trial in range(400):
+        R = int(rng.integers(1, 4))
+        gamma = int(rng.integers(1, 5))
+        c = rng.uniform(0.05, 1.0, (R, gamma)).astype(np.float32)
+        B_full = R * (gamma + 1)
+        B_max = int(rng.integers(R, B_full + 1))
+        if trial % 3 == 0:
+            # jagged cost curve (non-monotone SPS) to produce multimodal objectives
+            sps = rng.uniform(0.2, 1.0, B_max).astype(np.float32)
+        else:
+            k1, k2 = rng.uniform(0.01, 3.0), rng.uniform(0.0, 0.5)
+            Bs = np.arange(1, B_max + 1, dtype=np.float64)
+            sps = (1.0 / (1.0 + k1 * Bs + k2 * Bs * Bs)).astype(np.float32)
+        tau0 = float(rng.choice([0.0, float(R)]))
+        length, a, B, _ = orc.schedule(c, sps, B_max, tau0, 1)
+        spsd = sps.astype(np.float64)
+        # exhaustive optimum over every l vector
+        best = -1.0
+        for lv in itertools.product(range(gamma + 1), repeat=R):
+            Bv = R + sum(lv)
+            if Bv > B_max:
+                continue
+            tau = tau0 + sum(float(a[r_, :lv[r_]].astype(np.float64).sum()) for r_ in range(R))
+            best = max(best, tau * spsd[Bv - 1])
+        theta, order, rr, jj = _prefix_curve(a, spsd, R, tau0, B_max)
+        assert abs(theta.max() - best) <= 1e-12 * max(best, 1e-300)
+        # early stop = first n with theta_{n+1} <= theta_n
+        n_star = 0
+        while n_star + 1 < len(theta) and theta[n_star + 1] > theta[n_star] * (1 + 1e-12):
+            n_star += 1
+        assert B == R + n_star, (trial, B, R, n_star)
+        expect_len = np.bincount(rr[order[:n_star]], minlength=R)
+        np.testing.assert_array_equal(length, expect_len)
+        # admitted sets are prefixes of each request's block
+        unimodal = all(theta[i + 1] <= theta[i] for i in range(n_star, len(theta) - 1))
+        if unimodal:
+            kinds["unimodal"] += 1
+            assert abs(theta[n_star] - best) <= 1e-12 * max(best, 1e-300)
+        else:
+            kinds["multimodal"] += 1
+    assert kinds["unimodal"] > 50 and kinds["multimodal"] > 5, kinds
+
+
+def test_scheduler_causality(orc):
+    """Whether position j of request r is verified must not depend on x_{r,j} or
+    later tokens, i.e. on c_{r,j+1..}: perturbing those keeps min(l_r, j+1)."""
+    rng = np.random.default_rng(8)
+    for _ in range(300):
+        R, gamma = int(rng.integers(1, 6)), int(rng.integers(2, 7))
+        c = rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
+        Bs = np.arange(1, R * (gamma + 1) + 1, dtype=np.float64)
+        sps = (1.0 / (12 + 0.1 * Bs + 0.0008 * Bs ** 2 * rng.uniform(1, 200))).astype(np.float32)
+        l0, _, _, _ = orc.schedule(c, sps, R * (gamma + 1), 0.0, 1)
+        r = int(rng.integers(0, R))
+        j = int(rng.integers(0, gamma - 1))
+        c2 = c.copy()
+        c2[r, j + 1:] = rng.uniform(0.0, 1.0, gamma - j - 1).astype(np.float32)
+        l1, _, _, _ = orc.schedule(c2, sps, R * (gamma + 1), 0.0, 1)
+        assert min(l0[r], j + 1) == min(l1[r], j + 1)
+
+
+def test_scheduler_off_and_limits(orc):
+    c = np.full((3, 4), 0.9, np.float32)
+    length, a, B, _ = orc.schedule(c, np.ones(15, np.float32), 15, 0.0, 0)
+    assert list(length) == [4, 4, 4] and B == 15
+    # B_max = R admits nothing
+    length, _, B, _ = orc.schedule(c, np.ones(3, np.float32), 3, 0.0, 1)
+    assert list(length) == [0, 0, 0] and B == 3
+    # a = 0 never raises the objective
+    length, _, B, _ = orc.schedule(np.zeros((2, 3), np.float32), np.ones(8, np.float32), 8, 0.0, 1)
+    assert list(length) == [0, 0] and B == 2
+
+
+# ---------------------------------------------------------------------------
+# Lossless verification: identities of the proof and the pages' examples
+# ---------------------------------------------------------------------------
+
+def _tiny_single_position(rng, V, r, skew=None):
+    base_row = rng.normal(0, 1.5, V).astype(np.float32)
+    E = bf16(rng.normal(0, 0.4, (V, r)))
+    W2 = bf16(rng.normal(0, 0.4, (V, r)))
+    target_rows = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+    return base_row, E, W2, target_rows
+
+
+def test_total_acceptance_is_sum_min_and_residual_law(orc):
+    """Page 5's proof: acceptance probability sum_x min(p, q); rejection
+    probability sum max(0, p - q); after rejection y ~ max(0, p - q) normalised.
+    10^7 trials at one position, V = 6."""
+    rng = np.random.default_rng(9)
+    V, r, n, T = 6, 4, 10_000_000, 1.0
+    base_row, E, W2, trows = _tiny_single_position(rng, V, r)
+    anchor = 2
+    base = np.broadcast_to(base_row, (n, 1, V)).copy()
+    target = np.broadcast_to(trows, (n, 2, V)).copy()
+    req = np.arange(n, dtype=np.int32)
+    anc = np.full(n, anchor, np.int32)
+    tok, q, _, _ = orc.draft(base, E, W2, anc, req, T, 11, 3)
+    res = orc.verify(target, base, E, W2, anc, tok, q, np.ones(n, np.int32), req, T, 11, 3)
+    lg, _ = orc.markov_logits(base_row, E, W2, anchor)
+    qd, _ = orc.softmax(lg, T)
+    p, _ = orc.softmax(trows[0], T)
+    acc_rate = float((res["accept"][:, 0] == 1).mean())
+    smin = float(np.minimum(p, qd).sum())
+    assert abs(acc_rate - smin) < 5 * math.sqrt(smin * (1 - smin) / n)
+    rej = res["n_accept"] == 0
+    rho = np.maximum(0.0, p - qd)
+    assert abs(rej.mean() - rho.sum()) < 5 * math.sqrt(rho.sum() * (1 - rho.sum()) / n)
+    ok, pv = chi2_ok(np.bincount(res["y"][rej], minlength=V), rho / rho.sum(), 1e-4)
+    assert ok, pv
+    # emitted token at position 0 ~ p (lossless)
+    emitted = np.where(rej, res["y"], tok[:, 0])
+    ok, pv = chi2_ok(np.bincount(emitted, minlength=V), p, 1e-4)
+    assert ok, pv
+
+
+def test_two_token_example(orc):
+    """Target wants A 60% / B 40%; a draft skewed either way leaves the output
+    law at 60/40 (10^7 trials per skew)."""
+    tgt = np.array([float(x) for x in _golden("two_token_example.txt")["target"][0]])
+    n = 10_000_000
+    E = bf16([[0.0], [0.0]])
+    W2 = bf16([[0.0], [0.0]])
+    tl = np.log(tgt).astype(np.float32)
+    p, _ = orc.softmax(tl, 1.0)
+    for qa in (0.95, 0.05, 0.6):
+        ql = np.log(np.array([qa, 1 - qa])).astype(np.float32)
+        base = np.broadcast_to(ql, (n, 1, 2)).copy()
+        target = np.broadcast_to(np.stack([tl, tl]), (n, 2, 2)).copy()
+        req = np.arange(n, dtype=np.int32)
+        anc = np.full(n, -1, np.int32)
+        tok, q, _, _ = orc.draft(base, E, W2, anc, req, 1.0, 21, 0)
+        res = orc.verify(target, base, E, W2, anc, tok, q, np.ones(n, np.int32), req, 1.0, 21, 0)
+        emitted = np.where(res["n_accept"] == 0, res["y"], tok[:, 0])
+        fa = float((emitted == 0).mean())
+        assert abs(fa - p[0]) < 5 * math.sqrt(p[0] * p[1] / n), (qa, fa)
+
+
+def test_reductions_p_equals_q_and_zero_length(orc):
+    rng = np.random.default_rng(10)
+    V, r, g, n, T = 16, 4, 3, 20000, 0.9
+    base = rng.normal(0, 1, (n, g, V)).astype(np.float32)
+    E = bf16(rng.normal(0, 0.2, (V, r)))
+    W2 = bf16(np.zeros((V, r)))
+    anc = rng.integers(0, V, n).astype(np.int32)
+    req = np.arange(n, dtype=np.int32)
+    tok, q, _, _ = orc.draft(base, E, W2, anc, req, T, 1, 1)
+    # target equal to the draft logits (no bias since W2 = 0): p = q, all accepted
+    target = np.concatenate([base, rng.normal(0, 1, (n, 1, V)).astype(np.float32)], axis=1)
+    res = orc.verify(target, base, E, W2, anc, tok, q, np.full(n, g, np.int32), req, T, 1, 1)
+    assert np.all(res["n_accept"] == g) and np.all(res["accept"] == 1)
+    np.testing.assert_allclose(res["p"], q, rtol=1e-12)
+    # l = 0: verification is one draw from target row 0 (the bonus of an empty block)
+    n2 = 2_000_000
+    row = rng.normal(0, 1, V).astype(np.float32)
+    tgt2 = np.broadcast_to(np.stack([row] * (g + 1)), (n2, g + 1, V)).copy()
+    b2 = np.zeros((n2, g, V), np.float32)
+    res2 = orc.verify(tgt2, b2, E, W2, np.zeros(n2, np.int32), np.zeros((n2, g), np.int32),
+                      np.ones((n2, g)), np.zeros(n2, np.int32), np.arange(n2, dtype=np.int32), T, 4, 4)
+    assert np.all(res2["n_accept"] == 0) and np.all(res2["accept"] == -1)
+    ok, pv = chi2_ok(np.bincount(res2["y"], minlength=V), sp_softmax(row.astype(np.float64) / T), 1e-4)
+    assert ok, pv
+
+
+def test_greedy_verification_is_exact_match(orc):
+    rng = np.random.default_rng(12)
+    V, r, g, n = 40, 4, 4, 300
+    base = rng.normal(0, 2, (n, g, V)).astype(np.float32)
+    E = bf16(rng.normal(0, 0.2, (V, r)))
+    W2 = bf16(rng.normal(0, 0.2, (V, r)))
+    anc = rng.integers(0, V, n).astype(np.int32)
+    req = np.arange(n, dtype=np.int32)
+    tok, q, _, _ = orc.draft(base, E, W2, anc, req, 0.0, 0, 0)
+    target = rng.normal(0, 2, (n, g + 1, V)).astype(np.float32)
+    # make the target agree with the draft on a random prefix
+    for i in range(n):
+        m = int(rng.integers(0, g + 1))
+        for j in range(m):
+            target[i, j, tok[i, j]] = target[i, j].max() + 1.0
+    length = rng.integers(0, g + 1, n).astype(np.int32)
+    res = orc.verify(target, base, E, W2, anc, tok, q, length, req, 0.0, 0, 0)
+    for i in range(n):
+        am = target[i].argmax(axis=1)
+        nacc = 0
+        while nacc < length[i] and tok[i, nacc] == am[nacc]:
+            nacc += 1
+        assert res["n_accept"][i] == nacc
+        assert res["y"][i] == am[nacc]
+
+
+@pytest.mark.slow
+def test_whole_path_output_law_chi2(orc):
+    """Whole round with the scheduler on, V = 6, gamma = 3: over 10^7 request
+    trials, the token emitted at every reached position j follows p_j, because
+    whether j is verified depends only on x_{<j}."""
+    rng = np.random.default_rng(13)
+    V, r, g, d, T = 6, 4, 3, 8, 1.0
+    R, rounds = 1000, 10_000
+    base_row = rng.normal(0, 1.0, (g, V)).astype(np.float32)
+    trows = (np.concatenate([base_row, rng.normal(0, 1.0, (1, V))]) +
+             rng.normal(0, 0.8, (g + 1, V))).astype(np.float32)
+    E = bf16(rng.normal(0, 0.5, (V, r)))
+    W2 = bf16(rng.normal(0, 0.5, (V, r)))
+    h = bf16(rng.normal(0, 1, (g, d)))
+    w = rng.normal(0, 0.5, d + r).astype(np.float32)
+    Tk = np.array([1.0, 1.2, 1.4], np.float32)
+    Bs = np.arange(1, R * (g + 1) + 1, dtype=np.float64)
+    # a cost curve flat enough that every length 0..gamma occurs
+    sps = (1.0 / (12 + 0.3 * Bs + 2e-5 * Bs * Bs)).astype(np.float32)
+    base = np.broadcast_to(base_row, (R, g, V)).copy()
+    target = np.broadcast_to(trows, (R, g + 1, V)).copy()
+    hh = np.broadcast_to(h, (R, g, d)).copy()
+    anc = rng.integers(0, V, R).astype(np.int32)
+    req = np.arange(R, dtype=np.int32)
+    counts = np.zeros((g + 1, V), np.int64)
+    lens = np.zeros(g + 1, np.int64)
+    for rnd in range(rounds):
+        tok, q, _, _ = orc.draft(base, E, W2, anc, req, T, 77, rnd)
+        c, _ = orc.confidence(hh, E, anc, tok, w, Tk)
+        length, _, _, _ = orc.schedule(c.astype(np.float32), sps, R * (g + 1), 0.0, 1)
+        res = orc.verify(target, base, E, W2, anc, tok, q, length, req, T, 77, rnd)
+        nacc = res["n_accept"]
+        lens += np.bincount(length, minlength=g + 1)
+        for j in range(g + 1):
+            reached = nacc >= j
+            em = np.where(nacc[reached] == j, res["y"][reached],
+                          tok[reached, min(j, g - 1)] if j < g else res["y"][reached])
+            counts[j] += np.bincount(em, minlength=V)
+    assert np.all(lens > 0.03 * lens.sum()), lens  # ragged lengths actually occur
+    for j in range(g + 1):
+        p, _ = orc.softmax(trows[j], T)
+        ok, pv = chi2_ok(counts[j], p, 1e-4 / (g + 1))
+        assert ok, (j, pv, counts[j])
+
+
+def test_oracle_is_deterministic(orc):
+    from draft_sampling_lossless_markov_amd.workloads import WORKLOADS, make_inputs
+    inp = make_inputs(WORKLOADS[0], 3)
+    a = orc.run_round(inp, 1.0, 0, 5)
+    b = orc.run_round(inp, 1.0, 0, 5)
+    for k in ("tok", "q", "c", "len", "y", "n_accept", "accept"):
+        np.testing.assert_array_equal(a[k], b[k])
+    c = orc.run_round(inp, 1.0, 0, 6)
+    assert not np.array_equal(a["tok"], c["tok"]) or not np.array_equal(a["y"], c["y"])

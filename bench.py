@@ -1,0 +1,205 @@
+"""Benchmark of the DSpark draft / confidence / schedule / verify path on one GPU.
+
+One step = one decode round over a batch of synthetic inputs already resident in
+HBM: gamma x dsp_draft_step, dsp_confidence, dsp_schedule, dsp_verify, issued
+back to back on one stream.  Prints one JSON line (metric, throughput, the
+roofline of the dominant entry point measured with HIP events on the launch
+stream inside the timed region, and the CPU oracle timed on a bounded sample).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from draft_sampling_lossless_markov_amd import dsp  # noqa: E402
+from draft_sampling_lossless_markov_amd.engine import Round  # noqa: E402
+from draft_sampling_lossless_markov_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "verified draft positions/sec (draft+verify) and % of MI355X HBM roofline"
+UNIT = "verified draft positions/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def round_bytes(wl, inp, len_sum, n_rej, greedy):
+    """Algorithmic HBM bytes of one round: logit rows streamed once (draft base
+    rows, verified and bonus target rows, the p and base rows re-read for each
+    residual draw), W2 once, hidden states and embedding rows once."""
+    s = inp["base"].element_size()
+    R, g, V, r, d = inp["R"], inp["gamma"], inp["V"], inp["r"], inp["d"]
+    rows = R * g + (R + len_sum) + (0 if greedy else 2 * n_rej)
+    return s * V * rows + 2 * r * V + 2 * R * g * (d + r)
+
+
+def draft_step_bytes(inp):
+    """Compulsory bytes of one dsp_draft_step launch pair: the [R, V] base slice,
+    all of W2 (every vocabulary column needs its bias), the gathered E rows and
+    the per-request outputs."""
+    s = inp["base"].element_size()
+    R, V, r = inp["R"], inp["V"], inp["r"]
+    return s * R * V + 2 * r * V + 2 * R * r + R * 16
+
+
+def cpu_baseline(wl, inp, temp, budget_s):
+    """The oracle as it stands, one thread, on whole requests of set 0 until about
+    budget_s seconds of CPU work; every position of a sampled request verified."""
+    import oracle
+    E = oracle.bf16_bits(inp["E"])
+    W2 = oracle.bf16_bits(inp["W2"])
+    anchor = inp["anchor"].cpu().numpy()
+    w, T = inp["w"].cpu().numpy(), inp["T"].cpu().numpy()
+    off = None if inp["offset"] is None else inp["offset"].cpu().numpy()
+    g = inp["gamma"]
+    done, positions, spent = 0, 0, 0.0
+    while spent < budget_s and done < inp["R"]:
+        n = done
+        sl = slice(n, n + 1)
+        base = oracle.host_logits(inp["base"][sl])
+        target = oracle.host_logits(inp["target"][sl])
+        h = oracle.bf16_bits(inp["h"][sl])
+        t0 = time.perf_counter()
+        tok, q, _, _ = oracle.draft(base, E, W2, anchor[sl], np.array([n], np.int32), temp, 0, 0)
+        oracle.confidence(h, E, anchor[sl], tok, w, T, None if off is None else off[sl])
+        oracle.verify(target, base, E, W2, anchor[sl], tok, q, np.array([g], np.int32),
+                      np.array([n], np.int32), temp, 0, 0)
+        spent += time.perf_counter() - t0
+        done += 1
+        positions += g
+    return {"value": positions / spent, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {inp['R']} requests of one round of {wl.name} "
+                      f"(draft + confidence + verify of all {g} positions each), "
+                      f"{spent:.1f} s on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--mode", choices=["sampling", "greedy"], default=None)
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures the one-GPU path only; --gpus {args.gpus} is not supported "
+              "(the path shards by request; see the multi-GPU design notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    mode = args.mode or wl.modes[-1]
+    greedy = mode == "greedy"
+    temp = 0.0 if greedy else wl.temperature
+    dsp.lib()
+    log(f"workload {wl.name}, {mode}, building {args.sets} input sets")
+    sets = [make_inputs(wl, s, device="cuda") for s in range(args.sets)]
+    inp0 = sets[0]
+    R, g, V, r = inp0["R"], inp0["gamma"], inp0["V"], inp0["r"]
+    rd = Round(R, g, V, r)
+    stream = torch.cuda.current_stream()
+    seed = 0
+
+    def one_round(i, ev=None):
+        inp = sets[i % len(sets)]
+        for k in range(g):
+            if ev is not None:
+                ev[k].record(stream)
+            dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
+                               rd.stats, k, temp, seed, i, rd.ws_draft, stream)
+        if ev is not None:
+            ev[g].record(stream)
+        rd.confidence(inp, stream)
+        if ev is not None:
+            ev[g + 1].record(stream)
+        rd.schedule(inp, stream=stream)
+        if ev is not None:
+            ev[g + 2].record(stream)
+        rd.verify(inp, temp, seed, i, stream)
+        if ev is not None:
+            ev[g + 3].record(stream)
+
+    for i in range(args.warmup):
+        one_round(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(g + 4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        one_round(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+
+    # per entry point (event-bracketed) average durations, in ms
+    draft_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(g)] for i in range(K)])
+    conf_ms = np.array([evs[i][g].elapsed_time(evs[i][g + 1]) for i in range(K)])
+    sched_ms = np.array([evs[i][g + 1].elapsed_time(evs[i][g + 2]) for i in range(K)])
+    ver_ms = np.array([evs[i][g + 2].elapsed_time(evs[i][g + 3]) for i in range(K)])
+
+    # replay the timed rounds (deterministic) to count verified positions
+    len_sum = rej = 0
+    for i in range(K):
+        one_round(args.warmup + i)
+        L = rd.len.cpu().numpy()
+        na = rd.n_accept.cpu().numpy()
+        len_sum += int(L.sum())
+        rej += int((na < L).sum())
+    len_per_round = len_sum / K
+    rej_per_round = rej / K
+    value = len_per_round / (ms_per_step * 1e-3)
+    A = round_bytes(wl, inp0, len_per_round, rej_per_round, greedy)
+
+    step_bytes = draft_step_bytes(inp0)
+    draft_avg_s = float(draft_ms.mean()) * 1e-3
+    achieved = step_bytes / draft_avg_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "dsp_draft_step (draft_partials_kernel + draft_pick_kernel)",
+            "bytes_per_launch": int(step_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if inp0["base"].dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "R": R, "gamma": g, "V": V, "r": r, "d": inp0["d"],
+                   "mode": mode, "scheduler": "on" if wl.mode == 1 else "off (every position verified)",
+                   "parallelism": "single GPU"},
+        "round_roofline": {"algorithmic_bytes": int(A), "t_roof_us": round(A / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                           "frac": round(A / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)},
+        "entry_points_us": {"draft_step": round(float(draft_ms.mean()) * 1e3, 2),
+                            "confidence": round(float(conf_ms.mean()) * 1e3, 2),
+                            "schedule": round(float(sched_ms.mean()) * 1e3, 2),
+                            "verify": round(float(ver_ms.mean()) * 1e3, 2)},
+        "verified_per_round": len_per_round, "drafted_per_round": R * g,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, inp0, temp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+// api.cpp -- the C-ABI entry points of libdsp.so (declared in include/dsp.h).
+//
+// Every argument is validated on the host before any HIP call, so argument
+// errors are reported without touching a device; kernels are then launched on
+// the caller's stream.  No exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsp.h"
+#include "dsp_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsp_status fail(dsp_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dsp_status ok()
+{
+    g_err[0] = '\0';
+    return DSP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dsp_status hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(DSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// shapes shared by the Markov-head calls
+dsp_status check_markov(int R, int gamma, int V, int r)
+{
+    if (R <= 0) return fail(DSP_ERR_INVALID_ARG, "R must be >= 1 (got %d)", R);
+    if (gamma <= 0) return fail(DSP_ERR_INVALID_ARG, "gamma must be >= 1 (got %d)", gamma);
+    if (V <= 0) return fail(DSP_ERR_INVALID_ARG, "V must be >= 1 (got %d)", V);
+    if (r <= 0) return fail(DSP_ERR_INVALID_ARG, "r must be >= 1 (got %d)", r);
+    if (gamma > dsp::kGammaMax)
+        return fail(DSP_ERR_UNSUPPORTED, "gamma = %d exceeds the supported maximum %d", gamma,
+                    dsp::kGammaMax);
+    if (r > 256 || (r % 8) != 0)
+        return fail(DSP_ERR_UNSUPPORTED, "r = %d: the bias kernels need r %% 8 == 0 and r <= 256", r);
+    if ((int64_t)R * (gamma + 1) > (int64_t)INT32_MAX / 2)
+        return fail(DSP_ERR_UNSUPPORTED, "R * (gamma + 1) too large");
+    return DSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsp_status_string(dsp_status s)
+{
+    switch (s) {
+    case DSP_OK: return "DSP_OK";
+    case DSP_ERR_INVALID_ARG: return "DSP_ERR_INVALID_ARG";
+    case DSP_ERR_UNSUPPORTED: return "DSP_ERR_UNSUPPORTED";
+    case DSP_ERR_WORKSPACE: return "DSP_ERR_WORKSPACE";
+    case DSP_ERR_HIP: return "DSP_ERR_HIP";
+    }
+    return "DSP_ERR_UNKNOWN";
+}
+
+const char* dsp_last_error(void) { return g_err; }
+
+int dsp_version(void) { return 100; }
+
+size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
+{
+    if (R <= 0 || gamma <= 0 || V <= 0 || r <= 0) return 0;
+    if (which == DSP_WS_DRAFT) return dsp::draft_workspace_bytes(R, V);
+    if (which == DSP_WS_VERIFY) return dsp::verify_workspace_bytes(R, gamma, V);
+    return 0;
+}
+
+dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
+                          const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
+                          float* stats, int R, int gamma, int V, int r, int k,
+                          float temperature, uint64_t seed, uint32_t round, void* ws,
+                          size_t ws_bytes, void* stream)
+{
+    if (!base || !E || !W2 || !anchor || !tok || !q || !stats)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: null pointer argument");
+    if (dtype != DSP_F32 && dtype != DSP_BF16)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: unknown dtype %d", (int)dtype);
+    dsp_status st = check_markov(R, gamma, V, r);
+    if (st != DSP_OK) return st;
+    if (k < 0 || k >= gamma)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: k = %d outside [0, gamma)", k);
+    if (!(temperature >= 0.0f) || std::isinf(temperature))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: temperature must be finite and >= 0");
+    if (!aligned16(base) || !aligned16(E) || !aligned16(W2))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: base, E and W2 must be 16-byte aligned");
+    const size_t need = dsp::draft_workspace_bytes(R, V);
+    if (!ws || ws_bytes < need)
+        return fail(DSP_ERR_WORKSPACE, "dsp_draft_step: workspace of %zu bytes, %zu needed",
+                    ws_bytes, need);
+    return hip_status(dsp::launch_draft_step(base, dtype == DSP_BF16, E, W2, anchor, tok, q,
+                                             stats, R, gamma, V, r, k, temperature, seed, round,
+                                             ws, static_cast<hipStream_t>(stream)),
+                      "dsp_draft_step launch");
+}
+
+dsp_status dsp_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
+                          const int32_t* tok, const float* w, const float* T,
+                          const float* offset, float* c, int R, int gamma, int d, int V, int r,
+                          void* stream)
+{
+    if (!E || !anchor || !tok || !w || !T || !c || (!h && d > 0))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_confidence: null pointer argument");
+    if (R <= 0 || gamma <= 0 || V <= 0 || r <= 0 || d < 0)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_confidence: bad sizes R=%d gamma=%d d=%d V=%d r=%d",
+                    R, gamma, d, V, r);
+    if ((int64_t)R * gamma > (int64_t)INT32_MAX / 2)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_confidence: R * gamma too large");
+    if ((h && !aligned16(h)) || !aligned16(w))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_confidence: h and w must be 16-byte aligned");
+    return hip_status(dsp::launch_confidence(h, E, anchor, tok, w, T, offset, c, R, gamma, d, V,
+                                             r, static_cast<hipStream_t>(stream)),
+                      "dsp_confidence launch");
+}
+
+dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0, int mode,
+                        int32_t* len, float* a, int32_t* B, int R, int gamma, void* stream)
+{
+    if (!c || !len || !a || !B || (mode != 0 && !sps))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: null pointer argument");
+    if (R <= 0 || gamma <= 0)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: bad sizes R=%d gamma=%d", R, gamma);
+    if (mode != 0 && mode != 1)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: mode must be 0 or 1 (got %d)", mode);
+    if (mode == 1 && B_max < R)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: B_max = %d < R = %d", B_max, R);
+    if (!(tau0 >= 0.0) || !(tau0 < 1e6))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: tau0 must be in [0, 1e6)");
+    if ((int64_t)R * gamma > dsp::kSchedMaxCand)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_schedule: R * gamma = %lld exceeds %d",
+                    (long long)R * gamma, dsp::kSchedMaxCand);
+    const uint64_t S0 = (uint64_t)std::floor(tau0 * 281474976710656.0);
+    return hip_status(dsp::launch_schedule(c, sps, B_max, S0, mode, len, a, B, R, gamma,
+                                           static_cast<hipStream_t>(stream)),
+                      "dsp_schedule launch");
+}
+
+dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, const uint16_t* E,
+                      const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
+                      const float* q, const float* stats, const int32_t* len, int8_t* accept,
+                      int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
+                      float temperature, uint64_t seed, uint32_t round, void* ws,
+                      size_t ws_bytes, void* stream)
+{
+    if (!target || !base || !E || !W2 || !anchor || !tok || !q || !stats || !len || !accept ||
+        !n_accept || !y || !p)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_verify: null pointer argument");
+    if (dtype != DSP_F32 && dtype != DSP_BF16)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_verify: unknown dtype %d", (int)dtype);
+    dsp_status st = check_markov(R, gamma, V, r);
+    if (st != DSP_OK) return st;
+    if (!(temperature >= 0.0f) || std::isinf(temperature))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_verify: temperature must be finite and >= 0");
+    if (!aligned16(target) || !aligned16(base) || !aligned16(E) || !aligned16(W2))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_verify: target, base, E and W2 must be 16-byte aligned");
+    const size_t need = dsp::verify_workspace_bytes(R, gamma, V);
+    if (!ws || ws_bytes < need)
+        return fail(DSP_ERR_WORKSPACE, "dsp_verify: workspace of %zu bytes, %zu needed", ws_bytes,
+                    need);
+    return hip_status(dsp::launch_verify(target, base, dtype == DSP_BF16, E, W2, anchor, tok, q,
+                                         stats, len, accept, n_accept, y, p, R, gamma, V, r,
+                                         temperature, seed, round, ws,
+                                         static_cast<hipStream_t>(stream)),
+                      "dsp_verify launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// dsp_launch.h -- host-side launchers of the gfx950 kernels (internal to libdsp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsp {
+
+constexpr int kSchedMaxCand = 16384;   // R * gamma limit of the one-workgroup scheduler
+constexpr int kGammaMax = 64;
+
+size_t draft_workspace_bytes(int R, int V);
+size_t verify_workspace_bytes(int R, int gamma, int V);
+
+hipError_t launch_draft_step(const void* base, bool bf16, const uint16_t* E, const uint16_t* W2,
+                             const int32_t* anchor, int32_t* tok, float* q, float* stats, int R,
+                             int gamma, int V, int r, int k, float temperature, uint64_t seed,
+                             uint32_t round, void* ws, hipStream_t s);
+
+hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
+                             const int32_t* tok, const float* w, const float* T,
+                             const float* offset, float* c, int R, int gamma, int d, int V, int r,
+                             hipStream_t s);
+
+hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t S0, int mode,
+                           int32_t* len, float* a, int32_t* B, int R, int gamma, hipStream_t s);
+
+hipError_t launch_verify(const void* target, const void* base, bool bf16, const uint16_t* E,
+                         const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
+                         const float* q, const float* stats, const int32_t* len, int8_t* accept,
+                         int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
+                         float temperature, uint64_t seed, uint32_t round, void* ws,
+                         hipStream_t s);
+
+}  // namespace dsp

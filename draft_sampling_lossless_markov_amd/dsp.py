@@ -1,0 +1,128 @@
+"""ctypes binding of libdsp.so -- argument marshalling only.
+
+The functions carry the C-ABI names (include/dsp.h).  They take torch tensors
+that already live on the GPU, pass their data pointers and the current HIP
+stream, and raise DspError on a non-OK status.  Every step of the path runs in
+the HIP kernels of libdsp.so; there is no fallback: if the library is missing
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsp.so")
+
+DSP_OK, DSP_ERR_INVALID_ARG, DSP_ERR_UNSUPPORTED, DSP_ERR_WORKSPACE, DSP_ERR_HIP = range(5)
+DSP_F32, DSP_BF16 = 0, 1
+DSP_WS_DRAFT, DSP_WS_VERIFY = 0, 1
+
+EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
+            "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
+
+_lib = None
+
+
+class DspError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+
+
+def _status_name(s):
+    return ["DSP_OK", "DSP_ERR_INVALID_ARG", "DSP_ERR_UNSUPPORTED", "DSP_ERR_WORKSPACE",
+            "DSP_ERR_HIP"][s] if 0 <= s < 5 else f"status {s}"
+
+
+def lib():
+    """Load libdsp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m draft_sampling_lossless_markov_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    P, I, U64, U32, F, D, SZ = (C.c_void_p, C.c_int, C.c_uint64, C.c_uint32, C.c_float,
+                                C.c_double, C.c_size_t)
+    L.dsp_status_string.argtypes = [I]
+    L.dsp_status_string.restype = C.c_char_p
+    L.dsp_last_error.argtypes = []
+    L.dsp_last_error.restype = C.c_char_p
+    L.dsp_version.restype = I
+    L.dsp_workspace_size.argtypes = [I, I, I, I, I]
+    L.dsp_workspace_size.restype = SZ
+    L.dsp_draft_step.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, F, U64, U32, P, SZ, P]
+    L.dsp_confidence.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
+    L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
+    L.dsp_verify.argtypes = [P, P, I, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, U64, U32,
+                             P, SZ, P]
+    for f in ("dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify"):
+        getattr(L, f).restype = I
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != DSP_OK:
+        raise DspError(status, lib().dsp_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSP_F32
+    if t.dtype == torch.bfloat16:
+        return DSP_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def dsp_workspace_size(which: int, R: int, gamma: int, V: int, r: int) -> int:
+    return int(lib().dsp_workspace_size(which, R, gamma, V, r))
+
+
+def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_, ws,
+                   stream=None):
+    R, gamma, V = base.shape
+    r = E.shape[1]
+    _check(lib().dsp_draft_step(_ptr(base), _dtype(base), _ptr(E), _ptr(W2), _ptr(anchor),
+                                _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V, r, int(k),
+                                float(temperature), int(seed), int(round_), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsp_confidence(h, E, anchor, tok, w, T, offset, c, stream=None):
+    R, gamma, d = h.shape
+    V, r = E.shape
+    _check(lib().dsp_confidence(_ptr(h), _ptr(E), _ptr(anchor), _ptr(tok), _ptr(w), _ptr(T),
+                                _ptr(offset), _ptr(c), R, gamma, d, V, r, _stream(stream)))
+
+
+def dsp_schedule(c, sps, B_max, tau0, mode, length, a, B, stream=None):
+    R, gamma = c.shape
+    _check(lib().dsp_schedule(_ptr(c), _ptr(sps), int(B_max), float(tau0), int(mode),
+                              _ptr(length), _ptr(a), _ptr(B), R, gamma, _stream(stream)))
+
+
+def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_accept, y, p,
+               temperature, seed, round_, ws, stream=None):
+    R, g1, V = target.shape
+    r = E.shape[1]
+    _check(lib().dsp_verify(_ptr(target), _ptr(base), _dtype(target), _ptr(E), _ptr(W2),
+                            _ptr(anchor), _ptr(tok), _ptr(q), _ptr(stats), _ptr(length),
+                            _ptr(accept), _ptr(n_accept), _ptr(y), _ptr(p), R, g1 - 1, V, r,
+                            float(temperature), int(seed), int(round_), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,0 +1,60 @@
+"""One DSpark decode round on the GPU: gamma draft steps, the confidence head,
+the prefix scheduler and verification, issued back to back on one stream.
+
+The Round object owns the output tensors and the two workspaces (allocated once,
+reused every round) and calls the C-ABI in order; it does no arithmetic itself.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import dsp
+
+
+class Round:
+    def __init__(self, R: int, gamma: int, V: int, r: int, device="cuda"):
+        self.R, self.gamma, self.V, self.r = R, gamma, V, r
+        dev = torch.device(device)
+        i32, f32 = torch.int32, torch.float32
+        self.tok = torch.zeros((R, gamma), dtype=i32, device=dev)
+        self.q = torch.zeros((R, gamma), dtype=f32, device=dev)
+        self.stats = torch.zeros((R, gamma, 2), dtype=f32, device=dev)
+        self.c = torch.zeros((R, gamma), dtype=f32, device=dev)
+        self.len = torch.zeros((R,), dtype=i32, device=dev)
+        self.a = torch.zeros((R, gamma), dtype=f32, device=dev)
+        self.B = torch.zeros((1,), dtype=i32, device=dev)
+        self.accept = torch.zeros((R, gamma), dtype=torch.int8, device=dev)
+        self.n_accept = torch.zeros((R,), dtype=i32, device=dev)
+        self.y = torch.zeros((R,), dtype=i32, device=dev)
+        self.p = torch.zeros((R, gamma), dtype=f32, device=dev)
+        self.ws_draft = torch.empty(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, R, gamma, V, r)),
+                                    dtype=torch.uint8, device=dev)
+        self.ws_verify = torch.empty(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, R, gamma, V, r)),
+                                     dtype=torch.uint8, device=dev)
+
+    def draft(self, inp, temperature, seed, rnd, stream=None):
+        for k in range(self.gamma):
+            dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok, self.q,
+                               self.stats, k, temperature, seed, rnd, self.ws_draft, stream)
+
+    def confidence(self, inp, stream=None):
+        dsp.dsp_confidence(inp["h"], inp["E"], inp["anchor"], self.tok, inp["w"], inp["T"],
+                           inp["offset"], self.c, stream)
+
+    def schedule(self, inp, mode=None, tau0=None, stream=None):
+        mode = inp["mode"] if mode is None else mode
+        tau0 = inp["tau0"] if tau0 is None else tau0
+        dsp.dsp_schedule(self.c, inp["sps"], inp["B_max"], tau0, mode, self.len, self.a, self.B,
+                         stream)
+
+    def verify(self, inp, temperature, seed, rnd, stream=None):
+        dsp.dsp_verify(inp["target"], inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok,
+                       self.q, self.stats, self.len, self.accept, self.n_accept, self.y, self.p,
+                       temperature, seed, rnd, self.ws_verify, stream)
+
+    def run(self, inp, temperature, seed, rnd, mode=None, tau0=None, stream=None):
+        self.draft(inp, temperature, seed, rnd, stream)
+        self.confidence(inp, stream)
+        self.schedule(inp, mode, tau0, stream)
+        self.verify(inp, temperature, seed, rnd, stream)
+        return self

@@ -1,0 +1,194 @@
+/*
+ * dsp.h -- C-ABI of libdsp.so: the per-token hot path of DSpark
+ * confidence-scheduled speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One decode round is
+ *     for k in 0..gamma-1: dsp_draft_step(k)      semi-autoregressive draft
+ *     dsp_confidence                               confidence head + STS
+ *     dsp_schedule                                 hardware-aware prefix scheduler
+ *     dsp_verify                                   lossless verification
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller, row-major with
+ *     the last index contiguous and no padding.  The library never allocates or
+ *     frees memory; scratch comes from a caller workspace sized by
+ *     dsp_workspace_size().
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No call synchronises the host; lengths and batch sizes
+ *     stay on the device.  Calls on different streams with different workspaces
+ *     may run concurrently; two calls sharing a workspace must be ordered.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Token ids and lengths are int32; V < 2^31.  seed is 64-bit, round 32-bit.
+ *   - Randomness: u(seed, round, request, position, purpose) in [0, 1) is the top
+ *     24 bits of word 0 of Philox4x32-10 with counter (round, request, position,
+ *     purpose) and key (seed low, seed high), divided by 2^24.  Purposes:
+ *     0 draft sample, 1 accept test, 2 correction / bonus draw.
+ *   - Errors: argument problems return DSP_ERR_INVALID_ARG and shapes outside the
+ *     kernels' support DSP_ERR_UNSUPPORTED, both before any HIP call; a workspace
+ *     that is too small returns DSP_ERR_WORKSPACE; a failed launch returns
+ *     DSP_ERR_HIP.  dsp_last_error() gives a thread-local explanation.  Faults
+ *     inside kernels surface at the caller's next synchronisation.  No C++
+ *     exception crosses this boundary.
+ *
+ * Sizes supported: R >= 1, 1 <= gamma <= 64, V >= 1, 8 <= r <= 256 with
+ * r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
+ */
+#ifndef DSP_H
+#define DSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSP_OK = 0,
+    DSP_ERR_INVALID_ARG = 1,
+    DSP_ERR_UNSUPPORTED = 2,
+    DSP_ERR_WORKSPACE = 3,
+    DSP_ERR_HIP = 4
+} dsp_status;
+
+typedef enum { DSP_F32 = 0, DSP_BF16 = 1 } dsp_dtype;
+
+typedef enum { DSP_WS_DRAFT = 0, DSP_WS_VERIFY = 1 } dsp_ws_kind;
+
+/* Static text for a status code. */
+const char* dsp_status_string(dsp_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* dsp_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int dsp_version(void);
+
+/* Bytes of workspace dsp_draft_step (DSP_WS_DRAFT) or dsp_verify (DSP_WS_VERIFY)
+ * needs for these sizes; 0 for invalid sizes. */
+size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
+
+/*
+ * dsp_draft_step -- one draft position k for all R requests.
+ *
+ * Semi-autoregressive draft with the Markov head (DSpark paper summaries: page
+ * "DeepSeek联合北大最新文章DSpark", two-stage design, sequential head: the
+ * previous token enters the next position's distribution through a low-rank
+ * matrix; page "DSpark.让每一轮计算，多走几步", Markov-head paragraph: a low-rank
+ * transition table adds a bias to the vocabulary before each sample; page
+ * "DeepSeek DSpark 技术解析" section 四: only the token id is passed forward).
+ *
+ * For each request n:
+ *   prev     = anchor[n] if k == 0 else tok[n, k-1]   (prev < 0: no bias)
+ *   logit_v  = base[n, k, v] + sum_i E[prev, i] * W2[v, i]   (fp32)
+ *   greedy (temperature == 0): tok[n,k] = argmax_v logit_v (lowest index on
+ *     ties), q[n,k] = 1, stats[n,k] = (max logit, 0)
+ *   sampling: pi_v proportional to exp((logit_v - M) / temperature), M = max;
+ *     tok[n,k] = min{v : sum_{i<=v} pi_i > u(seed, round, n, k, 0)};
+ *     q[n,k] = pi of that token; stats[n,k] = (M, log sum exp((logit - M)/T))
+ *
+ * base   [R, gamma, V] fp32 or bf16 (dtype)   draft base logits of the backbone
+ * E      [V, r] bf16   Markov embedding; row x is the embedding of token x
+ * W2     [V, r] bf16   low-rank output factor stored transposed: W2[v, i] is
+ *                      element (i, v) of the r x V matrix
+ * anchor [R]  int32    the token the target emitted last (x_{-1})
+ * tok    [R, gamma] int32   column k written, column k-1 read (k >= 1)
+ * q      [R, gamma] f32     column k written
+ * stats  [R, gamma, 2] f32  column k written
+ * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
+ */
+dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
+                          const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
+                          float* stats, int R, int gamma, int V, int r, int k,
+                          float temperature, uint64_t seed, uint32_t round, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * dsp_confidence -- confidence head with sequential temperature scaling.
+ *
+ * Page "DeepSeek联合北大最新文章DSpark", section 2.1: c_k is the probability that
+ * draft token k is accepted given that every earlier one was; it is a sigmoid of
+ * a linear map of [h_k; W1[x_{k-1}]]; temperatures fitted left to right per
+ * position calibrate the cumulative survival (the same section, sequential
+ * temperature scaling).
+ *
+ *   y       = sum_{i<d} w[i] h[n,k,i] + sum_{i<r} w[d+i] E[prev,i]   (fp64)
+ *   c[n,k]  = 1 / (1 + exp(-(y + offset[n]) / T[k]))   rounded to fp32
+ * prev = anchor[n] for k = 0, tok[n, k-1] otherwise (prev < 0 drops the E term).
+ *
+ * h [R, gamma, d] bf16; E [V, r] bf16; anchor [R]; tok [R, gamma];
+ * w [d + r] f32; T [gamma] f32 (> 0); offset [R] f32 or NULL; c [R, gamma] f32.
+ */
+dsp_status dsp_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
+                          const int32_t* tok, const float* w, const float* T,
+                          const float* offset, float* c, int R, int gamma, int d, int V, int r,
+                          void* stream);
+
+/*
+ * dsp_schedule -- hardware-aware prefix scheduler.
+ *
+ * Page "DeepSeek联合北大最新文章DSpark", section 2.2: choose the verify lengths
+ * l_r maximising Theta = tau * SPS(B), B = sum_r (1 + l_r), tau = sum_r
+ * sum_{j <= l_r} a_{r,j}, SPS a profiled lookup table; solved by sorting every
+ * candidate by survival probability, admitting one by one, stopping as soon as
+ * the throughput stops rising.  Survival a_{r,j} = c_{r,1} x ... x c_{r,j}
+ * (page "DSpark.让每一轮计算，多走几步", section 写得长，不如验得值).
+ *
+ *   a[r,j]  = fl32(a[r,j-1] * c[r,j]) left to right
+ *   order   : a descending, then r ascending, then j ascending (stable)
+ *   tau_n   = tau0 + sum of the n best a, each truncated to a multiple of 2^-48
+ *             (exact fixed point, so the sum is independent of evaluation order)
+ *   Theta_n = double(tau_n) * SPS(R + n);  admit the n-th candidate while
+ *             Theta_n > Theta_{n-1} and R + n <= B_max
+ *   len[r]  = admitted candidates of request r;  *B = R + sum_r len[r]
+ * mode 0 verifies everything: len[r] = gamma, *B = R (1 + gamma); a still written.
+ *
+ * c [R, gamma] f32 in [0, 1]; sps [B_max] f32 with sps[B-1] = SPS(B); B_max >= R;
+ * tau0 >= 0; len [R] int32; a [R, gamma] f32; B [1] int32 (all device memory).
+ * Runs as one workgroup; mode 1 needs R * gamma <= 16384.
+ */
+dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0, int mode,
+                        int32_t* len, float* a, int32_t* B, int R, int gamma, void* stream);
+
+/*
+ * dsp_verify -- lossless verification of the scheduled prefixes.
+ *
+ * Accept rule, residual and bonus token: page "DSpark.让每一轮计算，多走几步",
+ * lossless section (keep the accepted prefix, one correction token after the
+ * first rejection, one extra token when everything passed; greedy mode accepts
+ * only an identical choice); page "为什么DSpark 可以加速推理？", section on the
+ * mathematics of speculative decoding (acceptance min(1, p/q), residual
+ * max(0, p - q) normalised).
+ *
+ * For each request n with l = len[n] (0 <= l <= gamma):
+ *   p_j = softmax(target[n, j, :] / temperature), j = 0..l
+ *   j < l, sampling: accept[n,j] = u(seed, round, n, j, 1) <= min(1, p_j(x_j)/q[n,j])
+ *          greedy (temperature == 0): accept[n,j] = (x_j == argmax target[n,j,:])
+ *   n_accept[n] = first j < l with accept 0, else l
+ *   y[n]: if n_accept < l: sampling draws from max(0, p_m - q_m) normalised,
+ *         m = n_accept, q_m the full draft row at position m recomputed from base,
+ *         E, W2 and stats[n, m] (from p_m if that mass is zero); greedy: argmax
+ *         of target row m.  If n_accept == l: a draw from p_l (greedy: argmax).
+ *         Draws use u(seed, round, n, n_accept, 2) and the inverse-CDF rule of
+ *         dsp_draft_step.
+ *   accept[n,j] = -1 and p[n,j] = 0 for j >= l; p[n,j] = p_j(x_j) for j < l
+ *   (greedy: 1 if accepted else 0).
+ *
+ * target [R, gamma+1, V] and base [R, gamma, V] of the same dtype; E, W2 as for
+ * dsp_draft_step; anchor [R]; tok, q [R, gamma] and stats [R, gamma, 2] as
+ * written by dsp_draft_step; len [R]; outputs accept [R, gamma] int8,
+ * n_accept [R] int32, y [R] int32, p [R, gamma] f32.
+ * ws >= dsp_workspace_size(DSP_WS_VERIFY, R, gamma, V, r) bytes.
+ */
+dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, const uint16_t* E,
+                      const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
+                      const float* q, const float* stats, const int32_t* len, int8_t* accept,
+                      int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
+                      float temperature, uint64_t seed, uint32_t round, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSP_H */

@@ -142,23 +142,21 @@ int orc_markov_logits(int V, int r, const void* base_row, int dtype,
     return 0;
 }
 
-/* Tempered softmax statistics in fp64: z_v = logit_v / T, m = max z,
- * prob_v = exp(z_v - m) / sum exp(z - m).  stats = (m, log-normaliser). */
+/* Tempered softmax in fp64: M = max logit, prob_v = exp((logit_v - M) / T) / Z
+ * with Z = sum_v exp((logit_v - M) / T).  stats = (M, Z). */
 int orc_softmax(int V, const float* logit, double temperature, double* prob, double* stats)
 {
     if (V <= 0 || !(temperature > 0.0)) return 1;
-    double m = -INFINITY;
-    for (int v = 0; v < V; ++v) {
-        const double z = (double)logit[v] / temperature;
-        if (z > m) m = z;
-    }
+    double M = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if ((double)logit[v] > M) M = (double)logit[v];
     double Z = 0.0;
     for (int v = 0; v < V; ++v) {
-        prob[v] = exp((double)logit[v] / temperature - m);
+        prob[v] = exp(((double)logit[v] - M) / temperature);
         Z += prob[v];
     }
     for (int v = 0; v < V; ++v) prob[v] /= Z;
-    if (stats) { stats[0] = m; stats[1] = m + log(Z); }
+    if (stats) { stats[0] = M; stats[1] = Z; }
     return 0;
 }
 
@@ -211,7 +209,7 @@ static int argmax_f32(int V, const float* x)
 /*   prev = anchor (k = 0) else x_{k-1}; logits via the Markov head;         */
 /*   greedy (temperature == 0): x_k = argmax, q = 1;                         */
 /*   sampling: x_k = inverse CDF of softmax(logits / T) at u(seed, round,     */
-/*   req, k, purpose 0); q = prob of x_k; stats = (max z, log-normaliser).   */
+/*   req, k, purpose 0); q = prob of x_k; stats = (max logit, Z).            */
 /* flag[i,k] = 1 when the decision is within rounding reach of a boundary:   */
 /*   sampling: u within 1e-6 of the CDF on either side of x_k;               */
 /*   greedy: top-2 logit gap within the bias summation bound plus 2 ulp.     */

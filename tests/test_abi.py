@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every symbol include/dsp.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsp.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from draft_sampling_lossless_markov_amd import dsp
+    if not os.path.exists(dsp.LIB_PATH):
+        from draft_sampling_lossless_markov_amd import build
+        build.build()
+    return dsp.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsp_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    from draft_sampling_lossless_markov_amd import dsp
+    names = declared_functions()
+    assert set(names) == set(dsp.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", dsp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dsp_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_status_strings_and_version(L):
+    assert L.dsp_status_string(0) == b"DSP_OK"
+    assert L.dsp_status_string(3) == b"DSP_ERR_WORKSPACE"
+    assert L.dsp_version() >= 100
+
+
+def test_workspace_sizes(L):
+    from draft_sampling_lossless_markov_amd import dsp
+    assert dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 0, 4, 32, 8) == 0
+    a = dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 64, 7, 151936, 256)
+    assert a == 64 * ((151936 + 255) // 256) * 8
+    b = dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, 64, 7, 151936, 256)
+    assert b > 64 * 8 * 19 * 8
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation returns first
+
+
+def _draft(L, **kw):
+    a = dict(base=FAKE, dtype=1, E=FAKE, W2=FAKE, anchor=FAKE, tok=FAKE, q=FAKE, stats=FAKE,
+             R=4, gamma=4, V=32, r=8, k=0, temperature=1.0, seed=0, round=0, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return L.dsp_draft_step(*[C.c_void_p(v) if isinstance(v, int) and k in
+                              ("base", "E", "W2", "anchor", "tok", "q", "stats", "ws") else v
+                              for k, v in a.items()])
+
+
+def test_draft_validation(L):
+    assert _draft(L, base=0) == 1
+    assert _draft(L, dtype=7) == 1
+    assert _draft(L, R=0) == 1
+    assert _draft(L, V=-1) == 1
+    assert _draft(L, k=4) == 1
+    assert _draft(L, k=-1) == 1
+    assert _draft(L, temperature=-0.5) == 1
+    assert _draft(L, temperature=float("nan")) == 1
+    assert _draft(L, gamma=65) == 2
+    assert _draft(L, r=12) == 2
+    assert _draft(L, r=264) == 2
+    assert _draft(L, ws_bytes=8) == 3
+    assert _draft(L, ws=0) == 3
+    assert _draft(L, base=FAKE + 4) == 1
+    assert b"16-byte" in L.dsp_last_error()
+
+
+def test_schedule_validation(L):
+    P = C.c_void_p
+    f = L.dsp_schedule
+    assert f(P(0), P(FAKE), 20, 0.0, 1, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), 3, 0.0, 1, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), 20, -1.0, 1, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), 20, 0.0, 2, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), 10 ** 6, 0.0, 1, P(FAKE), P(FAKE), P(FAKE), 4097, 4, None) == 2
+    assert b"16384" in L.dsp_last_error()
+
+
+def test_confidence_and_verify_validation(L):
+    P = C.c_void_p
+    assert L.dsp_confidence(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(0), P(FAKE), None, P(FAKE),
+                            4, 4, 16, 32, 8, None) == 1
+    assert L.dsp_confidence(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE),
+                            4, 4, -1, 32, 8, None) == 1
+    two = [P(FAKE)] * 2
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0, 0, 0, P(FAKE), 16, None)
+    assert v == 3   # workspace too small
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 12, 1.0, 0, 0, P(FAKE), 1 << 20, None)
+    assert v == 2
+    v = L.dsp_verify(P(0), P(FAKE), 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0, 0, 0, P(FAKE), 1 << 20,
+                     None)
+    assert v == 1

@@ -205,7 +205,9 @@ def test_softmax_matches_scipy(orc):
         p, st = orc.softmax(x, T)
         ref = sp_softmax(x.astype(np.float64) / T)
         np.testing.assert_allclose(p, ref, rtol=1e-13, atol=1e-300)
-        assert abs(st[1] - logsumexp(x.astype(np.float64) / T)) < 1e-12
+        xd = x.astype(np.float64)
+        assert st[0] == xd.max()
+        assert abs(st[0] / T + np.log(st[1]) - logsumexp(xd / T)) < 1e-12
 
 
 def test_inverse_cdf_matches_searchsorted(orc):

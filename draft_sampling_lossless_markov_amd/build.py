@@ -21,17 +21,17 @@ def _hipcc():
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def _flags():
+def _flags(extra=()):
     # packed-fp32 instructions are disabled: the compiler must not form
     # v_pk_{add,mul,fma}_f32 from scalar fp32 code.
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
+    return [*extra, "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-result"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [_hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [_hipcc(), *_flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -39,23 +39,23 @@ def _compile(src):
     return obj, noise
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, lib: str = LIB, build_dir: str = BUILD, extra=()) -> str:
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, build_dir, extra), SOURCES))
     for _, noise in results:
         if verbose and noise.strip():
             print(noise)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp,
            *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(LIB)
-    return LIB
+        print(lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -50,6 +50,8 @@ dsp_status check_markov(int R, int gamma, int V, int r)
     if (gamma > dsp::kGammaMax)
         return fail(DSP_ERR_UNSUPPORTED, "gamma = %d exceeds the supported maximum %d", gamma,
                     dsp::kGammaMax);
+    if (V > dsp::kVocabMax)
+        return fail(DSP_ERR_UNSUPPORTED, "V = %d exceeds the supported maximum %d", V, dsp::kVocabMax);
     if (r > 256 || (r % 8) != 0)
         return fail(DSP_ERR_UNSUPPORTED, "r = %d: the bias kernels need r %% 8 == 0 and r <= 256", r);
     if ((int64_t)R * (gamma + 1) > (int64_t)INT32_MAX / 2)
@@ -87,7 +89,7 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
                           const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
-                          float* stats, int R, int gamma, int V, int r, int k,
+                          double* stats, int R, int gamma, int V, int r, int k,
                           float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream)
 {
@@ -145,7 +147,7 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
         return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: B_max = %d < R = %d", B_max, R);
     if (!(tau0 >= 0.0) || !(tau0 < 1e6))
         return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: tau0 must be in [0, 1e6)");
-    if ((int64_t)R * gamma > dsp::kSchedMaxCand)
+    if (mode == 1 && (int64_t)R * gamma > dsp::kSchedMaxCand)
         return fail(DSP_ERR_UNSUPPORTED, "dsp_schedule: R * gamma = %lld exceeds %d",
                     (long long)R * gamma, dsp::kSchedMaxCand);
     const uint64_t S0 = (uint64_t)std::floor(tau0 * 281474976710656.0);
@@ -156,7 +158,7 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
 
 dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, const uint16_t* E,
                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
-                      const float* q, const float* stats, const int32_t* len, int8_t* accept,
+                      const float* q, const double* stats, const int32_t* len, int8_t* accept,
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
                       float temperature, uint64_t seed, uint32_t round, void* ws,
                       size_t ws_bytes, void* stream)

@@ -26,18 +26,29 @@ __global__ __launch_bounds__(256) void confidence_kernel(
     const uint16_t* hr = h + row * d;
     double acc = 0.0;
     if ((d & 7) == 0) {
-        for (int i = lane * 8; i < d; i += kWave * 8) {
-            const uint4 u = load_nt16(hr + i);
-            const float4 w0 = *reinterpret_cast<const float4*>(w + i);
-            const float4 w1 = *reinterpret_cast<const float4*>(w + i + 4);
-            acc += (double)w0.x * (double)__uint_as_float(u.x << 16);
-            acc += (double)w0.y * (double)__uint_as_float(u.x & 0xFFFF0000u);
-            acc += (double)w0.z * (double)__uint_as_float(u.y << 16);
-            acc += (double)w0.w * (double)__uint_as_float(u.y & 0xFFFF0000u);
-            acc += (double)w1.x * (double)__uint_as_float(u.z << 16);
-            acc += (double)w1.y * (double)__uint_as_float(u.z & 0xFFFF0000u);
-            acc += (double)w1.z * (double)__uint_as_float(u.w << 16);
-            acc += (double)w1.w * (double)__uint_as_float(u.w & 0xFFFF0000u);
+        // issue up to four 16-byte loads per lane before accumulating
+        for (int i0 = lane * 8; i0 < d; i0 += 4 * kWave * 8) {
+            uint4 u[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = i0 + t * kWave * 8;
+                u[t] = (i < d) ? load_nt16(hr + i) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = i0 + t * kWave * 8;
+                if (i >= d) break;
+                const float4 w0 = *reinterpret_cast<const float4*>(w + i);
+                const float4 w1 = *reinterpret_cast<const float4*>(w + i + 4);
+                acc += (double)w0.x * (double)__uint_as_float(u[t].x << 16);
+                acc += (double)w0.y * (double)__uint_as_float(u[t].x & 0xFFFF0000u);
+                acc += (double)w0.z * (double)__uint_as_float(u[t].y << 16);
+                acc += (double)w0.w * (double)__uint_as_float(u[t].y & 0xFFFF0000u);
+                acc += (double)w1.x * (double)__uint_as_float(u[t].z << 16);
+                acc += (double)w1.y * (double)__uint_as_float(u[t].z & 0xFFFF0000u);
+                acc += (double)w1.z * (double)__uint_as_float(u[t].w << 16);
+                acc += (double)w1.w * (double)__uint_as_float(u[t].w & 0xFFFF0000u);
+            }
         }
     } else {
         for (int i = lane; i < d; i += kWave) acc += (double)w[i] * (double)bf16_to_f32(hr[i]);

@@ -148,7 +148,10 @@ __device__ __forceinline__ float2 lse_merge(float2 a, float2 b, float it)
 }
 
 // ---------------------------------------------------------------------------
-// logit loads (fp32 or bf16 rows), 8 consecutive values
+// logit loads (fp32 or bf16 rows), 8 consecutive values.  `load8` unpacks to
+// fp32; `load8_raw` keeps the loaded bits (one 16-byte word per 8 bf16 values,
+// two per 8 fp32 values) and `raw_at` unpacks element e later, so prefetched
+// rows occupy half the registers for bf16.  Columns past V read as -inf.
 // ---------------------------------------------------------------------------
 template <typename LT>
 struct Logit;
@@ -156,45 +159,73 @@ struct Logit;
 template <>
 struct Logit<float> {
     static constexpr int kVecAlign = 4;   // elements per 16 bytes
+    static constexpr int kRaw = 2;        // 16-byte words per 8 elements
     __device__ static __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
-    // x[0..7] = row[v0 .. v0+7]; -inf past V.  `fast` when the 8 values are in
-    // range and 16-byte aligned.
+    __device__ static __forceinline__ void load8_raw(const float* row, int v0, int V, bool fast,
+                                                     uint4 r[2])
+    {
+        if (fast) {
+            r[0] = load_nt16(row + v0);
+            r[1] = load_nt16(row + v0 + 4);
+        } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                w[e] = (v0 + e < V) ? __float_as_uint(row[v0 + e]) : 0xFF800000u;
+            r[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            r[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    }
+    __device__ static __forceinline__ float raw_at(const uint4 r[2], int e)
+    {
+        const uint4 q = r[e >> 2];
+        const uint32_t w = ((e & 3) == 0) ? q.x : ((e & 3) == 1) ? q.y : ((e & 3) == 2) ? q.z : q.w;
+        return __uint_as_float(w);
+    }
     __device__ static __forceinline__ void load8(const float* row, int v0, int V, bool fast,
                                                  float x[8])
     {
-        if (fast) {
-            const uint4 a = load_nt16(row + v0);
-            const uint4 b = load_nt16(row + v0 + 4);
-            x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
-            x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
-            x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
-            x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
-        } else {
+        uint4 r[2];
+        load8_raw(row, v0, V, fast, r);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (v0 + e < V) ? row[v0 + e] : -INFINITY;
-        }
+        for (int e = 0; e < 8; ++e) x[e] = raw_at(r, e);
     }
 };
 
 template <>
 struct Logit<uint16_t> {
     static constexpr int kVecAlign = 8;
+    static constexpr int kRaw = 1;
     __device__ static __forceinline__ float at(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ static __forceinline__ void load8_raw(const uint16_t* row, int v0, int V, bool fast,
+                                                     uint4 r[1])
+    {
+        if (fast) {
+            r[0] = load_nt16(row + v0);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = (v0 + 2 * e < V) ? row[v0 + 2 * e] : 0xFF80u;
+                const uint32_t hi = (v0 + 2 * e + 1 < V) ? row[v0 + 2 * e + 1] : 0xFF80u;
+                w[e] = lo | (hi << 16);
+            }
+            r[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    __device__ static __forceinline__ float raw_at(const uint4 r[1], int e)
+    {
+        const uint4 q = r[0];
+        const uint32_t w = ((e >> 1) == 0) ? q.x : ((e >> 1) == 1) ? q.y : ((e >> 1) == 2) ? q.z : q.w;
+        return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    }
     __device__ static __forceinline__ void load8(const uint16_t* row, int v0, int V, bool fast,
                                                  float x[8])
     {
-        if (fast) {
-            const uint4 u = load_nt16(row + v0);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        uint4 r[1];
+        load8_raw(row, v0, V, fast, r);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[2 * e] = __uint_as_float(w[e] << 16);
-                x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (v0 + e < V) ? bf16_to_f32(row[v0 + e]) : -INFINITY;
-        }
+        for (int e = 0; e < 8; ++e) x[e] = raw_at(r, e);
     }
 };
 

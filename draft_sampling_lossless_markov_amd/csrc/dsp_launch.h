@@ -9,12 +9,14 @@ namespace dsp {
 
 constexpr int kSchedMaxCand = 16384;   // R * gamma limit of the one-workgroup scheduler
 constexpr int kGammaMax = 64;
+constexpr int kVocabMax = 2048 * 256;  // pick workgroups hold up to 8 tiles per thread
 
 size_t draft_workspace_bytes(int R, int V);
 size_t verify_workspace_bytes(int R, int gamma, int V);
+int pass_req_per_wg(int count_max, int n_vt);
 
 hipError_t launch_draft_step(const void* base, bool bf16, const uint16_t* E, const uint16_t* W2,
-                             const int32_t* anchor, int32_t* tok, float* q, float* stats, int R,
+                             const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, float temperature, uint64_t seed,
                              uint32_t round, void* ws, hipStream_t s);
 
@@ -28,7 +30,7 @@ hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t
 
 hipError_t launch_verify(const void* target, const void* base, bool bf16, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
-                         const float* q, const float* stats, const int32_t* len, int8_t* accept,
+                         const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
                          float temperature, uint64_t seed, uint32_t round, void* ws,
                          hipStream_t s);

@@ -18,7 +18,7 @@ class Round:
         i32, f32 = torch.int32, torch.float32
         self.tok = torch.zeros((R, gamma), dtype=i32, device=dev)
         self.q = torch.zeros((R, gamma), dtype=f32, device=dev)
-        self.stats = torch.zeros((R, gamma, 2), dtype=f32, device=dev)
+        self.stats = torch.zeros((R, gamma, 2), dtype=torch.float64, device=dev)
         self.c = torch.zeros((R, gamma), dtype=f32, device=dev)
         self.len = torch.zeros((R,), dtype=i32, device=dev)
         self.a = torch.zeros((R, gamma), dtype=f32, device=dev)

@@ -30,8 +30,8 @@
  *     inside kernels surface at the caller's next synchronisation.  No C++
  *     exception crosses this boundary.
  *
- * Sizes supported: R >= 1, 1 <= gamma <= 64, V >= 1, 8 <= r <= 256 with
- * r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
+ * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
+ * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
  */
 #ifndef DSP_H
 #define DSP_H
@@ -85,7 +85,7 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  *     ties), q[n,k] = 1, stats[n,k] = (max logit, 0)
  *   sampling: pi_v proportional to exp((logit_v - M) / temperature), M = max;
  *     tok[n,k] = min{v : sum_{i<=v} pi_i > u(seed, round, n, k, 0)};
- *     q[n,k] = pi of that token; stats[n,k] = (M, log sum exp((logit - M)/T))
+ *     q[n,k] = pi of that token; stats[n,k] = (M, Z), Z = sum_v exp((logit_v - M)/T)
  *
  * base   [R, gamma, V] fp32 or bf16 (dtype)   draft base logits of the backbone
  * E      [V, r] bf16   Markov embedding; row x is the embedding of token x
@@ -94,12 +94,12 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  * anchor [R]  int32    the token the target emitted last (x_{-1})
  * tok    [R, gamma] int32   column k written, column k-1 read (k >= 1)
  * q      [R, gamma] f32     column k written
- * stats  [R, gamma, 2] f32  column k written
+ * stats  [R, gamma, 2] f64  column k written
  * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
  */
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
                           const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
-                          float* stats, int R, int gamma, int V, int r, int k,
+                          double* stats, int R, int gamma, int V, int r, int k,
                           float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream);
 
@@ -175,14 +175,14 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
  *   (greedy: 1 if accepted else 0).
  *
  * target [R, gamma+1, V] and base [R, gamma, V] of the same dtype; E, W2 as for
- * dsp_draft_step; anchor [R]; tok, q [R, gamma] and stats [R, gamma, 2] as
+ * dsp_draft_step; anchor [R]; tok, q [R, gamma] and stats [R, gamma, 2] (f64) as
  * written by dsp_draft_step; len [R]; outputs accept [R, gamma] int8,
  * n_accept [R] int32, y [R] int32, p [R, gamma] f32.
  * ws >= dsp_workspace_size(DSP_WS_VERIFY, R, gamma, V, r) bytes.
  */
 dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, const uint16_t* E,
                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
-                      const float* q, const float* stats, const int32_t* len, int8_t* accept,
+                      const float* q, const double* stats, const int32_t* len, int8_t* accept,
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
                       float temperature, uint64_t seed, uint32_t round, void* ws,
                       size_t ws_bytes, void* stream);

@@ -48,7 +48,7 @@ def test_workspace_sizes(L):
     from draft_sampling_lossless_markov_amd import dsp
     assert dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 0, 4, 32, 8) == 0
     a = dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 64, 7, 151936, 256)
-    assert a == 64 * ((151936 + 255) // 256) * 8
+    assert a == 64 * ((151936 + 255) // 256) * 16
     b = dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, 64, 7, 151936, 256)
     assert b > 64 * 8 * 19 * 8
 

@@ -93,7 +93,19 @@ def main():
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy five times (the known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures the one-GPU path only; --gpus {args.gpus} is not supported "

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
                            sh.lg + wave * 64);
         __syncthreads();
         const float z = sh.lg[tid];
-        double e1[1] = {(z == -INFINITY) ? 0.0 : (double)exp_w((z - M) * inv_temp)};
+        double e1[1] = {(double)wexp(z - M, fold_itl(inv_temp))};
         double b2;
         const int loc = block_locate<1>(e1, target - before, &b2, sh);
         if (tid == loc) {

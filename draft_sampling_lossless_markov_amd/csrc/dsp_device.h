@@ -29,6 +29,17 @@ __device__ __forceinline__ uint4 load_nt16(const void* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load of the calling wave, which would drain the logit rows
+// prefetched for the next sub-block at each barrier; kernels whose global loads
+// land in registers (never read by another wave) use this one instead.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u)

@@ -35,6 +35,12 @@ __device__ __forceinline__ float exp_w(float x)
     return __builtin_amdgcn_exp2f(x * 1.44269502162933349609375f);
 }
 
+// exp((z - ref) / T) with itL = log2(e) / T folded once per kernel; every pass,
+// combine and rescan of a row uses this same form so partials and rescans agree.
+__device__ __forceinline__ float wexp(float d, float itL) { return __builtin_amdgcn_exp2f(d * itL); }
+
+__host__ __device__ inline float fold_itl(float inv_temp) { return inv_temp * 1.44269502162933349609375f; }
+
 // Partial of one 256-wide vocabulary tile of one row.
 //   softmax pass: m = max logit, s = sum exp((logit - m) / T) (fp64)
 //   greedy pass:  m = max logit, idx = lowest index of the max
@@ -83,8 +89,10 @@ constexpr int pass_min_blocks() { return (sizeof(LT) == 2 && KIND != kResidual) 
 template <typename LT, int KIND>
 __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_kernel(PassArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t e_tile[kReqBlock][kRankMax + kERowPad];
-    __shared__ Part red[4][kReqBlock];
+    // double-buffered embedding tiles and cross-wave partials: sub-block i + 1 is
+    // staged and its logit rows requested while sub-block i is computed
+    __shared__ __attribute__((aligned(16))) uint16_t e_tile[2][kReqBlock][kRankMax + kERowPad];
+    __shared__ Part red[2][4][kReqBlock];
     constexpr int RW = Logit<LT>::kRaw;
 
     const int count = (KIND == kResidual) ? *a.count : a.R;
@@ -104,89 +112,118 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_
     const int va = v_blk + 8 * g, vb = v_blk + 32 + 8 * g;
     const bool fa = vec_ok && va + 8 <= V, fb = vec_ok && vb + 8 <= V;
     const float it = a.inv_temp;
+    const float itL = fold_itl(it);
 
     bf16x8 afrag[4][kKSteps];
     load_w2_frags(a.W2, V, r, v_blk, lane, afrag);
 
-    for (int n0 = n_begin; n0 < n_end; n0 += kReqBlock) {
-        // stage the embedding rows of this sub-block's previous tokens: thread t
-        // owns row t / 4 and a quarter of it (one dependent load for the token)
-        {
-            const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
-            const int e = n0 + row;
-            int prev = -1;
-            if (e < n_end) {
-                if constexpr (KIND == kResidual) prev = a.list_prev[e];
-                else prev = prev_token(a.anchor, a.tok, e, gamma, a.k, V);
-            }
-            uint4 u[kRankMax / 32];
+    // embedding rows of sub-block n0 into buffer b: thread t owns row t % 64 and
+    // the quarter t / 64 of it, so a wave writes 64 different rows at one column
+    // (conflict-free LDS stores); two halves keep the staging registers small
+    auto stage_e = [&](int n0, int b) {
+        const int row = threadIdx.x & 63, q4 = threadIdx.x >> 6;
+        const int e = n0 + row;
+        int prev = -1;
+        if (e < n_end) {
+            if constexpr (KIND == kResidual) prev = a.list_prev[e];
+            else prev = prev_token(a.anchor, a.tok, e, gamma, a.k, V);
+        }
 #pragma unroll
-            for (int c = 0; c < kRankMax / 32; ++c) {
-                const int kk = (q4 * (kRankMax / 32) + c) * 8;
+        for (int h = 0; h < 2; ++h) {
+            uint4 u[kRankMax / 64];
+#pragma unroll
+            for (int c = 0; c < kRankMax / 64; ++c) {
+                const int kk = (q4 * (kRankMax / 32) + h * (kRankMax / 64) + c) * 8;
                 u[c] = make_uint4(0, 0, 0, 0);
                 if (prev >= 0 && kk < r) u[c] = *reinterpret_cast<const uint4*>(a.E + (int64_t)prev * r + kk);
             }
 #pragma unroll
-            for (int c = 0; c < kRankMax / 32; ++c)
-                *reinterpret_cast<uint4*>(&e_tile[row][(q4 * (kRankMax / 32) + c) * 8]) = u[c];
+            for (int c = 0; c < kRankMax / 64; ++c)
+                *reinterpret_cast<uint4*>(
+                    &e_tile[b][row][(q4 * (kRankMax / 32) + h * (kRankMax / 64) + c) * 8]) = u[c];
         }
-
-        // logit rows for the epilogue (raw bits), loaded before the MFMA chain
-        uint4 rs[4][2 * RW];
-        uint4 rt[KIND == kResidual ? 4 : 1][2 * RW];
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-            const int e = n0 + 16 * tn + c16;
-            const bool ok = e < n_end;
-            int n = e, m = a.k;
-            if constexpr (KIND == kResidual) {
-                n = ok ? a.list[e] : 0;
-                m = ok ? a.list_m[e] : 0;
-            }
-            const LT* row = base + ((int64_t)(ok ? n : 0) * gamma + m) * V;
-            Logit<LT>::load8_raw(row, ok ? va : V, V, ok && fa, rs[tn]);
-            Logit<LT>::load8_raw(row, ok ? vb : V, V, ok && fb, rs[tn] + RW);
-            if constexpr (KIND == kResidual) {
-                const LT* trow = target + ((int64_t)(ok ? n : 0) * (gamma + 1) + m) * V;
-                Logit<LT>::load8_raw(trow, ok ? va : V, V, ok && fa, rt[tn]);
-                Logit<LT>::load8_raw(trow, ok ? vb : V, V, ok && fb, rt[tn] + RW);
-            }
+    };
+    // raw logit words of N-tile tn of sub-block n0 (request rows for this lane)
+    auto load_raw = [&](int n0, int tn, uint4* rs_tn, uint4* rt_tn) {
+        const int e = n0 + 16 * tn + c16;
+        const bool ok = e < n_end;
+        int n = e, m = a.k;
+        if constexpr (KIND == kResidual) {
+            n = ok ? a.list[e] : 0;
+            m = ok ? a.list_m[e] : 0;
         }
-        __syncthreads();
+        const LT* row = base + ((int64_t)(ok ? n : 0) * gamma + m) * V;
+        Logit<LT>::load8_raw(row, ok ? va : V, V, ok && fa, rs_tn);
+        Logit<LT>::load8_raw(row, ok ? vb : V, V, ok && fb, rs_tn + RW);
+        if constexpr (KIND == kResidual) {
+            const LT* trow = target + ((int64_t)(ok ? n : 0) * (gamma + 1) + m) * V;
+            Logit<LT>::load8_raw(trow, ok ? va : V, V, ok && fa, rt_tn);
+            Logit<LT>::load8_raw(trow, ok ? vb : V, V, ok && fb, rt_tn + RW);
+        }
+    };
 
-        floatx4 acc[4][4];
+    uint4 rs[4][2 * RW];
+    uint4 rt[KIND == kResidual ? 4 : 1][2 * RW];
+    stage_e(n_begin, 0);
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
+    for (int tn = 0; tn < 4; ++tn) load_raw(n_begin, tn, rs[tn], rt[KIND == kResidual ? tn : 0]);
+    lds_barrier();
+
+    int buf = 0;
+    for (int n0 = n_begin; n0 < n_end; n0 += kReqBlock, buf ^= 1) {
+        const int n1 = n0 + kReqBlock;
+        const bool more = n1 < n_end;
+
+        // two halves of two N-tiles each: half the accumulators live at a time, and
+        // the embedding rows of the next sub-block are staged between the halves
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[tn][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int hf = 0; hf < 2; ++hf) {
+        floatx4 acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
             if (ks < ksteps) {
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) {
-                    const bf16x8 b = as_bf16x8(
-                        *reinterpret_cast<const uint4*>(&e_tile[16 * tn + c16][ks * kKStep + 8 * g]));
+                for (int i = 0; i < 2; ++i) {
+                    const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(
+                        &e_tile[buf][16 * (2 * hf + i) + c16][ks * kKStep + 8 * g]));
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[tn][t] = mfma_bf16(afrag[t][ks], b, acc[tn][t]);
+                    for (int t = 0; t < 4; ++t) acc[i][t] = mfma_bf16(afrag[t][ks], b, acc[i][t]);
                 }
             }
         }
+        if (hf == 0 && more) stage_e(n1, buf ^ 1);
 
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-            // biased logits of the 16 slots (-inf past V or past the sub-block)
+        for (int i = 0; i < 2; ++i) {
+            const int tn = 2 * hf + i;
             float z[16];
 #pragma unroll
             for (int s = 0; s < 16; ++s)
-                z[s] = Logit<LT>::raw_at(rs[tn] + (s >> 3) * RW, s & 7) + acc[tn][s >> 2][s & 3];
+                z[s] = Logit<LT>::raw_at(rs[tn] + (s >> 3) * RW, s & 7) + acc[i][s >> 2][s & 3];
+            float xt[KIND == kResidual ? 16 : 1];
+            if constexpr (KIND == kResidual) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s) xt[s] = Logit<LT>::raw_at(rt[tn] + (s >> 3) * RW, s & 7);
+            }
+            // the next sub-block's rows reuse this N-tile's registers
+            if (more) load_raw(n1, tn, rs[tn], rt[KIND == kResidual ? tn : 0]);
             Part res;
             if constexpr (KIND == kGreedy) {
-                ArgMax am{-INFINITY, 0x7fffffff};
+                // slot s maps to increasing vocabulary ids, so the first slot holding
+                // the lane maximum is the lane's lowest-index argmax; masked slots
+                // (past V) come last and carry -inf
+                float m = z[0];
 #pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    const int v = v_blk + slot_voff(g, s);
-                    if (v < V) am = argmax_merge(am, ArgMax{z[s], v});
-                }
+                for (int s = 1; s < 16; ++s) m = fmaxf(m, z[s]);
+                int si = 15;
+#pragma unroll
+                for (int s = 14; s >= 0; --s) si = (z[s] == m) ? s : si;
+                const int v = v_blk + slot_voff(g, si);
+                ArgMax am{m, v < V ? v : 0x7fffffff};
 #pragma unroll
                 for (int o = 16; o < 64; o <<= 1) {
                     ArgMax b;
@@ -201,12 +238,11 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_
                 for (int s = 1; s < 16; ++s) m = fmaxf(m, z[s]);
                 m = fmaxf(m, __shfl_xor(m, 16, kWave));
                 m = fmaxf(m, __shfl_xor(m, 32, kWave));
-                // an all-masked 64-block keeps m = -inf: its weights are exp(nan)
-                // guarded to 0 by using a finite reference
-                const float mref = (m == -INFINITY) ? 0.0f : m;
+                const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked block
                 double sum = 0.0;
 #pragma unroll
-                for (int s = 0; s < 16; ++s) sum += (double)exp_w((z[s] - mref) * it);
+                for (int s = 0; s < 16; s += 2)
+                    sum += (double)(wexp(z[s] - mref, itL) + wexp(z[s + 1] - mref, itL));
                 sum += __shfl_xor(sum, 16, kWave);
                 sum += __shfl_xor(sum, 32, kWave);
                 res = Part{m, 0, sum};
@@ -222,9 +258,8 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_
                     const double invZt = 1.0 / a.row_z[n];
 #pragma unroll
                     for (int s = 0; s < 16; ++s) {
-                        const float xt = Logit<LT>::raw_at(rt[tn] + (s >> 3) * RW, s & 7);
-                        const double pv = (double)exp_w((xt - Mt) * it) * invZt;
-                        const double qv = (double)exp_w((z[s] - Md) * it) * invZd;
+                        const double pv = (double)wexp(xt[s] - Mt, itL) * invZt;
+                        const double qv = (double)wexp(z[s] - Md, itL) * invZd;
                         sum += fmax(pv - qv, 0.0);
                     }
                 }
@@ -232,16 +267,17 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_
                 sum += __shfl_xor(sum, 32, kWave);
                 res = Part{0.f, 0, sum};
             }
-            if (g == 0) red[wave][16 * tn + c16] = res;
+            if (g == 0) red[buf][wave][16 * tn + c16] = res;
         }
-        __syncthreads();
+        }
+        lds_barrier();
         if (threadIdx.x < kReqBlock) {
             const int e = n0 + threadIdx.x;
             if (e < n_end) {
-                Part p = red[0][threadIdx.x];
+                Part p = red[buf][0][threadIdx.x];
 #pragma unroll
                 for (int w = 1; w < 4; ++w) {
-                    const Part b = red[w][threadIdx.x];
+                    const Part b = red[buf][w][threadIdx.x];
                     if constexpr (KIND == kGreedy) {
                         const ArgMax m = argmax_merge(ArgMax{p.m, p.idx}, ArgMax{b.m, b.idx});
                         p.m = m.v;
@@ -249,7 +285,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_
                     } else if constexpr (KIND == kSample) {
                         const float mm = fmaxf(p.m, b.m);
                         if (mm != -INFINITY)
-                            p.s = p.s * (double)exp_w((p.m - mm) * it) + b.s * (double)exp_w((b.m - mm) * it);
+                            p.s = p.s * (double)wexp(p.m - mm, itL) + b.s * (double)wexp(b.m - mm, itL);
                         p.m = mm;
                     } else {
                         p.s += b.s;
@@ -258,7 +294,6 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_
                 a.part[(int64_t)e * a.n_vt + vt] = p;
             }
         }
-        __syncthreads();
     }
 }
 

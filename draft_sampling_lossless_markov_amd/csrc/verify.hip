@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 {
     constexpr int RW = Logit<LT>::kRaw;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const float itL = fold_itl(inv_temp);
     if (blockIdx.x == 0 && tid == 0) *ws.resid_cnt = 0;
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int per_req = (gamma + 1) * spans;
@@ -135,7 +136,9 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += (double)exp_w((Logit<LT>::raw_at(raw[k], e) - mref) * inv_temp);
+            for (int e = 0; e < 8; e += 2)
+                s += (double)(wexp(Logit<LT>::raw_at(raw[k], e) - mref, itL) +
+                              wexp(Logit<LT>::raw_at(raw[k], e + 1) - mref, itL));
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
         if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
@@ -286,8 +289,8 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
             double rho[1] = {0.0};
             const float zd = sh.lg[tid];
             if (v < V && zd != -INFINITY) {
-                const double pv = (double)exp_w((Logit<LT>::at(trow, v) - Mt) * inv_temp) * invZt;
-                const double qv = (double)exp_w((zd - Md) * inv_temp) * invZd;
+                const double pv = (double)wexp(Logit<LT>::at(trow, v) - Mt, fold_itl(inv_temp)) * invZt;
+                const double qv = (double)wexp(zd - Md, fold_itl(inv_temp)) * invZd;
                 rho[0] = fmax(pv - qv, 0.0);
             }
             double b2;
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     const int tsel = block_locate<PER>(w, tgt, &before, sh);
     const LT* trow = target + ((int64_t)n * (gamma + 1) + row_j) * V;
     const int v = tsel * kVocabTile + tid;
-    double e1[1] = {(v < V) ? (double)exp_w((Logit<LT>::at(trow, v) - M) * inv_temp) : 0.0};
+    double e1[1] = {(v < V) ? (double)wexp(Logit<LT>::at(trow, v) - M, fold_itl(inv_temp)) : 0.0};
     double b2;
     const int loc = block_locate<1>(e1, tgt - before, &b2, sh);
     if (tid == 0) y[n] = tsel * kVocabTile + loc;

@@ -22,7 +22,8 @@ sys.path.insert(0, ROOT)
 
 from draft_sampling_lossless_markov_amd import dsp  # noqa: E402
 from draft_sampling_lossless_markov_amd.engine import Round  # noqa: E402
-from draft_sampling_lossless_markov_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
+from draft_sampling_lossless_markov_amd.workloads import (BENCH_LAYOUT, WORKLOADS,  # noqa: E402
+                                                          make_inputs)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 METRIC = "verified draft positions/sec (draft+verify) and % of MI355X HBM roofline"
@@ -121,7 +122,7 @@ def main():
     temp = 0.0 if greedy else wl.temperature
     dsp.lib()
     log(f"workload {wl.name}, {mode}, building {args.sets} input sets")
-    sets = [make_inputs(wl, s, device="cuda") for s in range(args.sets)]
+    sets = [make_inputs(wl, s, device="cuda", layout=BENCH_LAYOUT) for s in range(args.sets)]
     inp0 = sets[0]
     R, g, V, r = inp0["R"], inp0["gamma"], inp0["V"], inp0["r"]
     rd = Round(R, g, V, r)
@@ -197,6 +198,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "R": R, "gamma": g, "V": V, "r": r, "d": inp0["d"],
                    "mode": mode, "scheduler": "on" if wl.mode == 1 else "off (every position verified)",
+                   "base_layout": BENCH_LAYOUT + "-major [gamma, R, V]",
                    "parallelism": "single GPU"},
         "round_roofline": {"algorithmic_bytes": int(A), "t_roof_us": round(A / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                            "frac": round(A / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)},

@@ -40,6 +40,15 @@ dsp_status hip_status(hipError_t e, const char* what)
     return ok();
 }
 
+// strides of a logit tensor argument
+dsp_status check_strides(const char* fn, const char* name, int64_t rs, int64_t ps)
+{
+    if (rs < 0 || ps < 0)
+        return fail(DSP_ERR_INVALID_ARG, "%s: %s strides must be >= 0 (got %lld, %lld)", fn, name,
+                    (long long)rs, (long long)ps);
+    return DSP_OK;
+}
+
 // shapes shared by the Markov-head calls
 dsp_status check_markov(int R, int gamma, int V, int r)
 {
@@ -77,7 +86,7 @@ const char* dsp_status_string(dsp_status s)
 
 const char* dsp_last_error(void) { return g_err; }
 
-int dsp_version(void) { return 100; }
+int dsp_version(void) { return 200; }
 
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 {
@@ -87,8 +96,8 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
     return 0;
 }
 
-dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
-                          const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
+dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
+                          const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
                           double* stats, int R, int gamma, int V, int r, int k,
                           float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream)
@@ -101,6 +110,8 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
     if (st != DSP_OK) return st;
     if (k < 0 || k >= gamma)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: k = %d outside [0, gamma)", k);
+    st = check_strides("dsp_draft_step", "base", base_rs, base_ps);
+    if (st != DSP_OK) return st;
     if (!(temperature >= 0.0f) || std::isinf(temperature))
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: temperature must be finite and >= 0");
     if (!aligned16(base) || !aligned16(E) || !aligned16(W2))
@@ -109,7 +120,8 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
     if (!ws || ws_bytes < need)
         return fail(DSP_ERR_WORKSPACE, "dsp_draft_step: workspace of %zu bytes, %zu needed",
                     ws_bytes, need);
-    return hip_status(dsp::launch_draft_step(base, dtype == DSP_BF16, E, W2, anchor, tok, q,
+    return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
+                                             dtype == DSP_BF16, E, W2, anchor, tok, q,
                                              stats, R, gamma, V, r, k, temperature, seed, round,
                                              ws, static_cast<hipStream_t>(stream)),
                       "dsp_draft_step launch");
@@ -156,7 +168,8 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
                       "dsp_schedule launch");
 }
 
-dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, const uint16_t* E,
+dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                      int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                       const float* q, const double* stats, const int32_t* len, int8_t* accept,
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
@@ -172,13 +185,19 @@ dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, con
     if (st != DSP_OK) return st;
     if (!(temperature >= 0.0f) || std::isinf(temperature))
         return fail(DSP_ERR_INVALID_ARG, "dsp_verify: temperature must be finite and >= 0");
+    st = check_strides("dsp_verify", "target", target_rs, target_ps);
+    if (st != DSP_OK) return st;
+    st = check_strides("dsp_verify", "base", base_rs, base_ps);
+    if (st != DSP_OK) return st;
     if (!aligned16(target) || !aligned16(base) || !aligned16(E) || !aligned16(W2))
         return fail(DSP_ERR_INVALID_ARG, "dsp_verify: target, base, E and W2 must be 16-byte aligned");
     const size_t need = dsp::verify_workspace_bytes(R, gamma, V);
     if (!ws || ws_bytes < need)
         return fail(DSP_ERR_WORKSPACE, "dsp_verify: workspace of %zu bytes, %zu needed", ws_bytes,
                     need);
-    return hip_status(dsp::launch_verify(target, base, dtype == DSP_BF16, E, W2, anchor, tok, q,
+    return hip_status(dsp::launch_verify(target, dsp::RowStrides{target_rs, target_ps}, base,
+                                         dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16, E,
+                                         W2, anchor, tok, q,
                                          stats, len, accept, n_accept, y, p, R, gamma, V, r,
                                          temperature, seed, round, ws,
                                          static_cast<hipStream_t>(stream)),

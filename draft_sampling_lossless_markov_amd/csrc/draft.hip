@@ -25,7 +25,8 @@ namespace dsp {
 // ---------------------------------------------------------------------------
 template <typename LT, bool GREEDY, int PER>
 __global__ __launch_bounds__(256) void draft_pick_kernel(
-    const LT* __restrict__ base, const uint16_t* __restrict__ E, const uint16_t* __restrict__ W2,
+    const LT* __restrict__ base, RowStrides bs, const uint16_t* __restrict__ E,
+    const uint16_t* __restrict__ W2,
     const int32_t* __restrict__ anchor, int32_t* __restrict__ tok, float* __restrict__ q,
     double* __restrict__ stats, int R, int gamma, int V, int r, int k, float inv_temp,
     uint64_t seed, uint32_t round, int n_vt, const Part* __restrict__ part)
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
         const int tsel = block_locate<PER>(w, target, &before, sh);
 
         // rebuild the 256 logits of the chosen tile, 64 per wave
-        const LT* row = base + ((int64_t)n * gamma + k) * V;
+        const LT* row = base + (int64_t)n * bs.rs + (int64_t)k * bs.ps;
         block_logits64<LT>(row, E, W2, V, r, prev, tsel * kVocabTile + wave * 64, lane,
                            sh.lg + wave * 64);
         __syncthreads();
@@ -119,17 +120,17 @@ int pass_req_per_wg(int count_max, int n_vt)
 }
 
 template <typename LT, bool GREEDY, int PER>
-static void launch_pick(const LT* base, const uint16_t* E, const uint16_t* W2,
+static void launch_pick(const LT* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
                         const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                         int gamma, int V, int r, int k, float it, uint64_t seed, uint32_t round,
                         int n_vt, const Part* part, hipStream_t s)
 {
-    hipLaunchKernelGGL((draft_pick_kernel<LT, GREEDY, PER>), dim3(R), dim3(256), 0, s, base, E, W2,
+    hipLaunchKernelGGL((draft_pick_kernel<LT, GREEDY, PER>), dim3(R), dim3(256), 0, s, base, bs, E, W2,
                        anchor, tok, q, stats, R, gamma, V, r, k, it, seed, round, n_vt, part);
 }
 
 template <typename LT>
-static hipError_t launch_draft_t(const LT* base, const uint16_t* E, const uint16_t* W2,
+static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
                                  const int32_t* anchor, int32_t* tok, float* q, double* stats,
                                  int R, int gamma, int V, int r, int k, float temperature,
                                  uint64_t seed, uint32_t round, void* ws, hipStream_t s)
@@ -139,24 +140,29 @@ static hipError_t launch_draft_t(const LT* base, const uint16_t* E, const uint16
     const bool greedy = (temperature == 0.0f);
     const float it = greedy ? 1.0f : 1.0f / temperature;
     PassArgs a{};
-    a.base = base; a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.base = base; a.bs = bs; a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
     a.R = R; a.gamma = gamma; a.V = V; a.r = r; a.k = k; a.inv_temp = it;
     a.n_vt = n_vt;
     a.req_per_wg = pass_req_per_wg(R, n_vt);
     a.part = part;
     const dim3 g1(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
-    if (greedy)
-        hipLaunchKernelGGL((bias_pass_kernel<LT, kGreedy>), g1, dim3(256), 0, s, a);
+    const bool vec = rows_vec(bs, V, 8);
+    if (greedy && vec)
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kGreedy, true>), g1, dim3(256), 0, s, a);
+    else if (greedy)
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kGreedy, false>), g1, dim3(256), 0, s, a);
+    else if (vec)
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kSample, true>), g1, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((bias_pass_kernel<LT, kSample>), g1, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kSample, false>), g1, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int per = (n_vt + 255) / 256;
 #define DSP_PICK(P)                                                                              \
-    (greedy ? launch_pick<LT, true, P>(base, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, it, \
-                                       seed, round, n_vt, part, s)                               \
-            : launch_pick<LT, false, P>(base, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, it, \
-                                        seed, round, n_vt, part, s))
+    (greedy ? launch_pick<LT, true, P>(base, bs, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, \
+                                       it, seed, round, n_vt, part, s)                           \
+            : launch_pick<LT, false, P>(base, bs, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, \
+                                        it, seed, round, n_vt, part, s))
     if (per <= 1) DSP_PICK(1);
     else if (per <= 2) DSP_PICK(2);
     else if (per <= 4) DSP_PICK(4);
@@ -165,15 +171,16 @@ static hipError_t launch_draft_t(const LT* base, const uint16_t* E, const uint16
     return hipGetLastError();
 }
 
-hipError_t launch_draft_step(const void* base, bool bf16, const uint16_t* E, const uint16_t* W2,
+hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
+                             const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, float temperature, uint64_t seed,
                              uint32_t round, void* ws, hipStream_t s)
 {
     if (bf16)
-        return launch_draft_t(static_cast<const uint16_t*>(base), E, W2, anchor, tok, q, stats, R,
+        return launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats, R,
                               gamma, V, r, k, temperature, seed, round, ws, s);
-    return launch_draft_t(static_cast<const float*>(base), E, W2, anchor, tok, q, stats, R, gamma,
+    return launch_draft_t(static_cast<const float*>(base), bs, E, W2, anchor, tok, q, stats, R, gamma,
                           V, r, k, temperature, seed, round, ws, s);
 }
 

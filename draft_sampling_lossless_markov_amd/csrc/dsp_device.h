@@ -10,7 +10,7 @@ namespace dsp {
 
 constexpr int kWave = 64;
 constexpr int kRankMax = 256;             // largest Markov rank r the bias kernels hold
-constexpr int kKStep = 32;                // K of one v_mfma_f32_16x16x32_bf16
+constexpr int kKStep = 16;                // K of one v_mfma_f32_32x32x16_bf16
 constexpr int kKSteps = kRankMax / kKStep;
 constexpr int kVocabTile = 256;           // vocabulary columns per draft workgroup
 constexpr int kReqBlock = 64;             // requests per MFMA sub-block (4 N-tiles of 16)
@@ -19,6 +19,7 @@ constexpr int kVerifyChunk = 8192;        // vocabulary per verify row work item
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load that does not allocate in the caches (logit rows are
@@ -49,9 +50,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u)
     return r;
 }
 
-__device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c)
+// D = A B + C with A 32x16 (W2 rows), B 16x32 (embedding rows), fp32 C.  On
+// gfx950 this form issues at twice the rate of the 16x16x32 one.  Lane l holds
+// A row l % 32 and B column l % 32 at k = 8 (l / 32) .. +7, and D column l % 32
+// at rows 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..15.
+__device__ __forceinline__ floatx16 mfma32_bf16(bf16x8 a, bf16x8 b, floatx16 c)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -148,6 +153,57 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a)
     return a;
 }
 
+// ---------------------------------------------------------------------------
+// Combines across lanes l ^ 16 and l ^ 32 with the gfx950 row-swap instructions
+// (v_permlane16_swap / v_permlane32_swap): a register-to-register exchange, no
+// LDS round trip.  permlane16_swap(x, x) returns, in every lane, the values of
+// lanes l and l ^ 16 (in row order), permlane32_swap(x, x) those of l and l ^ 32.
+// Every combine below is commutative, so all lanes of a pair get identical bits.
+// ---------------------------------------------------------------------------
+template <int O>
+__device__ __forceinline__ void xswap(uint32_t x, uint32_t& p, uint32_t& q)
+{
+    static_assert(O == 16 || O == 32, "row swaps exist for 16 and 32 only");
+    if constexpr (O == 16) {
+        const auto v = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        p = v[0];
+        q = v[1];
+    } else {
+        const auto v = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        p = v[0];
+        q = v[1];
+    }
+}
+
+template <int O>
+__device__ __forceinline__ float xmax(float x)
+{
+    uint32_t p, q;
+    xswap<O>(__float_as_uint(x), p, q);
+    return fmaxf(__uint_as_float(p), __uint_as_float(q));
+}
+
+template <int O>
+__device__ __forceinline__ double xsum(double x)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    uint32_t p0, q0, p1, q1;
+    xswap<O>((uint32_t)b, p0, q0);
+    xswap<O>((uint32_t)(b >> 32), p1, q1);
+    const double a = __longlong_as_double((long long)(((uint64_t)p1 << 32) | p0));
+    const double c = __longlong_as_double((long long)(((uint64_t)q1 << 32) | q0));
+    return a + c;
+}
+
+template <int O>
+__device__ __forceinline__ ArgMax xargmax(ArgMax x)
+{
+    uint32_t pv, qv, pi, qi;
+    xswap<O>(__float_as_uint(x.v), pv, qv);
+    xswap<O>((uint32_t)x.i, pi, qi);
+    return argmax_merge(ArgMax{__uint_as_float(pv), (int)pi}, ArgMax{__uint_as_float(qv), (int)qi});
+}
+
 // Online-softmax partial (m, s): s = sum exp((x - m) * it) over a set of
 // logits with maximum m (m = -inf, s = 0 for the empty set).
 __device__ __forceinline__ float2 lse_merge(float2 a, float2 b, float it)
@@ -242,39 +298,36 @@ struct Logit<uint16_t> {
 
 // ---------------------------------------------------------------------------
 // The Markov-bias MFMA tile shared by every kernel that needs biased draft
-// logits.  A wave computes a 64-vocabulary x 16-request block per N-tile:
+// logits.  A wave computes a 64-vocabulary x 32-request block per N-tile:
 //   out[v, n] = sum_i W2[v, i] * E[prev_n, i]
-// with W2 rows as the A operand (M = vocabulary) and embedding rows as the B
-// operand (N = requests).  Lane l of the 16x16 output tile holds request column
-// l % 16 and rows 4 (l / 16) + 0..3.  The vocabulary order inside the 64-block
-// is permuted so that lane group g = l / 16 owns the 16 columns
-// {8g .. 8g+7} and {32+8g .. 32+8g+7}: two 16-byte logit loads per request.
-// Every caller issues the same K order (k-steps 0..ceil(r/32)-1 accumulated
-// into a zero tile), so a vocabulary element's bias is bit-identical wherever
-// it is recomputed.
+// with W2 rows as the A operand (two 32-row M-tiles) and embedding rows as the
+// B operand (N = requests).  The W2 rows are placed in the M-tiles in an order
+// that gives lane l (half h = l / 32) the 32 contiguous vocabulary columns
+// [32 h, 32 h + 32) of the 64-block in its accumulators: slot s = 16 t + j of
+// M-tile t, register j, is column 32 h + s.  Lanes l and l ^ 32 hold the two
+// halves of one request's 64 columns.  Every caller issues the same K order
+// (k-steps 0..15 accumulated into a zero tile; fragments past r are zero), so
+// a vocabulary element's bias is bit-identical wherever it is recomputed.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int bias_voff(int t, int m)
+// A row i of M-tile t -> vocabulary offset in the 64-block (inverse of the
+// accumulator placement above: row 8 q + 4 h + e holds column 32 h + 16 t + 4 q + e)
+__device__ __forceinline__ int a_row_voff(int t, int i)
 {
-    // output slot s of M-tile t, row m: lane group m / 4, position 4 t + m % 4
-    const int s = 4 * t + (m & 3);
-    const int g = m >> 2;
-    return (s < 8) ? (8 * g + s) : (32 + 8 * g + (s - 8));
+    const int q = i >> 3, h = (i >> 2) & 1, e = i & 3;
+    return 32 * h + 16 * t + 4 * q + e;
 }
-
-// value slot s (0..15) of lane group g -> vocabulary offset inside the 64-block
-__device__ __forceinline__ int slot_voff(int g, int s) { return (s < 8) ? (8 * g + s) : (24 + 8 * g + s); }
 
 // Load the A fragments (W2 rows) of a 64-vocabulary block starting at v_blk.
 __device__ __forceinline__ void load_w2_frags(const uint16_t* __restrict__ W2, int V, int r,
-                                              int v_blk, int lane, bf16x8 a[4][kKSteps])
+                                              int v_blk, int lane, bf16x8 a[2][kKSteps])
 {
-    const int m = lane & 15, g = lane >> 4;
+    const int i = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int v = v_blk + bias_voff(t, m);
+    for (int t = 0; t < 2; ++t) {
+        const int v = v_blk + a_row_voff(t, i);
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
-            const int kk = ks * kKStep + 8 * g;
+            const int kk = ks * kKStep + 8 * h;
             uint4 u = make_uint4(0, 0, 0, 0);
             if (v < V && kk < r) u = *reinterpret_cast<const uint4*>(W2 + (int64_t)v * r + kk);
             a[t][ks] = as_bf16x8(u);

@@ -11,11 +11,26 @@ constexpr int kSchedMaxCand = 16384;   // R * gamma limit of the one-workgroup s
 constexpr int kGammaMax = 64;
 constexpr int kVocabMax = 2048 * 256;  // pick workgroups hold up to 8 tiles per thread
 
+// Element strides of a logit tensor: element (n, k, v) of request n, position k
+// is p[n * rs + k * ps + v]; the vocabulary is contiguous.
+struct RowStrides {
+    int64_t rs;   // between requests
+    int64_t ps;   // between positions
+};
+
+// True when every row starts on a 16-byte boundary of a 16-byte-aligned tensor
+// (align = elements per 16 bytes) and a row is whole 8-element chunks.
+__host__ __device__ inline bool rows_vec(RowStrides s, int V, int align)
+{
+    return (V % 8) == 0 && (s.rs % align) == 0 && (s.ps % align) == 0;
+}
+
 size_t draft_workspace_bytes(int R, int V);
 size_t verify_workspace_bytes(int R, int gamma, int V);
 int pass_req_per_wg(int count_max, int n_vt);
 
-hipError_t launch_draft_step(const void* base, bool bf16, const uint16_t* E, const uint16_t* W2,
+hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
+                             const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, float temperature, uint64_t seed,
                              uint32_t round, void* ws, hipStream_t s);
@@ -28,7 +43,8 @@ hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t
 hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t S0, int mode,
                            int32_t* len, float* a, int32_t* B, int R, int gamma, hipStream_t s);
 
-hipError_t launch_verify(const void* target, const void* base, bool bf16, const uint16_t* E,
+hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
+                         bool bf16, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,

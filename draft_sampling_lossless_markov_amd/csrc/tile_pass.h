@@ -16,8 +16,11 @@
 // Tile partials are 256 columns wide everywhere, so a pick rescans 256 values.
 #pragma once
 
+#include <type_traits>
+
 #include "bias_tile.h"
 #include "dsp_device.h"
+#include "dsp_launch.h"
 
 namespace dsp {
 
@@ -54,6 +57,7 @@ struct __attribute__((aligned(16))) Part {
 struct PassArgs {
     const void* base;        // [R, gamma, V] draft base logits
     const void* target;      // [R, gamma+1, V] target logits (kResidual)
+    RowStrides bs, ts;       // element strides of base and target rows
     const uint16_t* E;
     const uint16_t* W2;
     const int32_t* anchor;
@@ -76,224 +80,367 @@ struct PassArgs {
 
 // ---------------------------------------------------------------------------
 // bias_pass_kernel: grid (n_vt, request chunks), 256 threads; wave w owns
-// vocabulary [256 vt + 64 w, +64) of every 64-request sub-block.  Lane l holds
-// request column l % 16 of each N-tile and the 16 vocabulary slots of lane group
-// l / 16 (bias_voff / slot_voff); the logit rows for those slots are prefetched
-// as raw 16-byte words before the MFMA chain.
+// vocabulary [256 vt + 64 w, +64) and walks the workgroup's requests in blocks of
+// 32 (one N-tile).  Lane l holds request l % 32 of the block and the 32
+// contiguous vocabulary columns [32 (l / 32), +32) of the wave's 64 (see
+// a_row_voff); lanes l and l ^ 32 share a request.
+//
+// Per block i, per wave: MFMA (bias of 64 columns x 32 requests, embedding rows
+// from LDS), then the epilogue, which in this order
+//   consumes block i's logit words (loaded two blocks earlier),
+//   stores block i+1's embedding rows (loaded one block earlier) to LDS,
+//   requests block i+2's embedding rows, block i+3's previous tokens and
+//   block i+2's logit words,
+//   reduces the block to partials;
+// then an LDS barrier and the merge of the four waves' partials.  Global loads
+// are thus issued in the order they are consumed: every wait on the in-order
+// load counter covers only data that is due, the barrier orders LDS only, and
+// the logit stream stays two blocks ahead.  Every load is unconditional
+// (clamped addresses, masked afterwards), so the load count is the same on
+// every path and the waits stay exact across the loop.
 // ---------------------------------------------------------------------------
-// Two workgroups per CU for the bf16 softmax / greedy passes (their registers
-// fit 256 per lane); the residual pass and fp32 rows need more and run one.
-template <typename LT, int KIND>
-constexpr int pass_min_blocks() { return (sizeof(LT) == 2 && KIND != kResidual) ? 2 : 1; }
+constexpr int kPassBlock = 32;   // requests per block (one 32-wide N-tile)
 
-template <typename LT, int KIND>
-__global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND>())) void bias_pass_kernel(PassArgs a)
+// Two workgroups per CU for the bf16 softmax / greedy passes on 16-byte-aligned
+// rows (their registers fit 256 per lane); the residual pass, fp32 rows and the
+// element-wise loads of other vocabulary sizes need more and run one.
+template <typename LT, int KIND, bool VEC>
+constexpr int pass_min_blocks() { return (sizeof(LT) == 2 && KIND != kResidual && VEC) ? 2 : 1; }
+
+// 32 bytes of -inf in either logit type: the source of every logit word that
+// falls outside the row (or belongs to a request past the end of the list).
+// Never written; declared without const so that it lives in the global address
+// space like the rows: a select between a row and a constant-space array would
+// turn the loads into flat loads, which the LDS wait counter also tracks.
+__device__ __attribute__((aligned(16))) uint32_t kNegInfWords[8] = {
+    0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u,
+    0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+__device__ __attribute__((aligned(16))) uint32_t kNegInfF32[8] = {
+    0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u,
+    0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
+
+// Raw words of 8 consecutive logits from v0 of a row (ok: the row belongs to a
+// live request; in: the chunk lies inside the row).  VEC (V % 8 == 0): a chunk
+// lies wholly inside or wholly outside the row, and an outside chunk or a dead
+// row reads the -inf words instead, without a branch.  Otherwise element by
+// element, each bounded by V.
+template <typename LT, bool VEC>
+__device__ __forceinline__ void load8_any(const LT* row, int v0, int V, bool ok, bool in, uint4* r)
 {
-    // double-buffered embedding tiles and cross-wave partials: sub-block i + 1 is
-    // staged and its logit rows requested while sub-block i is computed
-    __shared__ __attribute__((aligned(16))) uint16_t e_tile[2][kReqBlock][kRankMax + kERowPad];
-    __shared__ Part red[2][4][kReqBlock];
-    constexpr int RW = Logit<LT>::kRaw;
+    if constexpr (VEC) {
+        in = in && ok;
+        const LT* neg = (sizeof(LT) == 2) ? reinterpret_cast<const LT*>(kNegInfWords)
+                                          : reinterpret_cast<const LT*>(kNegInfF32);
+        const LT* p = in ? row + v0 : neg;
+        r[0] = load_nt16(p);
+        if constexpr (Logit<LT>::kRaw == 2) r[1] = load_nt16(p + 4);
+    } else {
+        Logit<LT>::load8_raw(row, ok ? v0 : V, V, false, r);   // bounds per element
+    }
+}
 
-    const int count = (KIND == kResidual) ? *a.count : a.R;
+// LDS of a bias-pass workgroup: first the W2 tile in transit to the MFMA
+// fragments (two 64-row quarter buffers, 16-byte slots XOR-swizzled per row),
+// then the embedding tiles and the cross-wave partials.
+union PassLds {
+    uint4 w2[2][64][kRankMax / 8];
+    struct {
+        uint16_t e[2][kPassBlock][kRankMax + kERowPad];
+        Part red[2][4][kPassBlock];
+    } s;
+};
+
+// slot of 16-byte word c of staged W2 row rho: the swizzle spreads the 32 rows an
+// A-fragment read touches (a_row_voff) over distinct banks, and keeps a row's
+// words a permutation of its slots
+__device__ __forceinline__ int w2_slot(int rho, int c) { return c ^ ((rho & 31) ^ (((rho >> 5) & 1) << 3)); }
+
+// The A fragments of the workgroup's 256-row W2 tile (rows v0 .. v0 + 255; wave w
+// takes rows 64 w .. 64 w + 63): each 64-row quarter is read contiguously (a
+// wave instruction covers two whole rows) into LDS, then the owning wave reads
+// its fragments.  Same values as load_w2_frags, at the streaming rate of W2.
+__device__ __forceinline__ void stage_w2_frags(const uint16_t* __restrict__ W2, int V, int r,
+                                               int v0, PassLds& L, bf16x8 a[2][kKSteps])
+{
+    constexpr int kWordsRow = kRankMax / 8;                    // 32 words of 16 bytes
+    constexpr int kPerThread = 64 * kWordsRow / 256;           // 8 words per quarter
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    uint4 cur[kPerThread], nxt[kPerThread];
+    auto fetch = [&](int q, uint4* u) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int f = i * 256 + tid, rho = f / kWordsRow, c = f % kWordsRow;
+            const int v = v0 + 64 * q + rho;
+            u[i] = (v < V && 8 * c < r)
+                       ? *reinterpret_cast<const uint4*>(W2 + (int64_t)v * r + 8 * c)
+                       : make_uint4(0, 0, 0, 0);
+        }
+    };
+    fetch(0, cur);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q + 1 < 4) fetch(q + 1, nxt);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int f = i * 256 + tid, rho = f / kWordsRow, c = f % kWordsRow;
+            L.w2[q & 1][rho][w2_slot(rho, c)] = cur[i];
+        }
+        lds_barrier();
+        if (wave == q) {
+            const int i32 = lane & 31, h = lane >> 5;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int rho = a_row_voff(t, i32);
+#pragma unroll
+                for (int ks = 0; ks < kKSteps; ++ks)
+                    a[t][ks] = as_bf16x8(L.w2[q & 1][rho][w2_slot(rho, 2 * ks + h)]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) cur[i] = nxt[i];
+    }
+    lds_barrier();   // the buffers are reused for the embedding tiles
+}
+
+template <typename LT, int KIND, bool VEC>
+__global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_pass_kernel(PassArgs a)
+{
+    __shared__ PassLds L;
+    auto& e_tile = L.s.e;
+    auto& red = L.s.red;
+    constexpr int RW = Logit<LT>::kRaw;
+    constexpr bool RES = (KIND == kResidual);
+
+    const int count = RES ? *a.count : a.R;
     const int n_begin = blockIdx.y * a.req_per_wg;
     if (n_begin >= count) return;   // workgroup-uniform
     const int n_end = min(count, n_begin + a.req_per_wg);
+    const int n_blk = (n_end - n_begin + kPassBlock - 1) / kPassBlock;
 
     const int vt = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int g = lane >> 4, c16 = lane & 15;
+    const int h = lane >> 5, c32 = lane & 31;
     const int V = a.V, r = a.r, gamma = a.gamma;
     const int v_blk = vt * kVocabTile + wave * 64;
-    const int ksteps = (r + kKStep - 1) / kKStep;
+    const int v_lane = v_blk + 32 * h;   // first of this lane's 32 columns
     const LT* __restrict__ base = static_cast<const LT*>(a.base);
     const LT* __restrict__ target = static_cast<const LT*>(a.target);
-    const bool vec_ok = (V % Logit<LT>::kVecAlign) == 0;
-    const int va = v_blk + 8 * g, vb = v_blk + 32 + 8 * g;
-    const bool fa = vec_ok && va + 8 <= V, fb = vec_ok && vb + 8 <= V;
-    const float it = a.inv_temp;
-    const float itL = fold_itl(it);
+    const float itL = fold_itl(a.inv_temp);
 
-    bf16x8 afrag[4][kKSteps];
-    load_w2_frags(a.W2, V, r, v_blk, lane, afrag);
+    bf16x8 afrag[2][kKSteps];
+    stage_w2_frags(a.W2, V, r, vt * kVocabTile, L, afrag);
 
-    // embedding rows of sub-block n0 into buffer b: thread t owns row t % 64 and
-    // the quarter t / 64 of it, so a wave writes 64 different rows at one column
-    // (conflict-free LDS stores); two halves keep the staging registers small
-    auto stage_e = [&](int n0, int b) {
-        const int row = threadIdx.x & 63, q4 = threadIdx.x >> 6;
-        const int e = n0 + row;
-        int prev = -1;
-        if (e < n_end) {
-            if constexpr (KIND == kResidual) prev = a.list_prev[e];
-            else prev = prev_token(a.anchor, a.tok, e, gamma, a.k, V);
-        }
+    // --- embedding rows: thread t stages row t % 32 of a block, 16-byte words
+    // [4 q, 4 q + 4) of it, q = t / 32, so a wave's stores hit 32 rows at two
+    // columns (no bank conflicts with the 264-element row pitch)
+    const int srow = threadIdx.x & 31, sq = threadIdx.x >> 5;
+    // the raw token of this thread's staging row in block blk (unconditional
+    // load, clamped index); it is validated only where it is used, a block
+    // later, so that nothing waits for it early
+    auto prev_raw = [&](int blk) -> int {
+        const int ec = min(n_begin + blk * kPassBlock + srow, n_end - 1);
+        if constexpr (RES) return a.list_prev[ec];
+        else return (a.k == 0) ? a.anchor[ec] : a.tok[(int64_t)ec * gamma + (a.k - 1)];
+    };
+    // the token selects a Markov row: a live request and a token inside [0, V)
+    auto prev_ok = [&](int blk, int p) -> bool {
+        return n_begin + blk * kPassBlock + srow < n_end && p >= 0 && p < V;
+    };
+    constexpr int kWords = kRankMax / 8 / 8;   // 16-byte words per thread (4)
+    uint4 eu[kWords];
+    auto load_e = [&](int blk, int praw) {
+        const int prev = prev_ok(blk, praw) ? praw : 0;
+        const uint16_t* rowp = a.E + (int64_t)prev * r;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint4 u[kRankMax / 64];
-#pragma unroll
-            for (int c = 0; c < kRankMax / 64; ++c) {
-                const int kk = (q4 * (kRankMax / 32) + h * (kRankMax / 64) + c) * 8;
-                u[c] = make_uint4(0, 0, 0, 0);
-                if (prev >= 0 && kk < r) u[c] = *reinterpret_cast<const uint4*>(a.E + (int64_t)prev * r + kk);
-            }
-#pragma unroll
-            for (int c = 0; c < kRankMax / 64; ++c)
-                *reinterpret_cast<uint4*>(
-                    &e_tile[b][row][(q4 * (kRankMax / 32) + h * (kRankMax / 64) + c) * 8]) = u[c];
+        for (int c = 0; c < kWords; ++c) {
+            const int kk = (sq * kWords + c) * 8;
+            eu[c] = *reinterpret_cast<const uint4*>(rowp + (kk < r ? kk : 0));
         }
     };
-    // raw logit words of N-tile tn of sub-block n0 (request rows for this lane)
-    auto load_raw = [&](int n0, int tn, uint4* rs_tn, uint4* rt_tn) {
-        const int e = n0 + 16 * tn + c16;
+    auto store_e = [&](int b, int blk, int praw) {
+        const bool ok = prev_ok(blk, praw);
+#pragma unroll
+        for (int c = 0; c < kWords; ++c) {
+            const int kk = (sq * kWords + c) * 8;
+            const bool live = ok && kk < r;
+            *reinterpret_cast<uint4*>(&e_tile[b][srow][kk]) = live ? eu[c] : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // --- logit words of block blk for this lane (its request, its 32 columns
+    // as four 8-element chunks) into ring slot sl
+    uint4 rs[2][4 * RW];
+    uint4 rt[RES ? 2 : 1][4 * RW];
+    auto load_raw = [&](int blk, int sl) {
+        const int e = n_begin + blk * kPassBlock + c32;
         const bool ok = e < n_end;
-        int n = e, m = a.k;
-        if constexpr (KIND == kResidual) {
-            n = ok ? a.list[e] : 0;
-            m = ok ? a.list_m[e] : 0;
+        int n = min(e, n_end - 1), m = a.k;
+        if constexpr (RES) {
+            m = a.list_m[n];
+            n = a.list[n];
         }
-        const LT* row = base + ((int64_t)(ok ? n : 0) * gamma + m) * V;
-        Logit<LT>::load8_raw(row, ok ? va : V, V, ok && fa, rs_tn);
-        Logit<LT>::load8_raw(row, ok ? vb : V, V, ok && fb, rs_tn + RW);
-        if constexpr (KIND == kResidual) {
-            const LT* trow = target + ((int64_t)(ok ? n : 0) * (gamma + 1) + m) * V;
-            Logit<LT>::load8_raw(trow, ok ? va : V, V, ok && fa, rt_tn);
-            Logit<LT>::load8_raw(trow, ok ? vb : V, V, ok && fb, rt_tn + RW);
+        const LT* row = base + (int64_t)n * a.bs.rs + (int64_t)m * a.bs.ps;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int v0 = v_lane + 8 * c;
+            load8_any<LT, VEC>(row, v0, V, ok, v0 + 8 <= V, rs[sl] + c * RW);
+        }
+        if constexpr (RES) {
+            const LT* trow = target + (int64_t)n * a.ts.rs + (int64_t)m * a.ts.ps;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int v0 = v_lane + 8 * c;
+                load8_any<LT, VEC>(trow, v0, V, ok, v0 + 8 <= V, rt[sl] + c * RW);
+            }
         }
     };
 
-    uint4 rs[4][2 * RW];
-    uint4 rt[KIND == kResidual ? 4 : 1][2 * RW];
-    stage_e(n_begin, 0);
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn) load_raw(n_begin, tn, rs[tn], rt[KIND == kResidual ? tn : 0]);
+    // prologue: block 0's rows staged, then the loads in flight in the same
+    // order as at the end of every later block (logit words of the block after
+    // next ... embedding rows, tokens, logit words of the last one), so that the
+    // loop is entered with the load queue it leaves with
+    int prev1, prev2;   // raw tokens of blocks i + 1 and i + 2
+    {
+        const int prev0 = prev_raw(0);
+        prev1 = prev_raw(1);
+        load_e(0, prev0);
+        store_e(0, 0, prev0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_e(1, prev1);
+        prev2 = prev_raw(2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(1, 1);
+    }
     lds_barrier();
 
-    int buf = 0;
-    for (int n0 = n_begin; n0 < n_end; n0 += kReqBlock, buf ^= 1) {
-        const int n1 = n0 + kReqBlock;
-        const bool more = n1 < n_end;
+    // one block; SL = i % 2 is both the ring slot and the LDS buffer, a
+    // compile-time constant so the ring stays in registers
+    auto step = [&](int i, auto SL) {
+        constexpr int sl = decltype(SL)::value, b = sl;
+        const int n0 = n_begin + i * kPassBlock;
 
-        // two halves of two N-tiles each: half the accumulators live at a time, and
-        // the embedding rows of the next sub-block are staged between the halves
+        // bias of the block: all sixteen k-steps (fragments past r are zero on
+        // both sides, so they add exact zeros)
+        floatx16 acc[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-        floatx4 acc[2][4];
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
-            if (ks < ksteps) {
+            const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(
+                &e_tile[b][c32][ks * kKStep + 8 * h]));
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        &e_tile[buf][16 * (2 * hf + i) + c16][ks * kKStep + 8 * g]));
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[i][t] = mfma_bf16(afrag[t][ks], b, acc[i][t]);
-                }
-            }
+            for (int t = 0; t < 2; ++t) acc[t] = mfma32_bf16(afrag[t][ks], bv, acc[t]);
         }
-        if (hf == 0 && more) stage_e(n1, buf ^ 1);
+        // keep the embedding-fragment reads four k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps - 4; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 
+        // epilogue: consume, stage, request, reduce
+        float z[32];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tn = 2 * hf + i;
-            float z[16];
+        for (int s = 0; s < 32; ++s)
+            z[s] = Logit<LT>::raw_at(rs[sl] + (s >> 3) * RW, s & 7) + acc[s >> 4][s & 15];
+        float xt[RES ? 32 : 1];
+        if constexpr (RES) {
 #pragma unroll
-            for (int s = 0; s < 16; ++s)
-                z[s] = Logit<LT>::raw_at(rs[tn] + (s >> 3) * RW, s & 7) + acc[i][s >> 2][s & 3];
-            float xt[KIND == kResidual ? 16 : 1];
-            if constexpr (KIND == kResidual) {
-#pragma unroll
-                for (int s = 0; s < 16; ++s) xt[s] = Logit<LT>::raw_at(rt[tn] + (s >> 3) * RW, s & 7);
-            }
-            // the next sub-block's rows reuse this N-tile's registers
-            if (more) load_raw(n1, tn, rs[tn], rt[KIND == kResidual ? tn : 0]);
-            Part res;
-            if constexpr (KIND == kGreedy) {
-                // slot s maps to increasing vocabulary ids, so the first slot holding
-                // the lane maximum is the lane's lowest-index argmax; masked slots
-                // (past V) come last and carry -inf
-                float m = z[0];
-#pragma unroll
-                for (int s = 1; s < 16; ++s) m = fmaxf(m, z[s]);
-                int si = 15;
-#pragma unroll
-                for (int s = 14; s >= 0; --s) si = (z[s] == m) ? s : si;
-                const int v = v_blk + slot_voff(g, si);
-                ArgMax am{m, v < V ? v : 0x7fffffff};
-#pragma unroll
-                for (int o = 16; o < 64; o <<= 1) {
-                    ArgMax b;
-                    b.v = __shfl_xor(am.v, o, kWave);
-                    b.i = __shfl_xor(am.i, o, kWave);
-                    am = argmax_merge(am, b);
-                }
-                res = Part{am.v, am.i, 0.0};
-            } else if constexpr (KIND == kSample) {
-                float m = z[0];
-#pragma unroll
-                for (int s = 1; s < 16; ++s) m = fmaxf(m, z[s]);
-                m = fmaxf(m, __shfl_xor(m, 16, kWave));
-                m = fmaxf(m, __shfl_xor(m, 32, kWave));
-                const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked block
-                double sum = 0.0;
-#pragma unroll
-                for (int s = 0; s < 16; s += 2)
-                    sum += (double)(wexp(z[s] - mref, itL) + wexp(z[s + 1] - mref, itL));
-                sum += __shfl_xor(sum, 16, kWave);
-                sum += __shfl_xor(sum, 32, kWave);
-                res = Part{m, 0, sum};
-            } else {   // kResidual
-                const int e = n0 + 16 * tn + c16;
-                double sum = 0.0;
-                if (e < n_end) {
-                    const int n = a.list[e];
-                    const int m = a.list_m[e];
-                    const float Md = (float)a.stats[2 * ((int64_t)n * gamma + m)];
-                    const double invZd = 1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1];
-                    const float Mt = a.row_m[n];
-                    const double invZt = 1.0 / a.row_z[n];
-#pragma unroll
-                    for (int s = 0; s < 16; ++s) {
-                        const double pv = (double)wexp(xt[s] - Mt, itL) * invZt;
-                        const double qv = (double)wexp(z[s] - Md, itL) * invZd;
-                        sum += fmax(pv - qv, 0.0);
-                    }
-                }
-                sum += __shfl_xor(sum, 16, kWave);
-                sum += __shfl_xor(sum, 32, kWave);
-                res = Part{0.f, 0, sum};
-            }
-            if (g == 0) red[buf][wave][16 * tn + c16] = res;
+            for (int s = 0; s < 32; ++s) xt[s] = Logit<LT>::raw_at(rt[sl] + (s >> 3) * RW, s & 7);
         }
+        if (i + 1 < n_blk) store_e(b ^ 1, i + 1, prev1);
+        load_e(i + 2, prev2);         // block i + 2's embedding rows
+        prev1 = prev2;
+        prev2 = prev_raw(i + 3);      // block i + 3's tokens
+        // the loads above are due one block earlier than the logit words below:
+        // keep them ahead in issue order (the load counter is in-order)
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(i + 2, sl);          // block i + 2's logit words
+
+        Part res;
+        if constexpr (KIND == kGreedy) {
+            // slots map to increasing vocabulary ids: the first slot holding the
+            // lane maximum is the lane's lowest-index argmax (masked slots come
+            // last and hold -inf)
+            float m = z[0];
+#pragma unroll
+            for (int s = 1; s < 32; ++s) m = fmaxf(m, z[s]);
+            int si = 31;
+#pragma unroll
+            for (int s = 30; s >= 0; --s) si = (z[s] == m) ? s : si;
+            const int v = v_lane + si;
+            ArgMax am{m, v < V ? v : 0x7fffffff};
+            am = xargmax<32>(am);
+            res = Part{am.v, am.i, 0.0};
+        } else if constexpr (KIND == kSample) {
+            float m = z[0];
+#pragma unroll
+            for (int s = 1; s < 32; ++s) m = fmaxf(m, z[s]);
+            m = xmax<32>(m);
+            const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked block
+            float w[32];
+#pragma unroll
+            for (int s = 0; s < 32; ++s) w[s] = wexp(z[s] - mref, itL);
+            // pairwise tree over the lane's 32 weights (relative error below
+            // 5 * 2^-24), then fp64 across the lane pair, tiles and rows
+#pragma unroll
+            for (int hw = 16; hw >= 1; hw >>= 1)
+#pragma unroll
+                for (int s = 0; s < hw; ++s) w[s] = w[s] + w[s + hw];
+            res = Part{m, 0, xsum<32>((double)w[0])};
+        } else {   // kResidual
+            const int e = min(n0 + c32, n_end - 1);
+            const int n = a.list[e];
+            const int m = a.list_m[e];
+            const float Md = (float)a.stats[2 * ((int64_t)n * gamma + m)];
+            const double invZd = 1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1];
+            const float Mt = a.row_m[n];
+            const double invZt = 1.0 / a.row_z[n];
+            double sum = 0.0;
+#pragma unroll
+            for (int s = 0; s < 32; ++s) {
+                const double pv = (double)wexp(xt[s] - Mt, itL) * invZt;
+                const double qv = (double)wexp(z[s] - Md, itL) * invZd;
+                sum += fmax(pv - qv, 0.0);
+            }
+            res = Part{0.f, 0, xsum<32>(sum)};
         }
+        if (h == 0) red[b][wave][c32] = res;
         lds_barrier();
-        if (threadIdx.x < kReqBlock) {
-            const int e = n0 + threadIdx.x;
-            if (e < n_end) {
-                Part p = red[buf][0][threadIdx.x];
+
+        // merge the four waves' partials: lanes 0..7 of wave w take requests
+        // 8 w .. 8 w + 7 of the block
+        const int j = 8 * wave + lane;
+        if (lane < 8 && n0 + j < n_end) {
+            Part p = red[b][0][j];
 #pragma unroll
-                for (int w = 1; w < 4; ++w) {
-                    const Part b = red[buf][w][threadIdx.x];
-                    if constexpr (KIND == kGreedy) {
-                        const ArgMax m = argmax_merge(ArgMax{p.m, p.idx}, ArgMax{b.m, b.idx});
-                        p.m = m.v;
-                        p.idx = m.i;
-                    } else if constexpr (KIND == kSample) {
-                        const float mm = fmaxf(p.m, b.m);
-                        if (mm != -INFINITY)
-                            p.s = p.s * (double)wexp(p.m - mm, itL) + b.s * (double)wexp(b.m - mm, itL);
-                        p.m = mm;
-                    } else {
-                        p.s += b.s;
-                    }
+            for (int w = 1; w < 4; ++w) {
+                const Part q = red[b][w][j];
+                if constexpr (KIND == kGreedy) {
+                    const ArgMax mm = argmax_merge(ArgMax{p.m, p.idx}, ArgMax{q.m, q.idx});
+                    p.m = mm.v;
+                    p.idx = mm.i;
+                } else if constexpr (KIND == kSample) {
+                    const float mm = fmaxf(p.m, q.m);
+                    if (mm != -INFINITY)
+                        p.s = p.s * (double)wexp(p.m - mm, itL) + q.s * (double)wexp(q.m - mm, itL);
+                    p.m = mm;
+                } else {
+                    p.s += q.s;
                 }
-                a.part[(int64_t)e * a.n_vt + vt] = p;
             }
+            a.part[(int64_t)(n0 + j) * a.n_vt + vt] = p;
         }
+    };
+    for (int i = 0; i < n_blk; i += 2) {
+        step(i, std::integral_constant<int, 0>{});
+        if (i + 1 < n_blk) step(i + 1, std::integral_constant<int, 1>{});
     }
 }
 

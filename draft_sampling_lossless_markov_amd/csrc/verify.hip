@@ -79,7 +79,7 @@ __device__ __forceinline__ int clamp_len(const int32_t* len, int n, int gamma)
 // ---------------------------------------------------------------------------
 template <typename LT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_rows_kernel(
-    const LT* __restrict__ target, const int32_t* __restrict__ tok,
+    const LT* __restrict__ target, RowStrides ts, const int32_t* __restrict__ tok,
     const int32_t* __restrict__ len, int R, int gamma, int V, float inv_temp, int n_vt,
     VerifyWs ws)
 {
@@ -89,14 +89,14 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
     if (blockIdx.x == 0 && tid == 0) *ws.resid_cnt = 0;
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int per_req = (gamma + 1) * spans;
-    const bool vec_ok = (V % Logit<LT>::kVecAlign) == 0;
+    const bool vec_ok = rows_vec(ts, V, Logit<LT>::kVecAlign);
     const int item = blockIdx.x;
     const int n = item / per_req;
     const int rem = item - n * per_req;
     const int j = rem / spans, sp = rem - (rem / spans) * spans;
     const int l = clamp_len(len, n, gamma);
     if (j > l) return;
-    const LT* row = target + ((int64_t)n * (gamma + 1) + j) * V;
+    const LT* row = target + (int64_t)n * ts.rs + (int64_t)j * ts.ps;
     const int t = sp * kSpanTiles + wave * 8 + (lane >> 3);
     const int sub = lane & 7;
     uint4 raw[4][RW];
@@ -241,9 +241,10 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
 // ---------------------------------------------------------------------------
 template <typename LT, int PER>
 __global__ __launch_bounds__(256) void verify_pick_kernel(
-    const LT* __restrict__ target, const LT* __restrict__ base, const uint16_t* __restrict__ E,
-    const uint16_t* __restrict__ W2, const int32_t* __restrict__ anchor,
-    const int32_t* __restrict__ tok, const double* __restrict__ stats,
+    const LT* __restrict__ target, RowStrides ts, const LT* __restrict__ base, RowStrides bs,
+    const uint16_t* __restrict__ E, const uint16_t* __restrict__ W2,
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ tok,
+    const double* __restrict__ stats,
     const int32_t* __restrict__ len, const int32_t* __restrict__ n_accept,
     int32_t* __restrict__ y, int R, int gamma, int V, int r, float inv_temp, uint64_t seed,
     uint32_t round, int n_vt, VerifyWs ws)
@@ -276,11 +277,11 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
             double before;
             const int tsel = block_locate<PER>(w, tgt, &before, sh);
             const int prev = prev_token(anchor, tok, n, gamma, m, V);
-            const LT* drow = base + ((int64_t)n * gamma + m) * V;
+            const LT* drow = base + (int64_t)n * bs.rs + (int64_t)m * bs.ps;
             block_logits64<LT>(drow, E, W2, V, r, prev, tsel * kVocabTile + wave * 64, lane,
                                sh.lg + wave * 64);
             __syncthreads();
-            const LT* trow = target + ((int64_t)n * (gamma + 1) + m) * V;
+            const LT* trow = target + (int64_t)n * ts.rs + (int64_t)m * ts.ps;
             const float Md = (float)stats[2 * ((int64_t)n * gamma + m)];
             const double invZd = 1.0 / stats[2 * ((int64_t)n * gamma + m) + 1];
             const float Mt = ws.row_m[n];
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     const double tgt = u * Z;
     double before;
     const int tsel = block_locate<PER>(w, tgt, &before, sh);
-    const LT* trow = target + ((int64_t)n * (gamma + 1) + row_j) * V;
+    const LT* trow = target + (int64_t)n * ts.rs + (int64_t)row_j * ts.ps;
     const int v = tsel * kVocabTile + tid;
     double e1[1] = {(v < V) ? (double)wexp(Logit<LT>::at(trow, v) - M, fold_itl(inv_temp)) : 0.0};
     double b2;
@@ -348,19 +349,22 @@ size_t verify_workspace_bytes(int R, int gamma, int V)
 }
 
 template <typename LT, int PER>
-static void launch_vpick(const LT* target, const LT* base, const uint16_t* E, const uint16_t* W2,
+static void launch_vpick(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
+                         const uint16_t* E, const uint16_t* W2,
                          const int32_t* anchor, const int32_t* tok, const double* stats,
                          const int32_t* len, const int32_t* n_accept, int32_t* y, int R, int gamma,
                          int V, int r, float it, uint64_t seed, uint32_t round, int n_vt,
                          const VerifyWs& ws, hipStream_t s)
 {
-    hipLaunchKernelGGL((verify_pick_kernel<LT, PER>), dim3(R), dim3(256), 0, s, target, base, E, W2,
+    hipLaunchKernelGGL((verify_pick_kernel<LT, PER>), dim3(R), dim3(256), 0, s, target, ts, base, bs,
+                       E, W2,
                        anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt,
                        ws);
 }
 
 template <typename LT>
-static hipError_t launch_verify_t(const LT* target, const LT* base, const uint16_t* E,
+static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
+                                  const uint16_t* E,
                                   const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                                   const float* q, const double* stats, const int32_t* len,
                                   int8_t* accept, int32_t* n_accept, int32_t* y, float* p, int R,
@@ -375,18 +379,19 @@ static hipError_t launch_verify_t(const LT* target, const LT* base, const uint16
     const int64_t items = (int64_t)R * (gamma + 1) * spans;
     const dim3 g1((unsigned)items);
     if (greedy) {
-        hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, tok, len,
+        hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, ts, tok, len,
                            R, gamma, V, it, n_vt, ws);
         hipLaunchKernelGGL((verify_accept_kernel<true>), dim3(R), dim3(256), 0, s, anchor, V, tok, q, len,
                            accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, tok, len, R,
+    hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, ts, tok, len, R,
                        gamma, V, it, n_vt, ws);
     hipLaunchKernelGGL((verify_accept_kernel<false>), dim3(R), dim3(256), 0, s, anchor, V, tok, q, len,
                        accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws);
     PassArgs a{};
-    a.base = base; a.target = target; a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.base = base; a.target = target; a.bs = bs; a.ts = ts;
+    a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
     a.list = ws.resid_list; a.list_m = ws.resid_m; a.list_prev = ws.resid_prev;
     a.count = ws.resid_cnt; a.n_accept = n_accept; a.stats = stats;
     a.row_m = ws.row_m; a.row_z = ws.row_z;
@@ -395,27 +400,32 @@ static hipError_t launch_verify_t(const LT* target, const LT* base, const uint16
     a.req_per_wg = pass_req_per_wg(R, n_vt);
     a.part = ws.resid_part;
     const dim3 g3(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
-    hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual>), g3, dim3(256), 0, s, a);
+    if (rows_vec(bs, V, 8) && rows_vec(ts, V, 8))
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, true>), g3, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, false>), g3, dim3(256), 0, s, a);
     const int per = (n_vt + 255) / 256;
-    if (per <= 1) launch_vpick<LT, 1>(target, base, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
-    else if (per <= 2) launch_vpick<LT, 2>(target, base, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
-    else if (per <= 4) launch_vpick<LT, 4>(target, base, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
-    else launch_vpick<LT, 8>(target, base, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
+    if (per <= 1) launch_vpick<LT, 1>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
+    else if (per <= 2) launch_vpick<LT, 2>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
+    else if (per <= 4) launch_vpick<LT, 4>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
+    else launch_vpick<LT, 8>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
     return hipGetLastError();
 }
 
-hipError_t launch_verify(const void* target, const void* base, bool bf16, const uint16_t* E,
+hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
+                         bool bf16, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
                          float temperature, uint64_t seed, uint32_t round, void* ws, hipStream_t s)
 {
     if (bf16)
-        return launch_verify_t(static_cast<const uint16_t*>(target),
-                               static_cast<const uint16_t*>(base), E, W2, anchor, tok, q, stats,
+        return launch_verify_t(static_cast<const uint16_t*>(target), ts,
+                               static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,
                                len, accept, n_accept, y, p, R, gamma, V, r, temperature, seed, round,
                                ws, s);
-    return launch_verify_t(static_cast<const float*>(target), static_cast<const float*>(base), E, W2,
+    return launch_verify_t(static_cast<const float*>(target), ts, static_cast<const float*>(base), bs,
+                           E, W2,
                            anchor, tok, q, stats, len, accept, n_accept, y, p, R, gamma, V, r,
                            temperature, seed, round, ws, s);
 }

@@ -56,11 +56,13 @@ def lib():
     L.dsp_version.restype = I
     L.dsp_workspace_size.argtypes = [I, I, I, I, I]
     L.dsp_workspace_size.restype = SZ
-    L.dsp_draft_step.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, F, U64, U32, P, SZ, P]
+    I64 = C.c_int64
+    L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, F, U64, U32, P,
+                                 SZ, P]
     L.dsp_confidence.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
-    L.dsp_verify.argtypes = [P, P, I, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, U64, U32,
-                             P, SZ, P]
+    L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
+                             I, I, F, U64, U32, P, SZ, P]
     for f in ("dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify"):
         getattr(L, f).restype = I
     _lib = L
@@ -90,6 +92,13 @@ def _dtype(t: torch.Tensor) -> int:
     raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
 
 
+def _rows(t: torch.Tensor, name: str):
+    """(request stride, position stride) of a logit tensor viewed as [R, positions, V]."""
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise ValueError(f"{name} must be a 3-D [R, positions, V] view with contiguous rows")
+    return t.stride(0), t.stride(1)
+
+
 def dsp_workspace_size(which: int, R: int, gamma: int, V: int, r: int) -> int:
     return int(lib().dsp_workspace_size(which, R, gamma, V, r))
 
@@ -98,7 +107,8 @@ def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, rou
                    stream=None):
     R, gamma, V = base.shape
     r = E.shape[1]
-    _check(lib().dsp_draft_step(_ptr(base), _dtype(base), _ptr(E), _ptr(W2), _ptr(anchor),
+    rs, ps = _rows(base, "base")
+    _check(lib().dsp_draft_step(_ptr(base), _dtype(base), rs, ps, _ptr(E), _ptr(W2), _ptr(anchor),
                                 _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V, r, int(k),
                                 float(temperature), int(seed), int(round_), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)))
@@ -121,7 +131,12 @@ def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_acc
                temperature, seed, round_, ws, stream=None):
     R, g1, V = target.shape
     r = E.shape[1]
-    _check(lib().dsp_verify(_ptr(target), _ptr(base), _dtype(target), _ptr(E), _ptr(W2),
+    trs, tps = _rows(target, "target")
+    brs, bps = _rows(base, "base")
+    if base.dtype != target.dtype:
+        raise TypeError("base and target logits must share a dtype")
+    _check(lib().dsp_verify(_ptr(target), trs, tps, _ptr(base), brs, bps, _dtype(target),
+                            _ptr(E), _ptr(W2),
                             _ptr(anchor), _ptr(tok), _ptr(q), _ptr(stats), _ptr(length),
                             _ptr(accept), _ptr(n_accept), _ptr(y), _ptr(p), R, g1 - 1, V, r,
                             float(temperature), int(seed), int(round_), _ptr(ws),

@@ -12,7 +12,12 @@ L = 1).  The backbone and target models are not run: their outputs are drawn
 as Gaussian logits of the stated shapes.
 
 Layouts (row-major, last index contiguous):
-  base    [R, gamma,   V]  draft base logits (fp32 or bf16)
+  base    [R, gamma,   V]  draft base logits (fp32 or bf16); a view whose
+                           storage is [R, gamma, V] (layout "request"),
+                           [gamma, R, V] ("position": each draft position one
+                           contiguous [R, V] slab) or [R, gamma, V + 64]
+                           ("padded": rows of base and target padded by 64);
+                           the values do not depend on the layout
   target  [R, gamma+1, V]  target logits; row j is the law of draft position j,
                            row gamma is the bonus row
   E       [V, r]  bf16     Markov embedding (W1 on the pages)
@@ -101,10 +106,38 @@ def _temps(law: str, gamma: int, g: torch.Generator, device) -> torch.Tensor:
     return lo + (hi - lo) * u
 
 
+BASE_LAYOUTS = ("request", "position", "padded")
+# The layout of the measured configuration: the draft base logits position-major,
+# so that each draft step streams one contiguous [R, V] slab.
+BENCH_LAYOUT = "position"
+
+
+def empty_logits(R: int, P: int, V: int, dtype, device, layout: str, pad_target=False):
+    """An uninitialised [R, P, V] logit view whose storage follows `layout`
+    (for the target tensor only "padded" changes the storage)."""
+    if layout == "position" and not pad_target:
+        return torch.empty((P, R, V), dtype=dtype, device=device).permute(1, 0, 2)
+    if layout == "padded":
+        return torch.empty((R, P, V + 64), dtype=dtype, device=device)[:, :, :V]
+    return torch.empty((R, P, V), dtype=dtype, device=device)
+
+
+def place_logits(t: torch.Tensor, layout: str, device, pad_target=False) -> torch.Tensor:
+    """A copy of the [R, P, V] logit tensor t on `device`, stored as `layout`."""
+    R, P, V = t.shape
+    out = empty_logits(R, P, V, t.dtype, device, layout, pad_target)
+    out.copy_(t)
+    return out
+
+
 def make_inputs(wl: Workload, set_idx: int = 0, device="cpu", *, seed_base: int = 0,
-                R: Optional[int] = None, V: Optional[int] = None) -> dict:
+                R: Optional[int] = None, V: Optional[int] = None,
+                layout: str = "request") -> dict:
     """Draw one seeded input set.  `R`/`V` override the workload's sizes (smaller
-    parity cases keep the laws but shrink the shape)."""
+    parity cases keep the laws but shrink the shape); `layout` places the base
+    logits in memory (one of BASE_LAYOUTS) without changing a value."""
+    if layout not in BASE_LAYOUTS:
+        raise ValueError(f"layout must be one of {BASE_LAYOUTS}, got {layout!r}")
     R = wl.R if R is None else R
     V = wl.V if V is None else V
     gamma, r, d = wl.gamma, wl.r, wl.d
@@ -118,8 +151,8 @@ def make_inputs(wl: Workload, set_idx: int = 0, device="cpu", *, seed_base: int 
 
     # Target row j = draft base row j + noise; one extra base-law row feeds the
     # bonus row gamma of the target.
-    base = torch.empty((R, gamma, V), dtype=ldt, device=dev)
-    target = torch.empty((R, gamma + 1, V), dtype=ldt, device=dev)
+    base = empty_logits(R, gamma, V, ldt, dev, layout)
+    target = empty_logits(R, gamma + 1, V, ldt, dev, layout, pad_target=True)
     for j in range(gamma + 1):
         b = (torch.randn((R, V), generator=g, device=dev, dtype=torch.float32)
              * wl.base_std).to(ldt)
@@ -143,4 +176,4 @@ def make_inputs(wl: Workload, set_idx: int = 0, device="cpu", *, seed_base: int 
     sps = sps_table(wl.cost, B_max).to(dev)
     return dict(base=base, target=target, E=E, W2=W2, h=h, w=w, T=T, offset=offset,
                 anchor=anchor, sps=sps, R=R, gamma=gamma, V=V, r=r, d=d, B_max=B_max,
-                mode=wl.mode, tau0=wl.tau0, temperature=wl.temperature)
+                mode=wl.mode, tau0=wl.tau0, temperature=wl.temperature, layout=layout)

@@ -10,9 +10,21 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is DEVICE memory owned by the caller, row-major with
- *     the last index contiguous and no padding.  The library never allocates or
- *     frees memory; scratch comes from a caller workspace sized by
- *     dsp_workspace_size().
+ *     the last index contiguous and no padding, except the logit tensors (base,
+ *     target), whose rows are placed by element strides (below).  The library
+ *     never allocates or frees memory; scratch comes from a caller workspace
+ *     sized by dsp_workspace_size().
+ *   - Logit rows: element (n, k, v) -- request n, position k, vocabulary id v --
+ *     of a logit tensor p with strides (rs, ps) is p[n * rs + k * ps + v]
+ *     (strides in elements, >= 0; the vocabulary is contiguous).  A contiguous
+ *     [R, gamma, V] tensor has rs = gamma * V, ps = V; a position-major
+ *     [gamma, R, V] one has rs = V, ps = R * V.  Every row of the shape must be
+ *     readable memory.  Rows stream as 16-byte words when V and both strides
+ *     are multiples of 8 elements, otherwise element by element (same results).
+ *     Performance note: request strides that are multiples of 2 MiB alias in
+ *     HBM on MI355X and cost up to a third of the streaming rate of a draft
+ *     step; a position-major base tensor (each draft step reads one contiguous
+ *     [R, V] slab) or a row pitch padded off a power of two avoids it.
  *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is the
  *     default stream).  No call synchronises the host; lengths and batch sizes
  *     stay on the device.  Calls on different streams with different workspaces
@@ -32,6 +44,8 @@
  *
  * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
  * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
+ *
+ * ABI version 200: base and target take element strides.
  */
 #ifndef DSP_H
 #define DSP_H
@@ -87,7 +101,9 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  *     tok[n,k] = min{v : sum_{i<=v} pi_i > u(seed, round, n, k, 0)};
  *     q[n,k] = pi of that token; stats[n,k] = (M, Z), Z = sum_v exp((logit_v - M)/T)
  *
- * base   [R, gamma, V] fp32 or bf16 (dtype)   draft base logits of the backbone
+ * base   logits (n, k, v) at base[n * base_rs + k * base_ps + v], fp32 or bf16
+ *        (dtype): the draft base logits of the backbone, R x gamma rows of V;
+ *        only position k is read
  * E      [V, r] bf16   Markov embedding; row x is the embedding of token x
  * W2     [V, r] bf16   low-rank output factor stored transposed: W2[v, i] is
  *                      element (i, v) of the r x V matrix
@@ -97,8 +113,8 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  * stats  [R, gamma, 2] f64  column k written
  * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
  */
-dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, const uint16_t* E,
-                          const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
+dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
+                          const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
                           double* stats, int R, int gamma, int V, int r, int k,
                           float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream);
@@ -174,13 +190,16 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
  *   accept[n,j] = -1 and p[n,j] = 0 for j >= l; p[n,j] = p_j(x_j) for j < l
  *   (greedy: 1 if accepted else 0).
  *
- * target [R, gamma+1, V] and base [R, gamma, V] of the same dtype; E, W2 as for
- * dsp_draft_step; anchor [R]; tok, q [R, gamma] and stats [R, gamma, 2] (f64) as
+ * target logits (n, j, v), j = 0..gamma, at target[n * target_rs + j * target_ps
+ * + v] and base (n, k, v) at base[n * base_rs + k * base_ps + v], one dtype;
+ * E, W2 as for dsp_draft_step; anchor [R]; tok, q [R, gamma] and stats
+ * [R, gamma, 2] (f64) as
  * written by dsp_draft_step; len [R]; outputs accept [R, gamma] int8,
  * n_accept [R] int32, y [R] int32, p [R, gamma] f32.
  * ws >= dsp_workspace_size(DSP_WS_VERIFY, R, gamma, V, r) bytes.
  */
-dsp_status dsp_verify(const void* target, const void* base, dsp_dtype dtype, const uint16_t* E,
+dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                      int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                       const float* q, const double* stats, const int32_t* len, int8_t* accept,
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings_and_version(L):
     assert L.dsp_status_string(0) == b"DSP_OK"
     assert L.dsp_status_string(3) == b"DSP_ERR_WORKSPACE"
-    assert L.dsp_version() >= 100
+    assert L.dsp_version() == 200
 
 
 def test_workspace_sizes(L):
@@ -57,7 +57,8 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation returns first
 
 
 def _draft(L, **kw):
-    a = dict(base=FAKE, dtype=1, E=FAKE, W2=FAKE, anchor=FAKE, tok=FAKE, q=FAKE, stats=FAKE,
+    a = dict(base=FAKE, dtype=1, base_rs=4 * 32, base_ps=32, E=FAKE, W2=FAKE, anchor=FAKE,
+             tok=FAKE, q=FAKE, stats=FAKE,
              R=4, gamma=4, V=32, r=8, k=0, temperature=1.0, seed=0, round=0, ws=FAKE,
              ws_bytes=1 << 20, stream=None)
     a.update(kw)
@@ -80,6 +81,9 @@ def test_draft_validation(L):
     assert _draft(L, r=264) == 2
     assert _draft(L, ws_bytes=8) == 3
     assert _draft(L, ws=0) == 3
+    assert _draft(L, base_rs=-1) == 1
+    assert b"strides" in L.dsp_last_error()
+    assert _draft(L, base_ps=-32) == 1
     assert _draft(L, base=FAKE + 4) == 1
     assert b"16-byte" in L.dsp_last_error()
 
@@ -101,11 +105,18 @@ def test_confidence_and_verify_validation(L):
                             4, 4, 16, 32, 8, None) == 1
     assert L.dsp_confidence(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE),
                             4, 4, -1, 32, 8, None) == 1
-    two = [P(FAKE)] * 2
+    # target (rs, ps) = (5 * 32, 32), base (4 * 32, 32): contiguous [R, gamma(+1), V]
+    two = [P(FAKE), 5 * 32, 32, P(FAKE), 4 * 32, 32]
     v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0, 0, 0, P(FAKE), 16, None)
     assert v == 3   # workspace too small
     v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 12, 1.0, 0, 0, P(FAKE), 1 << 20, None)
     assert v == 2
-    v = L.dsp_verify(P(0), P(FAKE), 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0, 0, 0, P(FAKE), 1 << 20,
-                     None)
+    v = L.dsp_verify(P(0), 5 * 32, 32, P(FAKE), 4 * 32, 32, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0,
+                     0, 0, P(FAKE), 1 << 20, None)
     assert v == 1
+    v = L.dsp_verify(P(FAKE), -1, 32, P(FAKE), 4 * 32, 32, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0,
+                     0, 0, P(FAKE), 1 << 20, None)
+    assert v == 1 and b"target strides" in L.dsp_last_error()
+    v = L.dsp_verify(P(FAKE), 5 * 32, 32, P(FAKE), 4 * 32, -5, 1, *[P(FAKE)] * 11, 4, 4, 32, 8,
+                     1.0, 0, 0, P(FAKE), 1 << 20, None)
+    assert v == 1 and b"base strides" in L.dsp_last_error()

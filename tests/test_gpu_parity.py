@@ -17,7 +17,8 @@ from oracle.compare import (Tally, compare_confidence, compare_draft, compare_sc
                             compare_verify)
 from draft_sampling_lossless_markov_amd import dsp
 from draft_sampling_lossless_markov_amd.engine import Round
-from draft_sampling_lossless_markov_amd.workloads import WORKLOADS, Workload, make_inputs, _cost_q12
+from draft_sampling_lossless_markov_amd.workloads import (BENCH_LAYOUT, WORKLOADS, Workload,
+                                                          _cost_q12, make_inputs, place_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,9 +37,13 @@ def _gpu():
 
 
 def to_dev(inp):
+    """Device copies of an input set; the logits keep their memory layout."""
     out = {}
     for k, v in inp.items():
         out[k] = v.cuda() if isinstance(v, torch.Tensor) else v
+    lay = inp.get("layout", "request")
+    out["base"] = place_logits(inp["base"], lay, "cuda")
+    out["target"] = place_logits(inp["target"], lay, "cuda", pad_target=True)
     return out
 
 
@@ -110,6 +115,32 @@ def test_round_parity_small(case):
     assert tot.mismatch_rate() <= 1e-4, tot.summary()
 
 
+LAYOUT_CASES = [
+    (70, 5, 1000, 24, 100, torch.bfloat16, 0.7, 1),
+    (70, 5, 1000, 24, 100, torch.bfloat16, 0.0, 1),
+    (33, 3, 1003, 8, 12, torch.float32, 1.0, 1),
+    (130, 6, 4100, 256, 64, torch.bfloat16, 1.0, 1),
+]
+
+
+@pytest.mark.parametrize("layout", ["position", "padded"])
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=lambda c: f"R{c[0]}g{c[1]}V{c[2]}"
+                         f"{'bf16' if c[5] == torch.bfloat16 else 'f32'}T{c[6]}")
+def test_round_parity_layouts(case, layout):
+    """Position-major and padded logit rows (strided base and target): the same
+    values as the contiguous layout, so the same comparison against the oracle."""
+    R, gamma, V, r, d, dt, temp, mode = case
+    _say(f"round parity {case} layout={layout}")
+    wl = custom(R, gamma, V, r, d, dt, mode=mode)
+    tot = Tally()
+    for rnd in range(3):
+        inp = make_inputs(wl, rnd, layout=layout)
+        g, o = run_both(inp, temp, rnd)
+        tot.add(compare_round(g, o, temp == 0.0))
+    assert tot.ok(), tot.summary()
+    assert tot.mismatch_rate() <= 1e-4, tot.summary()
+
+
 def test_tiny_workload_1000_rounds():
     """The tiny workload: 1000 rounds with fresh inputs, greedy and sampling."""
     wl = WORKLOADS[0]
@@ -162,7 +193,7 @@ def test_full_size_stages(wid):
     wl = WORKLOADS[wid]
     _say(f"full size stages: {wl.name}")
     torch.manual_seed(0)
-    inp = make_inputs(wl, 0, device="cuda")
+    inp = make_inputs(wl, 0, device="cuda", layout=BENCH_LAYOUT)
     R, gamma, V, r, d = inp["R"], inp["gamma"], inp["V"], inp["r"], inp["d"]
     S = _sample(R)
     Sl = torch.as_tensor(S).long().cuda()
@@ -242,7 +273,7 @@ def test_full_vocab_sampling_mismatch_rate():
     bounded by the fp32 arithmetic (exp rounding and bias summation order leave
     a CDF error of a few 1e-9 against ~1.5e5 boundaries)."""
     wl = WORKLOADS[1]
-    inp = make_inputs(wl, 0, device="cuda")
+    inp = make_inputs(wl, 0, device="cuda", layout=BENCH_LAYOUT)
     R, gamma, V, r = inp["R"], inp["gamma"], inp["V"], inp["r"]
     E_h, W2_h = orc.bf16_bits(inp["E"]), orc.bf16_bits(inp["W2"])
     anchor = np_(inp["anchor"])

@@ -22,6 +22,11 @@ namespace dsp {
 
 // ---------------------------------------------------------------------------
 // draft_pick: grid R, 256 threads; thread t owns tiles [t * PER, t * PER + PER).
+// Sampling: combine the tile partials in fp64 -> (M, Z); u from Philox; locate
+// the tile whose cumulative mass crosses u Z; rebuild its 256 logits exactly as
+// the pass computed them; locate the token inside it.  The tile's base logits
+// and the embedding row are requested before the W2 fetch so their latencies
+// overlap.
 // ---------------------------------------------------------------------------
 template <typename LT, bool GREEDY, int PER>
 __global__ __launch_bounds__(256) void draft_pick_kernel(
@@ -36,17 +41,16 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const Part* pp = part + (int64_t)n * n_vt;
     const int64_t out = (int64_t)n * gamma + k;
-    const int prev = GREEDY ? -1 : prev_token(anchor, tok, n, gamma, k, V);   // issued early
 
     if constexpr (GREEDY) {
         ArgMax am{-INFINITY, 0x7fffffff};
         for (int t = tid; t < n_vt; t += 256) am = argmax_merge(am, ArgMax{pp[t].m, pp[t].idx});
         am = wave_argmax(am);
-        if (lane == 0) { sh.wmax[wave] = am.v; sh.hit[wave] = am.i; }
-        __syncthreads();
+        if (lane == 0) { sh.wmax[wave] = am.v; sh.hit[0][wave] = am.i; }
+        lds_barrier();
         if (tid == 0) {
-            ArgMax b{sh.wmax[0], sh.hit[0]};
-            for (int w = 1; w < 4; ++w) b = argmax_merge(b, ArgMax{sh.wmax[w], sh.hit[w]});
+            ArgMax b{sh.wmax[0], sh.hit[0][0]};
+            for (int w = 1; w < 4; ++w) b = argmax_merge(b, ArgMax{sh.wmax[w], sh.hit[0][w]});
             tok[out] = b.i;
             q[out] = 1.0f;
             stats[2 * out] = b.v;
@@ -54,6 +58,9 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
         }
         return;
     } else {
+        __shared__ PassLds L;
+        __shared__ __attribute__((aligned(16))) uint16_t e_row[kRankMax];
+        const int prev = prev_token(anchor, tok, n, gamma, k, V);   // issued early
         float mt[PER];
         double st[PER];
         float M = -INFINITY;
@@ -73,25 +80,26 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
             w[i] = (mt[i] == -INFINITY) ? 0.0 : st[i] * exp(((double)mt[i] - (double)M) * (double)inv_temp);
             ls += w[i];
         }
-        ls = wave_sum(ls);
-        if (lane == 0) sh.wsum[wave] = ls;
-        __syncthreads();
-        const double Z = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
-        __syncthreads();
+        const double Z = block_sum256(ls, sh);
         const double u = uniform24(seed, round, (uint32_t)n, (uint32_t)k, 0u);
         const double target = u * Z;
         double before;
-        const int tsel = block_locate<PER>(w, target, &before, sh);
+        const int tsel = block_locate<PER>(w, target, &before, sh, 0);
 
-        // rebuild the 256 logits of the chosen tile, 64 per wave
+        // rebuild the chosen tile's 256 logits (thread t: column tsel * 256 + t)
         const LT* row = base + (int64_t)n * bs.rs + (int64_t)k * bs.ps;
-        block_logits64<LT>(row, E, W2, V, r, prev, tsel * kVocabTile + wave * 64, lane,
-                           sh.lg + wave * 64);
-        __syncthreads();
-        const float z = sh.lg[tid];
-        double e1[1] = {(double)wexp(z - M, fold_itl(inv_temp))};
+        const int v = tsel * kVocabTile + tid;
+        const float xb = (v < V) ? Logit<LT>::at(row, v) : -INFINITY;
+        if (tid < kRankMax / 8) {
+            const int kk = 8 * tid;
+            uint4 ev = make_uint4(0, 0, 0, 0);
+            if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
+            *reinterpret_cast<uint4*>(e_row + kk) = ev;
+        }
+        const float z = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, L, sh);
+        double e1[1] = {(v < V) ? (double)wexp(z - M, fold_itl(inv_temp)) : 0.0};
         double b2;
-        const int loc = block_locate<1>(e1, target - before, &b2, sh);
+        const int loc = block_locate<1>(e1, target - before, &b2, sh, 1);
         if (tid == loc) {
             tok[out] = tsel * kVocabTile + loc;
             q[out] = (float)(e1[0] / Z);

@@ -204,6 +204,78 @@ __device__ __forceinline__ ArgMax xargmax(ArgMax x)
     return argmax_merge(ArgMax{__uint_as_float(pv), (int)pi}, ArgMax{__uint_as_float(qv), (int)qi});
 }
 
+// ---------------------------------------------------------------------------
+// Whole-wave reductions and scans on DPP row operations (quad permutes, row
+// mirrors, row shifts and row broadcasts) plus the row swaps above: VALU work,
+// no LDS round trips.  Every lane gets the result.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF, bool ZERO_FILL = false>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, ZERO_FILL);
+}
+
+template <int CTRL, int ROW_MASK = 0xF, bool ZERO_FILL = false>
+__device__ __forceinline__ double dpp64(double x)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = dpp32<CTRL, ROW_MASK, ZERO_FILL>((uint32_t)b);
+    const uint32_t hi = dpp32<CTRL, ROW_MASK, ZERO_FILL>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+
+__device__ __forceinline__ float wave_max_f(float x)
+{
+    x = fmaxf(x, __uint_as_float(dpp32<kDppXor1>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp32<kDppXor2>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp32<kDppMirror>(__float_as_uint(x))));
+    return xmax<32>(xmax<16>(x));
+}
+
+__device__ __forceinline__ double wave_sum_d(double x)
+{
+    x += dpp64<kDppXor1>(x);
+    x += dpp64<kDppXor2>(x);
+    x += dpp64<kDppHalfMirror>(x);
+    x += dpp64<kDppMirror>(x);
+    return xsum<32>(xsum<16>(x));
+}
+
+template <bool MAX>
+__device__ __forceinline__ int wave_minmax_i(int x)
+{
+    auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
+    x = op(x, (int)dpp32<kDppXor1>((uint32_t)x));
+    x = op(x, (int)dpp32<kDppXor2>((uint32_t)x));
+    x = op(x, (int)dpp32<kDppHalfMirror>((uint32_t)x));
+    x = op(x, (int)dpp32<kDppMirror>((uint32_t)x));
+    uint32_t p, q;
+    xswap<16>((uint32_t)x, p, q);
+    x = op((int)p, (int)q);
+    xswap<32>((uint32_t)x, p, q);
+    return op((int)p, (int)q);
+}
+
+// inclusive prefix sum over the 64 lanes: Hillis-Steele within each 16-lane row
+// (row shifts by 1, 2, 4, 8 with zero fill), then the row totals carried by the
+// row broadcasts of lane 15 (to rows 1 and 3) and lane 31 (to rows 2 and 3)
+__device__ __forceinline__ double wave_scan_d(double x)
+{
+    x += dpp64<0x111, 0xF, true>(x);
+    x += dpp64<0x112, 0xF, true>(x);
+    x += dpp64<0x114, 0xF, true>(x);
+    x += dpp64<0x118, 0xF, true>(x);
+    x += dpp64<0x142, 0xA>(x);
+    x += dpp64<0x143, 0xC>(x);
+    return x;
+}
+
 // Online-softmax partial (m, s): s = sum exp((x - m) * it) over a set of
 // logits with maximum m (m = -inf, s = 0 for the empty set).
 __device__ __forceinline__ float2 lse_merge(float2 a, float2 b, float it)

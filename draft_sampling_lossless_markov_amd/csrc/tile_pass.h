@@ -445,47 +445,59 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
 }
 
 // ---------------------------------------------------------------------------
-// block-wide helpers for 256-thread pick workgroups
+// block-wide helpers for 256-thread pick workgroups.  Wave-level work runs on
+// DPP and row swaps; each helper call owns its LDS slots, so a call needs one
+// LDS barrier (two for a locate) and none to release its slots.
 // ---------------------------------------------------------------------------
 struct PickScratch {
-    double wsum[4];
     float wmax[4];
-    double scan[4];
-    int hit[4];
+    double wsum[4];
+    double scan[2][4];
+    int hit[2][4];
+    double hb[2][4];
+    int last[2][4];
+    double fb[2];
     float lg[kVocabTile];
-    float wt[kVocabTile];
 };
 
 __device__ __forceinline__ float block_max256(float v, PickScratch& sh)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    v = wave_max(v);
+    v = wave_max_f(v);
     if (lane == 0) sh.wmax[wave] = v;
-    __syncthreads();
-    const float r = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
-    __syncthreads();
-    return r;
+    lds_barrier();
+    return fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
 }
 
-// Locate the first of n_items consecutive weights (thread t owns items
-// [t * per, t * per + per)) whose inclusive cumulative sum exceeds target.
+__device__ __forceinline__ double block_sum256(double v, PickScratch& sh)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    v = wave_sum_d(v);
+    if (lane == 0) sh.wsum[wave] = v;
+    lds_barrier();
+    return (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
+}
+
+// Locate the first of the block's consecutive weights (thread t owns items
+// [t * PER, t * PER + PER)) whose inclusive cumulative sum exceeds target.
 // w[] holds the thread's weights (zeros past the end).  Returns the item and
-// the cumulative mass before it; falls back to the last positive item.
+// the cumulative mass before it; falls back to the last positive item when
+// rounding leaves the target beyond the total.  slot: 0 or 1, one per call.
 template <int PER>
 __device__ __forceinline__ int block_locate(const double (&w)[PER], double target, double* before,
-                                            PickScratch& sh)
+                                            PickScratch& sh, int slot)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     double ls = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) ls += w[i];
-    const double incl = wave_incl_scan(ls, lane);
-    if (lane == kWave - 1) sh.scan[wave] = incl;
-    __syncthreads();
+    const double incl = wave_scan_d(ls);
+    if (lane == kWave - 1) sh.scan[slot][wave] = incl;
+    lds_barrier();
     double off = 0.0;
-    for (int w2 = 0; w2 < wave; ++w2) off += sh.scan[w2];
-    __syncthreads();
-    double c = off + incl - ls;
+    for (int w2 = 0; w2 < wave; ++w2) off += sh.scan[slot][w2];
+    const double c0 = off + incl - ls;
+    double c = c0;
     int hit = 0x7fffffff, last = -1;
     double hit_before = 0.0;
 #pragma unroll
@@ -500,36 +512,70 @@ __device__ __forceinline__ int block_locate(const double (&w)[PER], double targe
         if (w[i] > 0.0) last = (int)threadIdx.x * PER + i;
         c = nc;
     }
-    int h = wave_min_i(hit);
-    if (lane == 0) sh.hit[wave] = h;
-    __syncthreads();
-    h = min(min(sh.hit[0], sh.hit[1]), min(sh.hit[2], sh.hit[3]));
-    __syncthreads();
-    if (h == 0x7fffffff) {
-        // rounding left the target beyond the total: take the last positive item
-        int l = wave_max_i(last);
-        if (lane == 0) sh.hit[wave] = l;
-        __syncthreads();
-        h = max(max(sh.hit[0], sh.hit[1]), max(sh.hit[2], sh.hit[3]));
-        __syncthreads();
-        // cumulative mass before it
-        double b = 0.0;
-        if ((int)threadIdx.x == h / PER) {
-            double cc = off + incl - ls;
-            for (int i = 0; i < PER; ++i) { if ((int)threadIdx.x * PER + i == h) break; cc += w[i]; }
-            sh.scan[0] = cc;
-        }
-        __syncthreads();
-        b = sh.scan[0];
-        __syncthreads();
-        *before = b;
-        return h < 0 ? 0 : h;
+    const int hmin = wave_minmax_i<false>(hit);
+    const int lmax = wave_minmax_i<true>(last);
+    if (lane == 0) {
+        sh.hit[slot][wave] = hmin;
+        sh.last[slot][wave] = lmax;
     }
-    if ((int)threadIdx.x == h / PER) sh.scan[0] = hit_before;
-    __syncthreads();
-    *before = sh.scan[0];
-    __syncthreads();
-    return h;
+    if (hmin != 0x7fffffff && hit == hmin) sh.hb[slot][wave] = hit_before;
+    lds_barrier();
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+        const int h = sh.hit[slot][w2];
+        if (h != 0x7fffffff) {
+            *before = sh.hb[slot][w2];
+            return h;
+        }
+    }
+    // no crossing (block-uniform): the last positive item and the mass before it
+    const int l = max(max(sh.last[slot][0], sh.last[slot][1]), max(sh.last[slot][2], sh.last[slot][3]));
+    if (l >= 0 && (int)threadIdx.x == l / PER) {
+        double cc = c0;
+        for (int i = 0; i < PER; ++i) {
+            if ((int)threadIdx.x * PER + i == l) break;
+            cc += w[i];
+        }
+        sh.fb[slot] = cc;
+    }
+    lds_barrier();
+    *before = (l >= 0) ? sh.fb[slot] : 0.0;
+    return l < 0 ? 0 : l;
+}
+
+// One request's logits over the 256-wide tile at v0 (thread t: column v0 + t),
+// bit-identical to the bias pass: W2 fragments staged as there, the request's
+// embedding row in column 0 of the N-tile, the same MFMA sequence from zero,
+// then the base logit added.  xb: the thread's base logit (-inf past V), loaded
+// by the caller as early as it likes; e_row: the embedding row (zeros when prev
+// selects none), in LDS and visible after the staging's first barrier.
+__device__ __forceinline__ float tile_logit(const uint16_t* __restrict__ W2, int V, int r, int v0,
+                                            const uint16_t* e_row, float xb, PassLds& L,
+                                            PickScratch& sh)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = lane >> 5, c32 = lane & 31;
+    bf16x8 afrag[2][kKSteps];
+    stage_w2_frags(W2, V, r, v0, L, afrag);
+    floatx16 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (c32 == 0) u = *reinterpret_cast<const uint4*>(e_row + ks * kKStep + 8 * h);
+        const bf16x8 bv = as_bf16x8(u);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma32_bf16(afrag[t][ks], bv, acc[t]);
+    }
+    if (c32 == 0) {
+#pragma unroll
+        for (int s = 0; s < 32; ++s) sh.lg[wave * 64 + 32 * h + s] = acc[s >> 4][s & 15];
+    }
+    lds_barrier();
+    return xb + sh.lg[threadIdx.x];
 }
 
 }  // namespace dsp

@@ -250,14 +250,17 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     uint32_t round, int n_vt, VerifyWs ws)
 {
     __shared__ PickScratch sh;
+    __shared__ PassLds L;
+    __shared__ __attribute__((aligned(16))) uint16_t e_row[kRankMax];
     const int n = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int l = clamp_len(len, n, gamma);
     const int m = min(max(n_accept[n], 0), l);
     const int slot = ws.resid_slot[n];
     const double u = uniform24(seed, round, (uint32_t)n, (uint32_t)m, 2u);
+    const float itL = fold_itl(inv_temp);
 
-    if (slot >= 0) {
+    if (slot >= 0) {   // workgroup-uniform
         const Part* rp = ws.resid_part + (int64_t)slot * n_vt;
         double w[PER];
         double ls = 0.0;
@@ -267,35 +270,38 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
             w[i] = (t < n_vt) ? rp[t].s : 0.0;
             ls += w[i];
         }
-        ls = wave_sum(ls);
-        if (lane == 0) sh.wsum[wave] = ls;
-        __syncthreads();
-        const double rsum = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
-        __syncthreads();
+        const double rsum = block_sum256(ls, sh);
         if (rsum > 0.0) {
             const double tgt = u * rsum;
             double before;
-            const int tsel = block_locate<PER>(w, tgt, &before, sh);
+            const int tsel = block_locate<PER>(w, tgt, &before, sh, 0);
+            // the draft row's logits over the chosen tile, rebuilt as the residual
+            // pass computed them, and the target row's
             const int prev = prev_token(anchor, tok, n, gamma, m, V);
             const LT* drow = base + (int64_t)n * bs.rs + (int64_t)m * bs.ps;
-            block_logits64<LT>(drow, E, W2, V, r, prev, tsel * kVocabTile + wave * 64, lane,
-                               sh.lg + wave * 64);
-            __syncthreads();
             const LT* trow = target + (int64_t)n * ts.rs + (int64_t)m * ts.ps;
+            const int v = tsel * kVocabTile + tid;
+            const float xb = (v < V) ? Logit<LT>::at(drow, v) : -INFINITY;
+            const float xt = (v < V) ? Logit<LT>::at(trow, v) : -INFINITY;
             const float Md = (float)stats[2 * ((int64_t)n * gamma + m)];
             const double invZd = 1.0 / stats[2 * ((int64_t)n * gamma + m) + 1];
             const float Mt = ws.row_m[n];
             const double invZt = 1.0 / ws.row_z[n];
-            const int v = tsel * kVocabTile + tid;
+            if (tid < kRankMax / 8) {
+                const int kk = 8 * tid;
+                uint4 ev = make_uint4(0, 0, 0, 0);
+                if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
+                *reinterpret_cast<uint4*>(e_row + kk) = ev;
+            }
+            const float zd = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, L, sh);
             double rho[1] = {0.0};
-            const float zd = sh.lg[tid];
             if (v < V && zd != -INFINITY) {
-                const double pv = (double)wexp(Logit<LT>::at(trow, v) - Mt, fold_itl(inv_temp)) * invZt;
-                const double qv = (double)wexp(zd - Md, fold_itl(inv_temp)) * invZd;
+                const double pv = (double)wexp(xt - Mt, itL) * invZt;
+                const double qv = (double)wexp(zd - Md, itL) * invZd;
                 rho[0] = fmax(pv - qv, 0.0);
             }
             double b2;
-            const int loc = block_locate<1>(rho, tgt - before, &b2, sh);
+            const int loc = block_locate<1>(rho, tgt - before, &b2, sh, 1);
             if (tid == 0) y[n] = tsel * kVocabTile + loc;
             return;
         }
@@ -322,19 +328,15 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
         w[i] = (mt[i] == -INFINITY) ? 0.0 : st[i] * exp(((double)mt[i] - (double)M) * (double)inv_temp);
         ls += w[i];
     }
-    ls = wave_sum(ls);
-    if (lane == 0) sh.wsum[wave] = ls;
-    __syncthreads();
-    const double Z = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
-    __syncthreads();
+    const double Z = block_sum256(ls, sh);
     const double tgt = u * Z;
     double before;
-    const int tsel = block_locate<PER>(w, tgt, &before, sh);
+    const int tsel = block_locate<PER>(w, tgt, &before, sh, 0);
     const LT* trow = target + (int64_t)n * ts.rs + (int64_t)row_j * ts.ps;
     const int v = tsel * kVocabTile + tid;
-    double e1[1] = {(v < V) ? (double)wexp(Logit<LT>::at(trow, v) - M, fold_itl(inv_temp)) : 0.0};
+    double e1[1] = {(v < V) ? (double)wexp(Logit<LT>::at(trow, v) - M, itL) : 0.0};
     double b2;
-    const int loc = block_locate<1>(e1, tgt - before, &b2, sh);
+    const int loc = block_locate<1>(e1, tgt - before, &b2, sh, 1);
     if (tid == 0) y[n] = tsel * kVocabTile + loc;
 }
 

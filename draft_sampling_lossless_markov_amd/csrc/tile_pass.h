@@ -101,11 +101,11 @@ struct PassArgs {
 // ---------------------------------------------------------------------------
 constexpr int kPassBlock = 32;   // requests per block (one 32-wide N-tile)
 
-// Two workgroups per CU for the bf16 softmax / greedy passes on 16-byte-aligned
-// rows (their registers fit 256 per lane); the residual pass, fp32 rows and the
-// element-wise loads of other vocabulary sizes need more and run one.
+// Two workgroups per CU for the bf16 passes on 16-byte-aligned rows (their
+// registers fit 256 per lane); fp32 rows and the element-wise loads of other
+// vocabulary sizes need more and run one.
 template <typename LT, int KIND, bool VEC>
-constexpr int pass_min_blocks() { return (sizeof(LT) == 2 && KIND != kResidual && VEC) ? 2 : 1; }
+constexpr int pass_min_blocks() { return (sizeof(LT) == 2 && VEC) ? 2 : 1; }
 
 // 32 bytes of -inf in either logit type: the source of every logit word that
 // falls outside the row (or belongs to a request past the end of the list).
@@ -269,8 +269,14 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
 
     // --- logit words of block blk for this lane (its request, its 32 columns
     // as four 8-element chunks) into ring slot sl
-    uint4 rs[2][4 * RW];
-    uint4 rt[RES ? 2 : 1][4 * RW];
+    // The softmax and greedy passes keep a two-block ring of logit words.  The
+    // residual pass (a few blocks of rejected rows) fetches a block's draft and
+    // target words at the block's start, under its MFMA chain, which keeps its
+    // registers within two workgroups per CU.
+    constexpr int kRing = RES ? 1 : 2;
+    uint4 rs[kRing][4 * RW];
+    const LT* trow = nullptr;
+    uint4 rt[RES ? 4 * RW : 1];
     auto load_raw = [&](int blk, int sl) {
         const int e = n_begin + blk * kPassBlock + c32;
         const bool ok = e < n_end;
@@ -286,11 +292,11 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
             load8_any<LT, VEC>(row, v0, V, ok, v0 + 8 <= V, rs[sl] + c * RW);
         }
         if constexpr (RES) {
-            const LT* trow = target + (int64_t)n * a.ts.rs + (int64_t)m * a.ts.ps;
+            trow = target + (int64_t)n * a.ts.rs + (int64_t)m * a.ts.ps;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int v0 = v_lane + 8 * c;
-                load8_any<LT, VEC>(trow, v0, V, ok, v0 + 8 <= V, rt[sl] + c * RW);
+                load8_any<LT, VEC>(trow, v0, V, ok, v0 + 8 <= V, rt + c * RW);
             }
         }
     };
@@ -306,12 +312,12 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
         load_e(0, prev0);
         store_e(0, 0, prev0);
         __builtin_amdgcn_sched_barrier(0);
-        load_raw(0, 0);
+        if constexpr (!RES) load_raw(0, 0);
         __builtin_amdgcn_sched_barrier(0);
         load_e(1, prev1);
         prev2 = prev_raw(2);
         __builtin_amdgcn_sched_barrier(0);
-        load_raw(1, 1);
+        if constexpr (!RES) load_raw(1, 1);
     }
     lds_barrier();
 
@@ -323,6 +329,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
 
         // bias of the block: all sixteen k-steps (fragments past r are zero on
         // both sides, so they add exact zeros)
+        if constexpr (RES) load_raw(i, 0);
         floatx16 acc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -348,12 +355,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
         float z[32];
 #pragma unroll
         for (int s = 0; s < 32; ++s)
-            z[s] = Logit<LT>::raw_at(rs[sl] + (s >> 3) * RW, s & 7) + acc[s >> 4][s & 15];
-        float xt[RES ? 32 : 1];
-        if constexpr (RES) {
-#pragma unroll
-            for (int s = 0; s < 32; ++s) xt[s] = Logit<LT>::raw_at(rt[sl] + (s >> 3) * RW, s & 7);
-        }
+            z[s] = Logit<LT>::raw_at(rs[RES ? 0 : sl] + (s >> 3) * RW, s & 7) + acc[s >> 4][s & 15];
         if (i + 1 < n_blk) store_e(b ^ 1, i + 1, prev1);
         load_e(i + 2, prev2);         // block i + 2's embedding rows
         prev1 = prev2;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
         // the loads above are due one block earlier than the logit words below:
         // keep them ahead in issue order (the load counter is in-order)
         __builtin_amdgcn_sched_barrier(0);
-        load_raw(i + 2, sl);          // block i + 2's logit words
+        if constexpr (!RES) load_raw(i + 2, sl);   // block i + 2's logit words
 
         Part res;
         if constexpr (KIND == kGreedy) {
@@ -399,17 +401,19 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
             const int n = a.list[e];
             const int m = a.list_m[e];
             const float Md = (float)a.stats[2 * ((int64_t)n * gamma + m)];
-            const double invZd = 1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1];
+            const float invZd = (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]);
             const float Mt = a.row_m[n];
-            const double invZt = 1.0 / a.row_z[n];
-            double sum = 0.0;
+            const float invZt = (float)(1.0 / a.row_z[n]);
+            // max(0, p - q) per column in fp32 (relative error ~1e-7 of the larger
+            // of p and q), four running fp32 sums over the lane's 32 columns, then
+            // fp64 across lanes, tiles and rows
+            float d4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 32; ++s) {
-                const double pv = (double)wexp(xt[s] - Mt, itL) * invZt;
-                const double qv = (double)wexp(z[s] - Md, itL) * invZd;
-                sum += fmax(pv - qv, 0.0);
+                const float xt = Logit<LT>::raw_at(rt + (s >> 3) * RW, s & 7);
+                d4[s & 3] += fmaxf(wexp(xt - Mt, itL) * invZt - wexp(z[s] - Md, itL) * invZd, 0.0f);
             }
-            res = Part{0.f, 0, xsum<32>(sum)};
+            res = Part{0.f, 0, xsum<32>((double)((d4[0] + d4[1]) + (d4[2] + d4[3])))};
         }
         if (h == 0) red[b][wave][c32] = res;
         lds_barrier();

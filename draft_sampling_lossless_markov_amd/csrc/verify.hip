@@ -31,6 +31,7 @@ constexpr int kSpanTiles = 32;   // tiles per verify_rows work item (8192 column
 
 struct VerifyWs {
     Part* rowpart;       // [R, gamma+1, n_vt]
+    Part* spanpart;      // [R, gamma+1, 4 spans] the same rows, 8 tiles combined
     float* zx;           // [R, gamma] target logit at the drafted token
     int* resid_cnt;      // [1]
     int* resid_list;     // [R] request of each queue slot
@@ -50,7 +51,9 @@ inline VerifyWs carve(void* ws, int R, int gamma, int V, size_t* total)
     char* p = static_cast<char*>(ws);
     size_t off = 0;
     VerifyWs w;
+    const size_t spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     w.rowpart = reinterpret_cast<Part*>(p + off);     off += align256((size_t)R * (gamma + 1) * n_vt * sizeof(Part));
+    w.spanpart = reinterpret_cast<Part*>(p + off);    off += align256((size_t)R * (gamma + 1) * 4 * spans * sizeof(Part));
     w.zx = reinterpret_cast<float*>(p + off);         off += align256((size_t)R * gamma * sizeof(float));
     w.resid_cnt = reinterpret_cast<int*>(p + off);    off += align256(sizeof(int));
     w.resid_list = reinterpret_cast<int*>(p + off);   off += align256((size_t)R * sizeof(int));
@@ -123,6 +126,13 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
             am = argmax_merge(am, b);
         }
         if (sub == 0 && t < n_vt) out[t] = Part{am.v, am.i, 0.0};
+        // the wave's 8 tiles (lane groups) combined: one partial per wave
+        ArgMax b8;
+        b8.v = __shfl_xor(am.v, 8, kWave);
+        b8.i = __shfl_xor(am.i, 8, kWave);
+        am = xargmax<32>(xargmax<16>(argmax_merge(am, b8)));
+        if (lane == 0)
+            ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{am.v, am.i, 0.0};
     } else {
         float m = -INFINITY;
 #pragma unroll
@@ -142,6 +152,15 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
         if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
+        // the wave's 8 tiles (lane groups) rescaled to their max in fp64 and
+        // summed: one partial per wave
+        float mw = fmaxf(m, __shfl_xor(m, 8, kWave));
+        mw = xmax<32>(xmax<16>(mw));
+        double sw = (m == -INFINITY) ? 0.0 : s * exp(((double)m - (double)mw) * (double)inv_temp);
+        sw += __shfl_xor(sw, 8, kWave);
+        sw = xsum<32>(xsum<16>(sw));
+        if (lane == 0)
+            ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{mw, 0, sw};
         if (tid == 0 && j < l) {
             const int xj = tok[(int64_t)n * gamma + j];
             const int lo = sp * kSpanTiles * kVocabTile;
@@ -153,8 +172,10 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // verify_accept: one workgroup per request; wave w combines rows j = w, w+4, ...
+// from their 8-tile partials (lane l: partials [l * PER, l * PER + PER); at
+// most 256 per row).
 // ---------------------------------------------------------------------------
-template <bool GREEDY>
+template <bool GREEDY, int PER>
 __global__ __launch_bounds__(256) void verify_accept_kernel(
     const int32_t* __restrict__ anchor, int V,
     const int32_t* __restrict__ tok, const float* __restrict__ q, const int32_t* __restrict__ len,
@@ -170,13 +191,21 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
     const int n = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l = clamp_len(len, n, gamma);
-    const Part* rows = ws.rowpart + (int64_t)n * (gamma + 1) * n_vt;
+    const int np = 4 * ((n_vt + kSpanTiles - 1) / kSpanTiles);
+    const Part* rows = ws.spanpart + (int64_t)n * (gamma + 1) * np;
     const int last_row = GREEDY ? l : l - 1;
     for (int j = wave; j <= last_row; j += 4) {
-        const Part* pp = rows + (int64_t)j * n_vt;
+        const Part* pp = rows + (int64_t)j * np;
+        Part pt[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = lane * PER + i;
+            pt[i] = (t < np) ? pp[t] : Part{-INFINITY, 0x7fffffff, 0.0};
+        }
         if constexpr (GREEDY) {
             ArgMax am{-INFINITY, 0x7fffffff};
-            for (int t = lane; t < n_vt; t += kWave) am = argmax_merge(am, ArgMax{pp[t].m, pp[t].idx});
+#pragma unroll
+            for (int i = 0; i < PER; ++i) am = argmax_merge(am, ArgMax{pt[i].m, pt[i].idx});
             am = wave_argmax(am);
             if (lane == 0) {
                 am_s[j] = am.i;
@@ -188,14 +217,14 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
             }
         } else {
             float M = -INFINITY;
-            for (int t = lane; t < n_vt; t += kWave) M = fmaxf(M, pp[t].m);
-            M = wave_max(M);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) M = fmaxf(M, pt[i].m);
+            M = wave_max_f(M);
             double Z = 0.0;
-            for (int t = lane; t < n_vt; t += kWave) {
-                const Part p = pp[t];
-                if (p.m != -INFINITY) Z += p.s * exp(((double)p.m - (double)M) * (double)inv_temp);
-            }
-            Z = wave_sum(Z);
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (pt[i].m != -INFINITY) Z += pt[i].s * exp(((double)pt[i].m - (double)M) * (double)inv_temp);
+            Z = wave_sum_d(Z);
             if (lane == 0) {
                 const int64_t o = (int64_t)n * gamma + j;
                 const double p = exp(((double)ws.zx[o] - (double)M) * (double)inv_temp) / Z;
@@ -350,6 +379,26 @@ size_t verify_workspace_bytes(int R, int gamma, int V)
     return total;
 }
 
+template <bool GREEDY>
+static void launch_accept(const int32_t* anchor, int V, const int32_t* tok, const float* q,
+                          const int32_t* len, int8_t* accept, int32_t* n_accept, int32_t* y,
+                          float* p, int R, int gamma, float it, uint64_t seed, uint32_t round,
+                          int n_vt, const VerifyWs& ws, hipStream_t s)
+{
+    const int np = 4 * ((n_vt + kSpanTiles - 1) / kSpanTiles);
+    const int per = (np + kWave - 1) / kWave;     // <= 4 for V <= kVocabMax
+#define DSP_ACCEPT(P)                                                                          \
+    hipLaunchKernelGGL((verify_accept_kernel<GREEDY, P>), dim3(R), dim3(256), 0, s, anchor, V, \
+                       tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws)
+    if (per <= 1) DSP_ACCEPT(1);
+    else if (per <= 2) DSP_ACCEPT(2);
+    else if (per <= 4) DSP_ACCEPT(4);
+    else if (per <= 8) DSP_ACCEPT(8);
+    else if (per <= 16) DSP_ACCEPT(16);
+    else DSP_ACCEPT(32);
+#undef DSP_ACCEPT
+}
+
 template <typename LT, int PER>
 static void launch_vpick(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
                          const uint16_t* E, const uint16_t* W2,
@@ -383,14 +432,14 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     if (greedy) {
         hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, ts, tok, len,
                            R, gamma, V, it, n_vt, ws);
-        hipLaunchKernelGGL((verify_accept_kernel<true>), dim3(R), dim3(256), 0, s, anchor, V, tok, q, len,
-                           accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws);
+        launch_accept<true>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed,
+                            round, n_vt, ws, s);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, ts, tok, len, R,
                        gamma, V, it, n_vt, ws);
-    hipLaunchKernelGGL((verify_accept_kernel<false>), dim3(R), dim3(256), 0, s, anchor, V, tok, q, len,
-                       accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws);
+    launch_accept<false>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round,
+                         n_vt, ws, s);
     PassArgs a{};
     a.base = base; a.target = target; a.bs = bs; a.ts = ts;
     a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;

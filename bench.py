@@ -2,9 +2,12 @@
 
 One step = one decode round over a batch of synthetic inputs already resident in
 HBM: gamma x dsp_draft_step, dsp_confidence, dsp_schedule, dsp_verify, issued
-back to back on one stream.  Prints one JSON line (metric, throughput, the
-roofline of the dominant entry point measured with HIP events on the launch
-stream inside the timed region, and the CPU oracle timed on a bounded sample).
+back to back on one stream.  The throughput (`value`) times K rounds replayed
+from HIP graphs, one graph captured per round (its own round index and input
+set), so kernel launch gaps are not counted; a second, eager pass over the same
+K rounds times every entry point with HIP events on the launch stream and gives
+the roofline of the dominant one.  Prints one JSON line, with the CPU oracle
+timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
 """
@@ -94,6 +97,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the rounds as eager launches instead of graph replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy five times (the known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -129,40 +134,66 @@ def main():
     stream = torch.cuda.current_stream()
     seed = 0
 
-    def one_round(i, ev=None):
+    def one_round(i, ev=None, s=stream):
         inp = sets[i % len(sets)]
         for k in range(g):
             if ev is not None:
-                ev[k].record(stream)
+                ev[k].record(s)
             dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
-                               rd.stats, k, temp, seed, i, rd.ws_draft, stream)
+                               rd.stats, k, temp, seed, i, rd.ws_draft, s)
         if ev is not None:
-            ev[g].record(stream)
-        rd.confidence(inp, stream)
+            ev[g].record(s)
+        rd.confidence(inp, s)
         if ev is not None:
-            ev[g + 1].record(stream)
-        rd.schedule(inp, stream=stream)
+            ev[g + 1].record(s)
+        rd.schedule(inp, stream=s)
         if ev is not None:
-            ev[g + 2].record(stream)
-        rd.verify(inp, temp, seed, i, stream)
+            ev[g + 2].record(s)
+        rd.verify(inp, temp, seed, i, s)
         if ev is not None:
-            ev[g + 3].record(stream)
+            ev[g + 3].record(s)
 
     for i in range(args.warmup):
         one_round(i)
     torch.cuda.synchronize()
     K = args.steps
+
+    # eager pass: per entry point event timing (roofline, breakdown)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(g + 4)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
+    e_start.record(stream)
     for i in range(K):
         one_round(args.warmup + i, evs[i])
-    t_end.record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / K
+    eager_ms_per_step = e_start.elapsed_time(e_end) / K
+
+    # throughput pass: the same K rounds replayed from one captured graph each
+    if args.eager:
+        ms_per_step = eager_ms_per_step
+        timing = "eager launches"
+    else:
+        cap = torch.cuda.Stream()
+        graphs = []
+        for i in range(K):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap):
+                one_round(args.warmup + i, s=cap)
+            graphs.append(gr)
+        for gr in graphs[:2]:
+            gr.replay()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for gr in graphs:
+            gr.replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = t_start.elapsed_time(t_end) / K
+        timing = "HIP graph replay, one graph per round"
 
     # per entry point (event-bracketed) average durations, in ms
     draft_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(g)] for i in range(K)])
@@ -207,6 +238,7 @@ def main():
                             "schedule": round(float(sched_ms.mean()) * 1e3, 2),
                             "verify": round(float(ver_ms.mean()) * 1e3, 2)},
         "verified_per_round": len_per_round, "drafted_per_round": R * g,
+        "timing": timing, "eager_ms_per_step": round(eager_ms_per_step, 5),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -180,6 +180,30 @@ def test_determinism_and_replay():
         assert np.array_equal(outs[0][k], outs[1][k]), k
 
 
+@pytest.mark.parametrize("temp", [1.0, 0.0])
+def test_graph_capture_replays_match_eager(temp):
+    """A whole round captured in a HIP graph: every replay, with other eager rounds
+    and synchronisations between replays, reproduces the eager round bit for bit."""
+    wl = custom(70, 5, 1000, 24, 100, torch.bfloat16)
+    inp = to_dev(make_inputs(wl, 2))
+    rd = Round(70, 5, 1000, 24)
+    keys = ("tok", "q", "stats", "c", "len", "a", "B", "accept", "n_accept", "y", "p")
+    rd.run(inp, temp, 7, 11)
+    torch.cuda.synchronize()
+    ref = {k: np_(getattr(rd, k)).copy() for k in keys}
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        rd.run(inp, temp, 7, 11, stream=cap)
+    for rep in range(4):
+        rd.run(inp, temp, 7, 20 + rep)          # different work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert np.array_equal(np_(getattr(rd, k)), ref[k]), (rep, k)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, stage by stage on sampled requests
 # ---------------------------------------------------------------------------

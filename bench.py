@@ -29,6 +29,14 @@ from draft_sampling_lossless_markov_amd.workloads import (BENCH_LAYOUT, WORKLOAD
                                                           make_inputs)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+# sources of the draft-step kernels; the profiled HBM traffic is reported only
+# while they are byte-for-byte the profiled ones
+DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/csrc/draft.hip",
+                 "draft_sampling_lossless_markov_amd/csrc/tile_pass.h",
+                 "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",
+                 "draft_sampling_lossless_markov_amd/csrc/dsp_device.h",
+                 "draft_sampling_lossless_markov_amd/csrc/dsp_launch.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_step_traffic_qwen3-4b-R64-g7-V151936.txt")
 METRIC = "verified draft positions/sec (draft+verify) and % of MI355X HBM roofline"
 UNIT = "verified draft positions/s"
 
@@ -54,6 +62,29 @@ def draft_step_bytes(inp):
     s = inp["base"].element_size()
     R, V, r = inp["R"], inp["V"], inp["r"]
     return s * R * V + 2 * r * V + 2 * R * r + R * 16
+
+
+def draft_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DRAFT_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload):
+    """HBM bytes per draft step (FETCH_SIZE and WRITE_SIZE of its two kernels,
+    scaled by a plain copy) from the committed profile, or None when that profile
+    is of other kernel sources or another workload."""
+    try:
+        kv = dict(line.split(None, 1) for line in open(TRAFFIC_FILE).read().splitlines()
+                  if line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("workload", "").strip() != workload or kv.get("sources_sha256", "").strip() != draft_sources_digest():
+        return None
+    return int(kv["draft_step_bytes"])
 
 
 def cpu_baseline(wl, inp, temp, budget_s):
@@ -217,9 +248,10 @@ def main():
     step_bytes = draft_step_bytes(inp0)
     draft_avg_s = float(draft_ms.mean()) * 1e-3
     achieved = step_bytes / draft_avg_s / 1e9
+    traffic = profiled_traffic(wl.name)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "dsp_draft_step (draft_partials_kernel + draft_pick_kernel)",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "dsp_draft_step (bias_pass_kernel + draft_pick_kernel)",
             "bytes_per_launch": int(step_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2)}
 
     result = {

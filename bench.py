@@ -1,7 +1,7 @@
 """Benchmark of the DSpark draft / confidence / schedule / verify path on one GPU.
 
 One step = one decode round over a batch of synthetic inputs already resident in
-HBM: gamma x dsp_draft_step, dsp_confidence, dsp_schedule, dsp_verify, issued
+HBM: dsp_draft_step (all gamma positions), dsp_confidence, dsp_schedule, dsp_verify, issued
 back to back on one stream.  The throughput (`value`) times K rounds replayed
 from HIP graphs, one graph captured per round (its own round index and input
 set), so kernel launch gaps are not counted; a second, eager pass over the same
@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # sources of the draft-step kernels; the profiled HBM traffic is reported only
 # while they are byte-for-byte the profiled ones
 DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/csrc/draft.hip",
+                 "draft_sampling_lossless_markov_amd/csrc/draft_run.h",
                  "draft_sampling_lossless_markov_amd/csrc/tile_pass.h",
                  "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_device.h",
@@ -55,13 +56,28 @@ def round_bytes(wl, inp, len_sum, n_rej, greedy):
     return s * V * rows + 2 * r * V + 2 * R * g * (d + r)
 
 
-def draft_step_bytes(inp):
-    """Compulsory bytes of one dsp_draft_step launch pair: the [R, V] base slice,
-    all of W2 (every vocabulary column needs its bias), the gathered E rows and
-    the per-request outputs."""
+def draft_call_bytes(inp):
+    """Compulsory bytes of one dsp_draft_step call over all gamma positions: the
+    gamma [R, V] base slices, all of W2 once (every vocabulary column needs its
+    bias), the gathered E rows and the per-request outputs."""
     s = inp["base"].element_size()
-    R, V, r = inp["R"], inp["V"], inp["r"]
-    return s * R * V + 2 * r * V + 2 * R * r + R * 16
+    R, g, V, r = inp["R"], inp["gamma"], inp["V"], inp["r"]
+    return g * s * R * V + 2 * r * V + g * (2 * R * r + R * 16)
+
+
+def probe_draft_path(call):
+    """'persistent' when the persistent draft launch serves this workload, else
+    'streaming' (the path AUTO selects); leaves the selection on AUTO."""
+    dsp.dsp_set_draft_path(dsp.DSP_DRAFT_PERSISTENT)
+    try:
+        call()
+        path = "persistent"
+    except dsp.DspError:
+        path = "streaming"
+    finally:
+        dsp.dsp_set_draft_path(dsp.DSP_DRAFT_AUTO)
+    torch.cuda.synchronize()
+    return path
 
 
 def draft_sources_digest():
@@ -73,18 +89,20 @@ def draft_sources_digest():
     return h.hexdigest()
 
 
-def profiled_traffic(workload):
-    """HBM bytes per draft step (FETCH_SIZE and WRITE_SIZE of its two kernels,
-    scaled by a plain copy) from the committed profile, or None when that profile
-    is of other kernel sources or another workload."""
+def profiled_traffic(workload, path):
+    """HBM bytes of one dsp_draft_step call (FETCH_SIZE and WRITE_SIZE of its
+    kernels, scaled by a plain copy) from the committed profile, or None when that
+    profile is of other kernel sources, another workload or another draft path."""
     try:
         kv = dict(line.split(None, 1) for line in open(TRAFFIC_FILE).read().splitlines()
                   if line and not line.startswith("#"))
     except OSError:
         return None
-    if kv.get("workload", "").strip() != workload or kv.get("sources_sha256", "").strip() != draft_sources_digest():
+    if (kv.get("workload", "").strip() != workload
+            or kv.get("draft_path", "").strip() != path
+            or kv.get("sources_sha256", "").strip() != draft_sources_digest()):
         return None
-    return int(kv["draft_step_bytes"])
+    return int(kv["draft_call_bytes"])
 
 
 def cpu_baseline(wl, inp, temp, budget_s):
@@ -165,24 +183,30 @@ def main():
     stream = torch.cuda.current_stream()
     seed = 0
 
+    def draft(i, s=stream):
+        inp = sets[i % len(sets)]
+        dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
+                           rd.stats, 0, temp, seed, i, rd.ws_draft, s, n_steps=g)
+
     def one_round(i, ev=None, s=stream):
         inp = sets[i % len(sets)]
-        for k in range(g):
-            if ev is not None:
-                ev[k].record(s)
-            dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
-                               rd.stats, k, temp, seed, i, rd.ws_draft, s)
         if ev is not None:
-            ev[g].record(s)
+            ev[0].record(s)
+        draft(i, s)
+        if ev is not None:
+            ev[1].record(s)
         rd.confidence(inp, s)
         if ev is not None:
-            ev[g + 1].record(s)
+            ev[2].record(s)
         rd.schedule(inp, stream=s)
         if ev is not None:
-            ev[g + 2].record(s)
+            ev[3].record(s)
         rd.verify(inp, temp, seed, i, s)
         if ev is not None:
-            ev[g + 3].record(s)
+            ev[4].record(s)
+
+    draft_path = probe_draft_path(lambda: draft(0))
+    log(f"draft path: {draft_path}")
 
     for i in range(args.warmup):
         one_round(i)
@@ -190,7 +214,7 @@ def main():
     K = args.steps
 
     # eager pass: per entry point event timing (roofline, breakdown)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(g + 4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -227,10 +251,10 @@ def main():
         timing = "HIP graph replay, one graph per round"
 
     # per entry point (event-bracketed) average durations, in ms
-    draft_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(g)] for i in range(K)])
-    conf_ms = np.array([evs[i][g].elapsed_time(evs[i][g + 1]) for i in range(K)])
-    sched_ms = np.array([evs[i][g + 1].elapsed_time(evs[i][g + 2]) for i in range(K)])
-    ver_ms = np.array([evs[i][g + 2].elapsed_time(evs[i][g + 3]) for i in range(K)])
+    draft_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
+    conf_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
+    sched_ms = np.array([evs[i][2].elapsed_time(evs[i][3]) for i in range(K)])
+    ver_ms = np.array([evs[i][3].elapsed_time(evs[i][4]) for i in range(K)])
 
     # replay the timed rounds (deterministic) to count verified positions
     len_sum = rej = 0
@@ -245,14 +269,17 @@ def main():
     value = len_per_round / (ms_per_step * 1e-3)
     A = round_bytes(wl, inp0, len_per_round, rej_per_round, greedy)
 
-    step_bytes = draft_step_bytes(inp0)
+    call_bytes = draft_call_bytes(inp0)
     draft_avg_s = float(draft_ms.mean()) * 1e-3
-    achieved = step_bytes / draft_avg_s / 1e9
-    traffic = profiled_traffic(wl.name)
+    achieved = call_bytes / draft_avg_s / 1e9
+    traffic = profiled_traffic(wl.name, draft_path)
+    kernels = ("draft_run_kernel (one cooperative launch, all gamma positions)"
+               if draft_path == "persistent" else
+               "bias_pass_kernel + draft_pick_kernel per position")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "dsp_draft_step (bias_pass_kernel + draft_pick_kernel)",
-            "bytes_per_launch": int(step_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2)}
+            "kernel": f"dsp_draft_step, {g} positions: {kernels}",
+            "bytes_per_launch": int(call_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": K,
@@ -262,10 +289,11 @@ def main():
         "config": {"workload": wl.name, "R": R, "gamma": g, "V": V, "r": r, "d": inp0["d"],
                    "mode": mode, "scheduler": "on" if wl.mode == 1 else "off (every position verified)",
                    "base_layout": BENCH_LAYOUT + "-major [gamma, R, V]",
+                   "draft_path": draft_path,
                    "parallelism": "single GPU"},
         "round_roofline": {"algorithmic_bytes": int(A), "t_roof_us": round(A / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                            "frac": round(A / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)},
-        "entry_points_us": {"draft_step": round(float(draft_ms.mean()) * 1e3, 2),
+        "entry_points_us": {"draft_step_all_positions": round(float(draft_ms.mean()) * 1e3, 2),
                             "confidence": round(float(conf_ms.mean()) * 1e3, 2),
                             "schedule": round(float(sched_ms.mean()) * 1e3, 2),
                             "verify": round(float(ver_ms.mean()) * 1e3, 2)},

@@ -86,7 +86,18 @@ const char* dsp_status_string(dsp_status s)
 
 const char* dsp_last_error(void) { return g_err; }
 
-int dsp_version(void) { return 200; }
+int dsp_version(void) { return 300; }
+
+dsp_status dsp_set_draft_path(int path)
+{
+    if (path != DSP_DRAFT_AUTO && path != DSP_DRAFT_STREAMING && path != DSP_DRAFT_PERSISTENT)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_set_draft_path: unknown path %d", path);
+    static_assert(DSP_DRAFT_AUTO == dsp::kDraftPathAuto && DSP_DRAFT_STREAMING == dsp::kDraftPathStream &&
+                      DSP_DRAFT_PERSISTENT == dsp::kDraftPathPersistent,
+                  "path codes");
+    dsp::set_draft_path(path);
+    return ok();
+}
 
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 {
@@ -98,7 +109,7 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
                           const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
-                          double* stats, int R, int gamma, int V, int r, int k,
+                          double* stats, int R, int gamma, int V, int r, int k, int n_steps,
                           float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream)
 {
@@ -110,6 +121,9 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
     if (st != DSP_OK) return st;
     if (k < 0 || k >= gamma)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: k = %d outside [0, gamma)", k);
+    if (n_steps < 1 || n_steps > gamma - k)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: n_steps = %d outside [1, gamma - k] (k = %d)",
+                    n_steps, k);
     st = check_strides("dsp_draft_step", "base", base_rs, base_ps);
     if (st != DSP_OK) return st;
     if (!(temperature >= 0.0f) || std::isinf(temperature))
@@ -122,7 +136,7 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                     ws_bytes, need);
     return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
                                              dtype == DSP_BF16, E, W2, anchor, tok, q,
-                                             stats, R, gamma, V, r, k, temperature, seed, round,
+                                             stats, R, gamma, V, r, k, n_steps, temperature, seed, round,
                                              ws, static_cast<hipStream_t>(stream)),
                       "dsp_draft_step launch");
 }

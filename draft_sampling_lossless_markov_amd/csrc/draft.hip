@@ -1,6 +1,8 @@
 // draft.hip -- semi-autoregressive draft step with the Markov head (gfx950).
 //
-// One draft position k for all R requests, in two launches:
+// Draft positions k .. k + n_steps - 1 for all R requests.  Where the
+// vocabulary slice of W2 fits on chip (bf16 rows), one persistent launch runs
+// every position (draft_run.h); otherwise each position takes two launches:
 //   bias_pass_kernel<kSample | kGreedy>: per (request, 256-wide vocabulary tile)
 //     partials of logit = base[n, k, :] + E[prev_n] . W2^T (bias by bf16 MFMA,
 //     never stored);
@@ -13,7 +15,10 @@
 // a low-rank matrix (page "DeepSeek联合北大最新文章DSpark", two-stage design);
 // only the token id is carried to the next position (page "DeepSeek DSpark 技术
 // 解析", section 四).
+#include <atomic>
+
 #include "bias_tile.h"
+#include "draft_run.h"
 #include "dsp_device.h"
 #include "dsp_launch.h"
 #include "tile_pass.h"
@@ -112,11 +117,19 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-size_t draft_workspace_bytes(int R, int V)
+constexpr size_t kRunCtlBytes = 256;
+
+// partials of either path (the streaming path's 256-column tiles or a
+// persistent run's tiles), then the run's barrier words
+static size_t draft_part_bytes(int R, int V)
 {
     const size_t n_vt = (size_t)((V + kVocabTile - 1) / kVocabTile);
-    return (size_t)R * n_vt * sizeof(Part);
+    const size_t n_run = std::min<size_t>((size_t)((V + 31) / 32), (size_t)kRunTilesMax);
+    const size_t b = (size_t)R * std::max(n_vt, n_run) * sizeof(Part);
+    return (b + 255) / 256 * 256;
 }
+
+size_t draft_workspace_bytes(int R, int V) { return draft_part_bytes(R, V) + kRunCtlBytes; }
 
 // requests per workgroup of a bias pass: whole 64-request blocks, split into
 // balanced chunks so the grid has about 2048 workgroups
@@ -179,17 +192,141 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// persistent path
+// ---------------------------------------------------------------------------
+static std::atomic<int> g_draft_path{kDraftPathAuto};
+
+void set_draft_path(int path) { g_draft_path.store(path, std::memory_order_relaxed); }
+
+namespace {
+
+struct DevInfo {
+    int ncu, coop;
+};
+
+// compute units and cooperative-launch support of the current device (cached)
+DevInfo device_info()
+{
+    constexpr int kDevs = 64;
+    static std::atomic<int> ncu[kDevs], coop[kDevs], known[kDevs];
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) return DevInfo{0, 0};
+    if (d >= 0 && d < kDevs && known[d].load(std::memory_order_acquire))
+        return DevInfo{ncu[d].load(std::memory_order_relaxed), coop[d].load(std::memory_order_relaxed)};
+    int n = 0, c = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) n = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeCooperativeLaunch, d) != hipSuccess) c = 0;
+    if (d >= 0 && d < kDevs) {
+        ncu[d].store(n, std::memory_order_relaxed);
+        coop[d].store(c, std::memory_order_relaxed);
+        known[d].store(1, std::memory_order_release);
+    }
+    return DevInfo{n, c};
+}
+
+// the fewest 32-column units per wave for which the tiles (four per
+// workgroup, one workgroup per CU) cover V; 0 when none does
+int run_units(int V, int ncu, int* n_t)
+{
+    for (int tu = 1; tu <= kRunUnitsMax; ++tu) {
+        const int nt = (V + 32 * tu - 1) / (32 * tu);
+        if (nt <= kRunTilesMax && (nt + 3) / 4 <= ncu) {
+            *n_t = nt;
+            return tu;
+        }
+    }
+    return 0;
+}
+
+template <bool GREEDY, int TU>
+hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, hipStream_t s, bool* launched)
+{
+    *launched = false;
+    static std::atomic<int> occ{-1};
+    if (occ.load(std::memory_order_relaxed) < 0) {
+        int o = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, draft_run_kernel<GREEDY, TU>, 256, 0) !=
+            hipSuccess)
+            o = 0;
+        occ.store(o, std::memory_order_relaxed);
+    }
+    if (G > occ.load(std::memory_order_relaxed) * ncu) return hipSuccess;
+    const int64_t n_slots = 2 * (int64_t)ra.R * ra.n_t;
+    const int64_t n_clear = std::max<int64_t>(n_slots, (int64_t)ra.R * ra.n_steps);
+    const int cg = (int)std::min<int64_t>(1024, (n_clear + 255) / 256);
+    hipLaunchKernelGGL(run_clear_kernel, dim3(cg), dim3(256), 0, s, ra.slots, n_slots, ra.tok, ra.R,
+                       ra.gamma, ra.k0, ra.n_steps, ra.ctl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    RunArgs arg = ra;
+    void* args[] = {&arg};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&draft_run_kernel<GREEDY, TU>),
+                                   dim3(G), dim3(256), args, 0, s);
+    if (e == hipSuccess) *launched = true;
+    return e;
+}
+
+// one persistent launch for every position, when the shapes and the device allow
+hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
+                          const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
+                          int gamma, int V, int r, int k0, int n_steps, float temperature,
+                          uint64_t seed, uint32_t round, void* ws, hipStream_t s, bool* launched)
+{
+    *launched = false;
+    if (!rows_vec(bs, V, 8) || R > kRunReqMax) return hipSuccess;
+    const DevInfo di = device_info();
+    int n_t = 0;
+    const int tu = run_units(V, di.ncu, &n_t);
+    if (!di.coop || tu == 0) return hipSuccess;
+    const bool greedy = (temperature == 0.0f);
+    RunArgs ra{};
+    ra.base = base; ra.bs = bs; ra.E = E; ra.W2 = W2; ra.anchor = anchor; ra.tok = tok; ra.q = q;
+    ra.stats = stats; ra.R = R; ra.gamma = gamma; ra.V = V; ra.r = r; ra.k0 = k0;
+    ra.n_steps = n_steps; ra.inv_temp = greedy ? 1.0f : 1.0f / temperature; ra.seed = seed;
+    ra.round = round; ra.n_t = n_t;
+    ra.slots = static_cast<uint64_t*>(ws);
+    ra.ctl = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + draft_part_bytes(R, V));
+    const int G = (n_t + 3) / 4;
+#define DSP_RUN(TU)                                                                            \
+    return greedy ? launch_run_t<true, TU>(ra, G, di.ncu, s, launched)                         \
+                  : launch_run_t<false, TU>(ra, G, di.ncu, s, launched)
+    switch (tu) {
+    case 1: DSP_RUN(1);
+    case 2: DSP_RUN(2);
+    case 3: DSP_RUN(3);
+    case 4: DSP_RUN(4);
+    default: DSP_RUN(5);
+    }
+#undef DSP_RUN
+}
+
+}  // namespace
+
 hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
-                             int gamma, int V, int r, int k, float temperature, uint64_t seed,
-                             uint32_t round, void* ws, hipStream_t s)
+                             int gamma, int V, int r, int k, int n_steps, float temperature,
+                             uint64_t seed, uint32_t round, void* ws, hipStream_t s)
 {
-    if (bf16)
-        return launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats, R,
-                              gamma, V, r, k, temperature, seed, round, ws, s);
-    return launch_draft_t(static_cast<const float*>(base), bs, E, W2, anchor, tok, q, stats, R, gamma,
-                          V, r, k, temperature, seed, round, ws, s);
+    const int path = g_draft_path.load(std::memory_order_relaxed);
+    if (path != kDraftPathStream && bf16) {
+        bool launched = false;
+        const hipError_t e = try_launch_run(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok,
+                                            q, stats, R, gamma, V, r, k, n_steps, temperature, seed,
+                                            round, ws, s, &launched);
+        if (launched || e != hipSuccess) return e;
+    }
+    if (path == kDraftPathPersistent) return hipErrorNotSupported;
+    for (int i = 0; i < n_steps; ++i) {
+        const hipError_t e =
+            bf16 ? launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,
+                                  R, gamma, V, r, k + i, temperature, seed, round, ws, s)
+                 : launch_draft_t(static_cast<const float*>(base), bs, E, W2, anchor, tok, q, stats,
+                                  R, gamma, V, r, k + i, temperature, seed, round, ws, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace dsp

@@ -1,0 +1,542 @@
+// draft_run.h -- every draft position of a call in one persistent launch (gfx950).
+//
+// The Markov head makes draft position k depend on the token sampled at k - 1,
+// so the positions of a round run in sequence, and each one needs the bias
+// E[x_{k-1}] . W2^T over the whole vocabulary.  Re-reading W2 (V x r bf16) for
+// every position dominates the traffic of a small batch, so this kernel reads it
+// once per call: one workgroup per CU (co-resident by a cooperative launch), each
+// holding its slice of W2 on chip -- three 32-column units per wave in VGPRs as
+// MFMA fragments and up to two in LDS.  Per position:
+//   phase 1 (every workgroup): the previous tokens of all requests, then per
+//     32-request block the bias by MFMA from the resident slice plus the base
+//     logits, reduced to one partial per (request, tile) and published;
+//   phase 2 (workgroup n mod G for request n): wait for the request's partials,
+//     combine them, draw u, locate the tile, rebuild its logits with the same
+//     MFMA sequence and scan them (the steps of draft_pick_kernel), publish the
+//     token.
+// There is no grid-wide barrier: the published values themselves are the
+// signals.  Partial slots (double-buffered by position parity) and the tokens
+// of the call's positions hold "empty" markers before they are written (a clear
+// kernel sets them before the launch; a pick re-marks its request's slots for
+// two positions later), and readers poll until the marker is gone.  A pick
+// publishes its token only after its earlier stores -- those re-marks included
+// -- are complete, and a writer reads the tokens before it writes the next
+// partials, so a slot is never re-marked after its new value lands.
+//
+// DSpark pages: the sequential head adds a bias from the previous token before
+// each sample (page "DSpark.让每一轮计算，多走几步", Markov-head paragraph); it is
+// a low-rank matrix (page "DeepSeek联合北大最新文章DSpark", two-stage design).
+//
+// Values exchanged between workgroups are written and read with device-scope
+// relaxed atomics, which gfx950 performs coherently across its XCDs (no L2
+// writeback or invalidate is needed).  Every wait is bounded: one that exceeds
+// the limit sets the error word, and every later wait then returns at once, so
+// the grid always drains (a co-resident launch never gets there).
+#pragma once
+
+#include "tile_pass.h"
+
+namespace dsp {
+
+constexpr int kRunUnitsMax = 5;      // 32-column units per wave (one tile per wave)
+constexpr int kRunRegUnits = 3;      // units held in VGPRs; the rest in LDS
+constexpr int kRunTilesMax = 1024;   // tiles of one launch (four per workgroup)
+constexpr int kRunReqMax = 2048;     // requests of one launch (their tokens sit in LDS)
+constexpr unsigned kRunSpinLimit = 1u << 22;
+constexpr uint64_t kRunSlotEmpty = ~0ull;          // a partial slot not yet written
+constexpr int32_t kRunTokEmpty = (int32_t)0x80000000u;   // a token not yet drawn
+
+struct RunArgs {
+    const uint16_t* base;    // bf16 base logits, rows 16-byte aligned
+    RowStrides bs;
+    const uint16_t* E;       // [V, r]
+    const uint16_t* W2;      // [V, r]
+    const int32_t* anchor;   // [R]
+    int32_t* tok;            // [R, gamma]
+    float* q;                // [R, gamma]
+    double* stats;           // [R, gamma, 2]
+    int R, gamma, V, r, k0, n_steps;
+    float inv_temp;
+    uint64_t seed;
+    uint32_t round;
+    int n_t;                 // tiles of 32 * TU columns
+    uint64_t* slots;         // [2][R][n_t] partials: (max, sum) or (max, index)
+    unsigned* ctl;           // [0] error word
+};
+
+// MFMA row i of a 32-column unit -> column of the unit.  With this placement,
+// lane half h holds columns [8 h, 8 h + 8) in accumulator registers 0..7 and
+// [16 + 8 h, 16 + 8 h + 8) in registers 8..15, so the two 8-column words of a
+// request that a lane pair loads are 32 contiguous bytes.
+__host__ __device__ inline int unit_row_col(int i)
+{
+    const int h = (i >> 2) & 1, j = 4 * (i >> 3) + (i & 3);
+    return 8 * h + (j & 7) + 16 * (j >> 3);
+}
+
+// column of accumulator register j of lane half h
+__host__ __device__ inline int unit_acc_col(int h, int j) { return 8 * h + (j & 7) + 16 * (j >> 3); }
+
+// ---------------------------------------------------------------------------
+// coherent exchange between the workgroups of one launch
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dev_store_i32(int32_t* p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int32_t dev_load_i32(const int32_t* p)
+{
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void dev_store_u64(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t dev_load_u64(const uint64_t* p)
+{
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// every store this wave issued has completed (is visible to coherent loads)
+__device__ __forceinline__ void stores_done() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// a wait gave up (or another one did): record it; true when waiting should stop
+__device__ __forceinline__ bool run_give_up(unsigned* ctl, unsigned spins)
+{
+    if (spins > kRunSpinLimit) {
+        __hip_atomic_store(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
+    return __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
+__device__ __forceinline__ int32_t poll_tok(const int32_t* p, unsigned* ctl)
+{
+    int32_t v = dev_load_i32(p);
+    for (unsigned spins = 1; v == kRunTokEmpty; ++spins) {
+        __builtin_amdgcn_s_sleep(2);
+        if ((spins & 127u) == 0u && run_give_up(ctl, spins)) break;
+        v = dev_load_i32(p);
+    }
+    return v;
+}
+
+// partial slot words
+__device__ __forceinline__ uint64_t pack2(float m, uint32_t x) { return (uint64_t)__float_as_uint(m) | ((uint64_t)x << 32); }
+__device__ __forceinline__ float slot_m(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ uint32_t slot_x(uint64_t w) { return (uint32_t)(w >> 32); }
+
+template <int NL>
+struct RunLds {
+    uint4 w2[4][NL > 0 ? NL : 1][32][kRankMax / 8];   // LDS-resident units (first: staging)
+    uint16_t e[kPassBlock][kRankMax + kERowPad];       // embedding rows of a request block
+    uint16_t e_row[kRankMax];                          // the picked request's embedding row
+    int32_t tokl[kRunReqMax];                          // previous tokens of every request
+    PickScratch sh;
+};
+
+// Marks every partial slot of a launch and the tokens of its positions empty,
+// and clears the error word.
+__global__ void run_clear_kernel(uint64_t* slots, int64_t n_slots, int32_t* tok, int R, int gamma,
+                                 int k0, int n_steps, unsigned* ctl)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < n_slots; i += stride) slots[i] = kRunSlotEmpty;
+    const int64_t n_tok = (int64_t)R * n_steps;
+    for (int64_t i = i0; i < n_tok; i += stride)
+        tok[(i / n_steps) * gamma + k0 + (i % n_steps)] = kRunTokEmpty;
+    if (i0 == 0) ctl[0] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// draft_run_kernel: grid ceil(n_t / 4) (at most one workgroup per CU), 256
+// threads; wave w owns tile 4 blockIdx.x + w, i.e. the 32 TU columns from
+// 32 TU (4 blockIdx.x + w).  Lane l holds request l % 32 of a 32-request block.
+// ---------------------------------------------------------------------------
+template <bool GREEDY, int TU>
+__global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
+{
+    constexpr int NR = TU < kRunRegUnits ? TU : kRunRegUnits;
+    constexpr int NL = TU - NR;
+    constexpr int kWordsRow = kRankMax / 8;   // 16-byte words of a staged W2 row
+    __shared__ RunLds<NL> L;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int h = lane >> 5, c32 = lane & 31;
+    const int V = a.V, r = a.r, R = a.R, gamma = a.gamma, n_t = a.n_t;
+    const int G = gridDim.x;
+    const int tw = 4 * (int)blockIdx.x + wave;
+    const int v_tile = tw * 32 * TU;
+    const float itL = fold_itl(a.inv_temp);
+    const int prow = unit_row_col(c32);   // unit row of this lane's A fragments
+
+    // ---- the wave's W2 units: each read contiguously (an instruction covers
+    // two whole rows) into the wave's first LDS slot, then into fragments; the
+    // LDS-resident units are written straight to their slots
+    bf16x8 afrag[NR][kKSteps];
+    {
+        uint4 cur[16], nxt[16];
+        auto fetch = [&](int u, uint4* w) {
+            const int v0 = v_tile + 32 * u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int f = i * 64 + lane, rho = f / kWordsRow, c = f % kWordsRow;
+                const int v = v0 + rho;
+                w[i] = (v < V && 8 * c < r)
+                           ? *reinterpret_cast<const uint4*>(a.W2 + (int64_t)v * r + 8 * c)
+                           : make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto put = [&](int slot, const uint4* w) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int f = i * 64 + lane, rho = f / kWordsRow, c = f % kWordsRow;
+                L.w2[wave][slot][rho][w2_slot(rho, c)] = w[i];
+            }
+        };
+        fetch(0, cur);
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+            if (u + 1 < TU) fetch(u + 1, nxt);
+            if (u < NR) {
+                put(0, cur);
+                lds_barrier();
+#pragma unroll
+                for (int ks = 0; ks < kKSteps; ++ks)
+                    afrag[u < NR ? u : 0][ks] =
+                        as_bf16x8(L.w2[wave][0][prow][w2_slot(prow, 2 * ks + h)]);
+                lds_barrier();
+            } else {
+                put(u - NR, cur);
+            }
+            if (u + 1 < TU) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
+            }
+        }
+        lds_barrier();
+    }
+
+    const int srow = tid & 31, sq = tid >> 5;   // embedding staging: row, word group
+    const int RB = (R + kPassBlock - 1) / kPassBlock;
+    for (int s = 0; s < a.n_steps; ++s) {
+        const int k = a.k0 + s;
+        uint64_t* slots = a.slots + (int64_t)(k & 1) * R * n_t;
+
+        // ---- the previous token of every request (drawn in this launch: wait
+        // for it; the anchor or an earlier call's token: read it)
+        lds_barrier();   // the previous position's readers of tokl are done
+        for (int n = tid; n < R; n += 256) {
+            int t;
+            if (k == 0) t = a.anchor[n];
+            else if (s == 0) t = a.tok[(int64_t)n * gamma + k - 1];
+            else t = poll_tok(a.tok + (int64_t)n * gamma + k - 1, a.ctl);
+            L.tokl[n] = t;
+        }
+        lds_barrier();
+
+        // ================= phase 1: partials of every (request, tile) =========
+        uint4 eu[4];
+        auto load_e = [&](int n0) {
+            const int ne = n0 + srow;
+            const int p = (ne < R) ? L.tokl[ne] : -1;
+            const bool pok = p >= 0 && p < V;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int kk = (sq * 4 + c) * 8;
+                eu[c] = (pok && kk < r) ? *reinterpret_cast<const uint4*>(a.E + (int64_t)p * r + kk)
+                                        : make_uint4(0, 0, 0, 0);
+            }
+        };
+        // base words of this lane's request: its two 8-column words of each unit
+        constexpr int RING = (TU >= 4) ? 1 : 2;
+        uint4 bw[RING][TU][2];
+        auto load_base = [&](int n0, auto SL) {
+            constexpr int sl = decltype(SL)::value % RING;
+            const int n = n0 + c32;
+            const bool nok = n < R;
+            const uint16_t* row = a.base + (int64_t)(nok ? n : 0) * a.bs.rs + (int64_t)k * a.bs.ps;
+#pragma unroll
+            for (int u = 0; u < TU; ++u)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
+                    load8_any<uint16_t, true>(row, v0, V, nok, v0 + 8 <= V, &bw[sl][u][c]);
+                }
+        };
+        load_e(0);
+        load_base(0, std::integral_constant<int, 0>{});
+
+        // one request block; SL (block parity) is the base-word ring slot
+        auto block = [&](int b, auto SL) {
+            constexpr int sl = decltype(SL)::value % RING;
+            const int n0 = b * kPassBlock;
+            lds_barrier();   // the previous block's embedding tile is read
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                *reinterpret_cast<uint4*>(&L.e[srow][(sq * 4 + c) * 8]) = eu[c];
+            lds_barrier();
+            if (b + 1 < RB) {   // the next block's rows, under this block's MFMAs
+                load_e(n0 + kPassBlock);
+                if constexpr (RING == 2) load_base(n0 + kPassBlock, std::integral_constant<int, sl ^ 1>{});
+            }
+
+            // units in two groups (registers, then LDS), each reduced on its own
+            // and the two partials merged: fewer accumulators live at once
+            float gm[2] = {-INFINITY, -INFINITY};
+            double gs[2] = {0.0, 0.0};
+            int gi[2] = {0x7fffffff, 0x7fffffff};
+            auto group = [&](auto U0, auto U1) {
+                constexpr int u0 = decltype(U0)::value, u1 = decltype(U1)::value, nu = u1 - u0;
+                constexpr int gidx = u0 == 0 ? 0 : 1;
+                floatx16 acc[nu];
+#pragma unroll
+                for (int u = 0; u < nu; ++u)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) acc[u][j] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < kKSteps; ++ks) {
+                    const bf16x8 bv =
+                        as_bf16x8(*reinterpret_cast<const uint4*>(&L.e[c32][ks * kKStep + 8 * h]));
+#pragma unroll
+                    for (int u = 0; u < nu; ++u) {
+                        const int uu = u0 + u;
+                        const bf16x8 av = (u0 < NR) ? afrag[uu < NR ? uu : 0][ks]
+                                                    : as_bf16x8(L.w2[wave][uu >= NR ? uu - NR : 0][prow]
+                                                                     [w2_slot(prow, 2 * ks + h)]);
+                        acc[u] = mfma32_bf16(av, bv, acc[u]);
+                    }
+                }
+                // logits of the group's columns for this lane's request
+#pragma unroll
+                for (int u = 0; u < nu; ++u)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        acc[u][j] = Logit<uint16_t>::raw_at(&bw[sl][u0 + u][j >> 3], j & 7) + acc[u][j];
+                float m = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < nu; ++u)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) m = fmaxf(m, acc[u][j]);
+                if constexpr (GREEDY) {
+                    // the lowest column holding the lane maximum (columns grow
+                    // with u, then j); masked columns hold -inf and come last
+                    int best = 0x7fffffff;
+#pragma unroll
+                    for (int u = nu - 1; u >= 0; --u)
+#pragma unroll
+                        for (int j = 15; j >= 0; --j)
+                            best = (acc[u][j] == m) ? 32 * u + unit_acc_col(h, j) : best;
+                    best = (best == 0x7fffffff) ? best : v_tile + 32 * u0 + best;
+                    gm[gidx] = m;
+                    gi[gidx] = best < V ? best : 0x7fffffff;
+                } else {
+                    m = xmax<32>(m);
+                    const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked group
+                    // per unit a pairwise fp32 tree over the lane's 16 weights,
+                    // then fp64 across units and the lane pair
+                    double sd = 0.0;
+#pragma unroll
+                    for (int u = 0; u < nu; ++u) {
+                        float w[16];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) w[j] = wexp(acc[u][j] - mref, itL);
+#pragma unroll
+                        for (int hw = 8; hw >= 1; hw >>= 1)
+#pragma unroll
+                            for (int j = 0; j < hw; ++j) w[j] = w[j] + w[j + hw];
+                        sd += (double)w[0];
+                    }
+                    gm[gidx] = m;
+                    gs[gidx] = xsum<32>(sd);
+                }
+            };
+            group(std::integral_constant<int, 0>{}, std::integral_constant<int, NR>{});
+            if constexpr (NL > 0) group(std::integral_constant<int, NR>{}, std::integral_constant<int, TU>{});
+
+            uint64_t word;
+            if constexpr (GREEDY) {
+                ArgMax am{gm[0], gi[0]};
+                if constexpr (NL > 0) am = argmax_merge(am, ArgMax{gm[1], gi[1]});
+                am = xargmax<32>(am);
+                word = pack2(am.v, (uint32_t)am.i);
+            } else {
+                float m = gm[0];
+                double sum = gs[0];
+                if constexpr (NL > 0) {
+                    const float mm = fmaxf(gm[0], gm[1]);
+                    if (mm != -INFINITY)
+                        sum = gs[0] * (double)wexp(gm[0] - mm, itL) + gs[1] * (double)wexp(gm[1] - mm, itL);
+                    m = mm;
+                }
+                word = pack2(m, __float_as_uint((float)sum));
+            }
+            const int n = n0 + c32;
+            if (h == 0 && n < R && tw < n_t) dev_store_u64(slots + (int64_t)n * n_t + tw, word);
+            if constexpr (RING == 1) {
+                if (b + 1 < RB) load_base(n0 + kPassBlock, std::integral_constant<int, 0>{});
+            }
+        };
+        for (int b = 0; b < RB; b += 2) {
+            block(b, std::integral_constant<int, 0>{});
+            if (b + 1 < RB) block(b + 1, std::integral_constant<int, 1>{});
+        }
+
+        // ================= phase 2: one workgroup per request ==================
+        for (int n = blockIdx.x; n < R; n += G) {
+            const int64_t out = (int64_t)n * gamma + k;
+            uint64_t* ps = slots + (int64_t)n * n_t;
+            constexpr int PER = kRunTilesMax / 256;
+            // the request's partials: wait until every tile's has landed
+            uint64_t wv[PER];
+            {
+                bool miss = false;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int t = tid * PER + i;
+                    wv[i] = (t < n_t) ? dev_load_u64(ps + t) : 0ull;
+                    miss |= (wv[i] == kRunSlotEmpty);
+                }
+                for (unsigned spins = 1; miss; ++spins) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if ((spins & 127u) == 0u && run_give_up(a.ctl, spins)) break;
+                    miss = false;
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) {
+                        const int t = tid * PER + i;
+                        if (wv[i] == kRunSlotEmpty) wv[i] = dev_load_u64(ps + t);
+                        miss |= (wv[i] == kRunSlotEmpty);
+                    }
+                }
+            }
+            int tok_out = 0, tok_thread = 0;
+            float q_out = 1.0f;
+            double st0 = 0.0, st1 = 0.0;
+            if constexpr (GREEDY) {
+                ArgMax am{-INFINITY, 0x7fffffff};
+#pragma unroll
+                for (int i = 0; i < PER; ++i)
+                    if (tid * PER + i < n_t) am = argmax_merge(am, ArgMax{slot_m(wv[i]), (int)slot_x(wv[i])});
+                am = wave_argmax(am);
+                if (lane == 0) {
+                    L.sh.wmax[wave] = am.v;
+                    L.sh.hit[0][wave] = am.i;
+                }
+                lds_barrier();
+                ArgMax b{L.sh.wmax[0], L.sh.hit[0][0]};
+#pragma unroll
+                for (int w = 1; w < 4; ++w) b = argmax_merge(b, ArgMax{L.sh.wmax[w], L.sh.hit[0][w]});
+                tok_out = b.i;
+                st0 = b.v;
+            } else {
+                float mt[PER];
+                double sw[PER];
+                float M = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const bool in = tid * PER + i < n_t;
+                    mt[i] = in ? slot_m(wv[i]) : -INFINITY;
+                    sw[i] = in ? (double)__uint_as_float(slot_x(wv[i])) : 0.0;
+                    M = fmaxf(M, mt[i]);
+                }
+                M = block_max256(M, L.sh);
+                double ls = 0.0;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    sw[i] = (mt[i] == -INFINITY)
+                                ? 0.0
+                                : sw[i] * exp(((double)mt[i] - (double)M) * (double)a.inv_temp);
+                    ls += sw[i];
+                }
+                const double Z = block_sum256(ls, L.sh);
+                const double u = uniform24(a.seed, a.round, (uint32_t)n, (uint32_t)k, 0u);
+                const double target = u * Z;
+                double before;
+                const int tsel = block_locate<PER>(sw, target, &before, L.sh, 0);
+
+                // rebuild the tile's 32 TU logits (thread t: column vt0 + t); the
+                // embedding row, the base logit and this wave's W2 fragments
+                // (units w and w + 4) are requested together
+                const int vt0 = tsel * 32 * TU;
+                const int pv = L.tokl[n];
+                const bool pok = pv >= 0 && pv < V;
+                uint4 ev = make_uint4(0, 0, 0, 0);
+                if (tid < kRankMax / 8 && pok && 8 * tid < r)
+                    ev = *reinterpret_cast<const uint4*>(a.E + (int64_t)pv * r + 8 * tid);
+                const uint16_t* row = a.base + (int64_t)n * a.bs.rs + (int64_t)k * a.bs.ps;
+                const int v = vt0 + tid;
+                const bool vin = tid < 32 * TU && v < V;
+                const float xb = vin ? Logit<uint16_t>::at(row, v) : -INFINITY;
+                constexpr int NU = (TU + 3) / 4;   // units per wave in a rebuild
+                uint4 af[NU][kKSteps];
+#pragma unroll
+                for (int j = 0; j < NU; ++j) {
+                    const int vr = vt0 + 32 * (wave + 4 * j) + prow;
+                    const bool uin = wave + 4 * j < TU && vr < V;
+#pragma unroll
+                    for (int ks = 0; ks < kKSteps; ++ks) {
+                        const int kk = ks * kKStep + 8 * h;
+                        af[j][ks] = (uin && kk < r)
+                                        ? *reinterpret_cast<const uint4*>(a.W2 + (int64_t)vr * r + kk)
+                                        : make_uint4(0, 0, 0, 0);
+                    }
+                }
+                if (tid < kRankMax / 8) *reinterpret_cast<uint4*>(L.e_row + 8 * tid) = ev;
+                lds_barrier();
+#pragma unroll
+                for (int j = 0; j < NU; ++j) {
+                    const int uu = wave + 4 * j;
+                    if (uu < TU) {
+                        floatx16 acc;
+#pragma unroll
+                        for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.0f;
+#pragma unroll
+                        for (int ks = 0; ks < kKSteps; ++ks) {
+                            uint4 bu = make_uint4(0, 0, 0, 0);
+                            if (c32 == 0) bu = *reinterpret_cast<const uint4*>(L.e_row + ks * kKStep + 8 * h);
+                            acc = mfma32_bf16(as_bf16x8(af[j][ks]), as_bf16x8(bu), acc);
+                        }
+                        if (c32 == 0) {
+#pragma unroll
+                            for (int jj = 0; jj < 16; ++jj) L.sh.lg[32 * uu + unit_acc_col(h, jj)] = acc[jj];
+                        }
+                    }
+                }
+                lds_barrier();
+                const float z = vin ? xb + L.sh.lg[tid] : -INFINITY;
+                double e1[1] = {vin ? (double)wexp(z - M, itL) : 0.0};
+                double b2;
+                const int loc = block_locate<1>(e1, target - before, &b2, L.sh, 1);
+                tok_out = vt0 + loc;
+                tok_thread = loc;
+                q_out = (float)(e1[0] / Z);
+                st0 = M;
+                st1 = Z;
+            }
+            // publish: this workgroup's earlier stores (the slot re-marks of the
+            // previous position among them) complete first
+            stores_done();
+            lds_barrier();
+            if (tid == tok_thread) {
+                dev_store_i32(a.tok + out, tok_out);
+                a.q[out] = q_out;
+                a.stats[2 * out] = st0;
+                a.stats[2 * out + 1] = st1;
+            }
+            // re-mark the request's slots of this parity for position k + 2
+            if (s + 2 < a.n_steps) {
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int t = tid * PER + i;
+                    if (t < n_t) dev_store_u64(ps + t, kRunSlotEmpty);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace dsp

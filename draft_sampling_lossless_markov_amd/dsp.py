@@ -20,9 +20,10 @@ LIB_PATH = os.path.join(_PKG, "libdsp.so")
 DSP_OK, DSP_ERR_INVALID_ARG, DSP_ERR_UNSUPPORTED, DSP_ERR_WORKSPACE, DSP_ERR_HIP = range(5)
 DSP_F32, DSP_BF16 = 0, 1
 DSP_WS_DRAFT, DSP_WS_VERIFY = 0, 1
+DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING, DSP_DRAFT_PERSISTENT = 0, 1, 2
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
-            "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
+            "dsp_set_draft_path", "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
 
 _lib = None
 
@@ -57,8 +58,10 @@ def lib():
     L.dsp_workspace_size.argtypes = [I, I, I, I, I]
     L.dsp_workspace_size.restype = SZ
     I64 = C.c_int64
-    L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, F, U64, U32, P,
-                                 SZ, P]
+    L.dsp_set_draft_path.argtypes = [I]
+    L.dsp_set_draft_path.restype = I
+    L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, I, F, U64, U32,
+                                 P, SZ, P]
     L.dsp_confidence.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
     L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
@@ -103,15 +106,22 @@ def dsp_workspace_size(which: int, R: int, gamma: int, V: int, r: int) -> int:
     return int(lib().dsp_workspace_size(which, R, gamma, V, r))
 
 
+def dsp_set_draft_path(path):
+    """Process-wide dsp_draft_step implementation: DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING
+    or DSP_DRAFT_PERSISTENT."""
+    _check(lib().dsp_set_draft_path(int(path)))
+
+
 def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_, ws,
-                   stream=None):
+                   stream=None, n_steps=1):
+    """Draft positions k .. k + n_steps - 1 of every request."""
     R, gamma, V = base.shape
     r = E.shape[1]
     rs, ps = _rows(base, "base")
     _check(lib().dsp_draft_step(_ptr(base), _dtype(base), rs, ps, _ptr(E), _ptr(W2), _ptr(anchor),
                                 _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V, r, int(k),
-                                float(temperature), int(seed), int(round_), _ptr(ws),
-                                ws.numel() * ws.element_size(), _stream(stream)))
+                                int(n_steps), float(temperature), int(seed), int(round_),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dsp_confidence(h, E, anchor, tok, w, T, offset, c, stream=None):

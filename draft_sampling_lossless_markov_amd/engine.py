@@ -33,9 +33,9 @@ class Round:
                                      dtype=torch.uint8, device=dev)
 
     def draft(self, inp, temperature, seed, rnd, stream=None):
-        for k in range(self.gamma):
-            dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok, self.q,
-                               self.stats, k, temperature, seed, rnd, self.ws_draft, stream)
+        dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok, self.q,
+                           self.stats, 0, temperature, seed, rnd, self.ws_draft, stream,
+                           n_steps=self.gamma)
 
     def confidence(self, inp, stream=None):
         dsp.dsp_confidence(inp["h"], inp["E"], inp["anchor"], self.tok, inp["w"], inp["T"],

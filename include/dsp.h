@@ -3,7 +3,7 @@
  * confidence-scheduled speculative decoding on AMD Instinct MI355X (gfx950).
  *
  * One decode round is
- *     for k in 0..gamma-1: dsp_draft_step(k)      semi-autoregressive draft
+ *     dsp_draft_step(k = 0, n_steps = gamma)       semi-autoregressive draft
  *     dsp_confidence                               confidence head + STS
  *     dsp_schedule                                 hardware-aware prefix scheduler
  *     dsp_verify                                   lossless verification
@@ -45,7 +45,8 @@
  * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
  * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
  *
- * ABI version 200: base and target take element strides.
+ * ABI version 300: dsp_draft_step draws n_steps consecutive positions per call;
+ * dsp_set_draft_path selects its implementation.  (200: element strides.)
  */
 #ifndef DSP_H
 #define DSP_H
@@ -83,7 +84,8 @@ int dsp_version(void);
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
 
 /*
- * dsp_draft_step -- one draft position k for all R requests.
+ * dsp_draft_step -- draft positions k, k+1, ..., k+n_steps-1 for all R requests,
+ * in that order (each position's previous token is the one drawn before it).
  *
  * Semi-autoregressive draft with the Markov head (DSpark paper summaries: page
  * "DeepSeek联合北大最新文章DSpark", two-stage design, sequential head: the
@@ -103,21 +105,40 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  *
  * base   logits (n, k, v) at base[n * base_rs + k * base_ps + v], fp32 or bf16
  *        (dtype): the draft base logits of the backbone, R x gamma rows of V;
- *        only position k is read
+ *        positions k .. k+n_steps-1 are read
  * E      [V, r] bf16   Markov embedding; row x is the embedding of token x
  * W2     [V, r] bf16   low-rank output factor stored transposed: W2[v, i] is
  *                      element (i, v) of the r x V matrix
  * anchor [R]  int32    the token the target emitted last (x_{-1})
- * tok    [R, gamma] int32   column k written, column k-1 read (k >= 1)
- * q      [R, gamma] f32     column k written
- * stats  [R, gamma, 2] f64  column k written
+ * tok    [R, gamma] int32   columns k .. k+n_steps-1 written, column k-1 read (k >= 1)
+ * q      [R, gamma] f32     columns k .. k+n_steps-1 written
+ * stats  [R, gamma, 2] f64  columns k .. k+n_steps-1 written
+ * k, n_steps   0 <= k, 1 <= n_steps, k + n_steps <= gamma
  * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
+ *
+ * Implementation (results do not depend on it): with bf16 logits in 16-byte
+ * rows and a vocabulary whose W2 slice fits on chip (V <= 163840 for r <= 256 on
+ * 256 CUs), one persistent cooperative launch runs every position with W2 read
+ * once; otherwise each position is two streaming launches that read W2 again.
  */
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
                           const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
-                          double* stats, int R, int gamma, int V, int r, int k,
+                          double* stats, int R, int gamma, int V, int r, int k, int n_steps,
                           float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * dsp_set_draft_path -- process-wide choice of the dsp_draft_step implementation:
+ *   DSP_DRAFT_AUTO        persistent launch where it applies, streaming elsewhere
+ *   DSP_DRAFT_STREAMING   two launches per position always (for callers that
+ *                         share the GPU with work that must not wait behind a
+ *                         launch occupying every CU)
+ *   DSP_DRAFT_PERSISTENT  persistent launch only; calls it cannot serve return
+ *                         DSP_ERR_HIP (hipErrorNotSupported)
+ * Returns DSP_ERR_INVALID_ARG for any other value.  Takes effect on later calls.
+ */
+typedef enum { DSP_DRAFT_AUTO = 0, DSP_DRAFT_STREAMING = 1, DSP_DRAFT_PERSISTENT = 2 } dsp_draft_path;
+dsp_status dsp_set_draft_path(int path);
 
 /*
  * dsp_confidence -- confidence head with sequential temperature scaling.

@@ -41,14 +41,17 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings_and_version(L):
     assert L.dsp_status_string(0) == b"DSP_OK"
     assert L.dsp_status_string(3) == b"DSP_ERR_WORKSPACE"
-    assert L.dsp_version() == 200
+    assert L.dsp_version() == 300
 
 
 def test_workspace_sizes(L):
     from draft_sampling_lossless_markov_amd import dsp
     assert dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 0, 4, 32, 8) == 0
     a = dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 64, 7, 151936, 256)
-    assert a == 64 * ((151936 + 255) // 256) * 16
+    # partials of the larger tiling (a persistent run's at most 1024 tiles per
+    # row), rounded to 256 bytes, then 256 bytes of barrier words
+    assert a == 64 * 1024 * 16 + 256
+    assert dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 3, 4, 32, 8) == 256 + 256
     b = dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, 64, 7, 151936, 256)
     assert b > 64 * 8 * 19 * 8
 
@@ -59,7 +62,7 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation returns first
 def _draft(L, **kw):
     a = dict(base=FAKE, dtype=1, base_rs=4 * 32, base_ps=32, E=FAKE, W2=FAKE, anchor=FAKE,
              tok=FAKE, q=FAKE, stats=FAKE,
-             R=4, gamma=4, V=32, r=8, k=0, temperature=1.0, seed=0, round=0, ws=FAKE,
+             R=4, gamma=4, V=32, r=8, k=0, n_steps=1, temperature=1.0, seed=0, round=0, ws=FAKE,
              ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return L.dsp_draft_step(*[C.c_void_p(v) if isinstance(v, int) and k in
@@ -74,6 +77,9 @@ def test_draft_validation(L):
     assert _draft(L, V=-1) == 1
     assert _draft(L, k=4) == 1
     assert _draft(L, k=-1) == 1
+    assert _draft(L, n_steps=0) == 1
+    assert _draft(L, k=1, n_steps=4) == 1
+    assert b"n_steps" in L.dsp_last_error()
     assert _draft(L, temperature=-0.5) == 1
     assert _draft(L, temperature=float("nan")) == 1
     assert _draft(L, gamma=65) == 2
@@ -86,6 +92,13 @@ def test_draft_validation(L):
     assert _draft(L, base_ps=-32) == 1
     assert _draft(L, base=FAKE + 4) == 1
     assert b"16-byte" in L.dsp_last_error()
+
+
+def test_draft_path_selection(L):
+    assert L.dsp_set_draft_path(3) == 1
+    assert L.dsp_set_draft_path(-1) == 1
+    for p in (1, 2, 0):
+        assert L.dsp_set_draft_path(p) == 0
 
 
 def test_schedule_validation(L):

@@ -141,6 +141,86 @@ def test_round_parity_layouts(case, layout):
     assert tot.mismatch_rate() <= 1e-4, tot.summary()
 
 
+# draft paths: the persistent launch (W2 slice resident on chip, all positions in
+# one cooperative launch) at every units-per-wave count (V sets it: 1 .. 5, the
+# last two with LDS-resident units), against the streaming launches and the oracle
+PATH_CASES = [
+    # (R, gamma, V, r, temperature)
+    (70, 5, 1000, 24, 0.7),       # 1 unit per wave, 8 workgroups, ragged request block
+    (70, 5, 1000, 24, 0.0),
+    (300, 3, 40000, 256, 0.9),    # 2 units, ten request blocks
+    (17, 3, 80000, 128, 1.0),     # 3 units (all in registers)
+    (17, 3, 100000, 200, 0.0),    # 4 units (one in LDS); r not a multiple of 16
+    (9, 4, 160000, 256, 1.0),     # 5 units (two in LDS), 250 workgroups
+    (9, 4, 160000, 256, 0.0),
+]
+
+
+@pytest.fixture
+def draft_path():
+    yield dsp.dsp_set_draft_path
+    dsp.dsp_set_draft_path(dsp.DSP_DRAFT_AUTO)
+
+
+def _draft_all(inp, rd, temp, rnd, per_position=False):
+    g = inp["gamma"]
+    if per_position:
+        for k in range(g):
+            dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
+                               rd.stats, k, temp, SEED, rnd, rd.ws_draft)
+    else:
+        dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
+                           rd.stats, 0, temp, SEED, rnd, rd.ws_draft, n_steps=g)
+    torch.cuda.synchronize()
+    return np_(rd.tok).copy(), np_(rd.q).copy(), np_(rd.stats).copy()
+
+
+@pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: f"R{c[0]}g{c[1]}V{c[2]}r{c[3]}T{c[4]}")
+def test_draft_paths_vs_oracle(case, draft_path):
+    R, gamma, V, r, temp = case
+    greedy = temp == 0.0
+    wl = custom(R, gamma, V, r, 8, torch.bfloat16)
+    for rnd in range(2):
+        _say(f"draft paths {case} round {rnd}")
+        inp_cpu = make_inputs(wl, rnd, layout="position")
+        inp = to_dev(inp_cpu)
+        rd = Round(R, gamma, V, r)
+        draft_path(dsp.DSP_DRAFT_PERSISTENT)          # raises if the launch does not apply
+        pers = _draft_all(inp, rd, temp, rnd)
+        split = _draft_all(inp, rd, temp, rnd, per_position=True)
+        for a, b in zip(pers, split):
+            assert np.array_equal(a, b)
+        draft_path(dsp.DSP_DRAFT_STREAMING)
+        strm = _draft_all(inp, rd, temp, rnd)
+        S = np.arange(R, dtype=np.int32)
+        o_tok, o_q, o_stats, o_flag = orc.draft(orc.host_logits(inp_cpu["base"]),
+                                                orc.bf16_bits(inp_cpu["E"]),
+                                                orc.bf16_bits(inp_cpu["W2"]),
+                                                np_(inp_cpu["anchor"]), S, temp, SEED, rnd)
+        for name, (tok, q, st) in (("persistent", pers), ("streaming", strm)):
+            t, _ = compare_draft(tok, q, st, o_tok, o_q, o_stats, o_flag, greedy, S)
+            assert t.ok(), (name, t.summary())
+            assert t.mismatch_rate() <= 1e-3, (name, t.summary())
+        if greedy:
+            assert np.array_equal(pers[0], strm[0])
+        del rd, inp
+    torch.cuda.empty_cache()
+
+
+def test_persistent_path_refuses_what_it_cannot_hold(draft_path):
+    """V beyond the on-chip capacity and fp32 logits: the persistent-only setting
+    reports an error; AUTO serves them with the streaming launches."""
+    for V, dt in ((300000, torch.bfloat16), (1000, torch.float32)):
+        wl = custom(4, 2, V, 16, 8, dt)
+        inp = to_dev(make_inputs(wl, 0))
+        rd = Round(4, 2, V, 16)
+        draft_path(dsp.DSP_DRAFT_PERSISTENT)
+        with pytest.raises(dsp.DspError):
+            _draft_all(inp, rd, 1.0, 0)
+        draft_path(dsp.DSP_DRAFT_AUTO)
+        _draft_all(inp, rd, 1.0, 0)
+
+
 def test_tiny_workload_1000_rounds():
     """The tiny workload: 1000 rounds with fresh inputs, greedy and sampling."""
     wl = WORKLOADS[0]

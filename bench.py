@@ -37,7 +37,7 @@ DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/csrc/draft.hip",
                  "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_device.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_launch.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_step_traffic_qwen3-4b-R64-g7-V151936.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_call_traffic_qwen3-4b-R64-g7-V151936.txt")
 METRIC = "verified draft positions/sec (draft+verify) and % of MI355X HBM roofline"
 UNIT = "verified draft positions/s"
 
@@ -66,16 +66,13 @@ def draft_call_bytes(inp):
 
 
 def probe_draft_path(call):
-    """'persistent' when the persistent draft launch serves this workload, else
-    'streaming' (the path AUTO selects); leaves the selection on AUTO."""
-    dsp.dsp_set_draft_path(dsp.DSP_DRAFT_PERSISTENT)
+    """'persistent' when the persistent draft launch serves this workload (what
+    DSP_DRAFT_AUTO then runs), else 'streaming'."""
     try:
-        call()
+        call(dsp.DSP_DRAFT_PERSISTENT)
         path = "persistent"
     except dsp.DspError:
         path = "streaming"
-    finally:
-        dsp.dsp_set_draft_path(dsp.DSP_DRAFT_AUTO)
     torch.cuda.synchronize()
     return path
 
@@ -183,10 +180,10 @@ def main():
     stream = torch.cuda.current_stream()
     seed = 0
 
-    def draft(i, s=stream):
+    def draft(i, s=stream, flags=dsp.DSP_DRAFT_AUTO):
         inp = sets[i % len(sets)]
         dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
-                           rd.stats, 0, temp, seed, i, rd.ws_draft, s, n_steps=g)
+                           rd.stats, 0, temp, seed, i, rd.ws_draft, s, n_steps=g, flags=flags)
 
     def one_round(i, ev=None, s=stream):
         inp = sets[i % len(sets)]
@@ -205,7 +202,7 @@ def main():
         if ev is not None:
             ev[4].record(s)
 
-    draft_path = probe_draft_path(lambda: draft(0))
+    draft_path = probe_draft_path(lambda f: draft(0, flags=f))
     log(f"draft path: {draft_path}")
 
     for i in range(args.warmup):
@@ -270,7 +267,28 @@ def main():
     A = round_bytes(wl, inp0, len_per_round, rej_per_round, greedy)
 
     call_bytes = draft_call_bytes(inp0)
-    draft_avg_s = float(draft_ms.mean()) * 1e-3
+    if args.eager:
+        draft_avg_s = float(draft_ms.mean()) * 1e-3
+        draft_timing = "eager launches, events around each call"
+    else:
+        # the draft call alone, replayed from a graph, events on the launch stream:
+        # its kernels back to back (what the kernel trace's durations add up to)
+        cap = torch.cuda.Stream()
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd, stream=cap):
+            draft(args.warmup, s=cap)
+        for _ in range(2):
+            gd.replay()
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(K):
+            gd.replay()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        draft_avg_s = d0.elapsed_time(d1) / K * 1e-3
+        draft_timing = "graph replays of the draft call alone"
     achieved = call_bytes / draft_avg_s / 1e9
     traffic = profiled_traffic(wl.name, draft_path)
     kernels = ("draft_run_kernel (one cooperative launch, all gamma positions)"
@@ -279,7 +297,8 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": f"dsp_draft_step, {g} positions: {kernels}",
-            "bytes_per_launch": int(call_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2)}
+            "bytes_per_launch": int(call_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2),
+            "timing": draft_timing}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": K,

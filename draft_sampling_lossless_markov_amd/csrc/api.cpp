@@ -88,17 +88,6 @@ const char* dsp_last_error(void) { return g_err; }
 
 int dsp_version(void) { return 300; }
 
-dsp_status dsp_set_draft_path(int path)
-{
-    if (path != DSP_DRAFT_AUTO && path != DSP_DRAFT_STREAMING && path != DSP_DRAFT_PERSISTENT)
-        return fail(DSP_ERR_INVALID_ARG, "dsp_set_draft_path: unknown path %d", path);
-    static_assert(DSP_DRAFT_AUTO == dsp::kDraftPathAuto && DSP_DRAFT_STREAMING == dsp::kDraftPathStream &&
-                      DSP_DRAFT_PERSISTENT == dsp::kDraftPathPersistent,
-                  "path codes");
-    dsp::set_draft_path(path);
-    return ok();
-}
-
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 {
     if (R <= 0 || gamma <= 0 || V <= 0 || r <= 0) return 0;
@@ -110,8 +99,8 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
                           const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
                           double* stats, int R, int gamma, int V, int r, int k, int n_steps,
-                          float temperature, uint64_t seed, uint32_t round, void* ws,
-                          size_t ws_bytes, void* stream)
+                          unsigned flags, float temperature, uint64_t seed, uint32_t round,
+                          void* ws, size_t ws_bytes, void* stream)
 {
     if (!base || !E || !W2 || !anchor || !tok || !q || !stats)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: null pointer argument");
@@ -121,6 +110,11 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
     if (st != DSP_OK) return st;
     if (k < 0 || k >= gamma)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: k = %d outside [0, gamma)", k);
+    static_assert(DSP_DRAFT_AUTO == dsp::kDraftPathAuto && DSP_DRAFT_STREAMING == dsp::kDraftPathStream &&
+                      DSP_DRAFT_PERSISTENT == dsp::kDraftPathPersistent,
+                  "path codes");
+    if (flags != DSP_DRAFT_AUTO && flags != DSP_DRAFT_STREAMING && flags != DSP_DRAFT_PERSISTENT)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: unknown flags %u", flags);
     if (n_steps < 1 || n_steps > gamma - k)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: n_steps = %d outside [1, gamma - k] (k = %d)",
                     n_steps, k);
@@ -136,7 +130,8 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                     ws_bytes, need);
     return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
                                              dtype == DSP_BF16, E, W2, anchor, tok, q,
-                                             stats, R, gamma, V, r, k, n_steps, temperature, seed, round,
+                                             stats, R, gamma, V, r, k, n_steps, (int)flags, temperature,
+                                             seed, round,
                                              ws, static_cast<hipStream_t>(stream)),
                       "dsp_draft_step launch");
 }

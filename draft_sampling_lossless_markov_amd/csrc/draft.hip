@@ -195,10 +195,6 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
 // ---------------------------------------------------------------------------
 // persistent path
 // ---------------------------------------------------------------------------
-static std::atomic<int> g_draft_path{kDraftPathAuto};
-
-void set_draft_path(int path) { g_draft_path.store(path, std::memory_order_relaxed); }
-
 namespace {
 
 struct DevInfo {
@@ -306,10 +302,10 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
 hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
-                             int gamma, int V, int r, int k, int n_steps, float temperature,
-                             uint64_t seed, uint32_t round, void* ws, hipStream_t s)
+                             int gamma, int V, int r, int k, int n_steps, int path,
+                             float temperature, uint64_t seed, uint32_t round, void* ws,
+                             hipStream_t s)
 {
-    const int path = g_draft_path.load(std::memory_order_relaxed);
     if (path != kDraftPathStream && bf16) {
         bool launched = false;
         const hipError_t e = try_launch_run(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok,

@@ -487,6 +487,20 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 }
                 if (tid < kRankMax / 8) *reinterpret_cast<uint4*>(L.e_row + 8 * tid) = ev;
                 lds_barrier();
+                // the embedding row as B fragments (column 0 of the N-tile), read
+                // once for the wave's units
+                // once for the wave's unit (with two units per wave there is no room
+                // for them: then each k-step reads its own)
+                constexpr bool kBfHeld = (NU == 1);
+                uint4 bf[kBfHeld ? kKSteps : 1];
+                auto b_frag = [&](int ks) -> uint4 {
+                    return (c32 == 0) ? *reinterpret_cast<const uint4*>(L.e_row + ks * kKStep + 8 * h)
+                                      : make_uint4(0, 0, 0, 0);
+                };
+                if constexpr (kBfHeld) {
+#pragma unroll
+                    for (int ks = 0; ks < kKSteps; ++ks) bf[ks] = b_frag(ks);
+                }
 #pragma unroll
                 for (int j = 0; j < NU; ++j) {
                     const int uu = wave + 4 * j;
@@ -495,11 +509,9 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
 #pragma unroll
                         for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.0f;
 #pragma unroll
-                        for (int ks = 0; ks < kKSteps; ++ks) {
-                            uint4 bu = make_uint4(0, 0, 0, 0);
-                            if (c32 == 0) bu = *reinterpret_cast<const uint4*>(L.e_row + ks * kKStep + 8 * h);
-                            acc = mfma32_bf16(as_bf16x8(af[j][ks]), as_bf16x8(bu), acc);
-                        }
+                        for (int ks = 0; ks < kKSteps; ++ks)
+                            acc = mfma32_bf16(as_bf16x8(af[j][ks]),
+                                              as_bf16x8(kBfHeld ? bf[kBfHeld ? ks : 0] : b_frag(ks)), acc);
                         if (c32 == 0) {
 #pragma unroll
                             for (int jj = 0; jj < 16; ++jj) L.sh.lg[32 * uu + unit_acc_col(h, jj)] = acc[jj];

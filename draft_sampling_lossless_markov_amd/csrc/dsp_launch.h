@@ -34,13 +34,13 @@ int pass_req_per_wg(int count_max, int n_vt);
 constexpr int kDraftPathAuto = 0;
 constexpr int kDraftPathStream = 1;
 constexpr int kDraftPathPersistent = 2;
-void set_draft_path(int path);
 
 hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
-                             int gamma, int V, int r, int k, int n_steps, float temperature,
-                             uint64_t seed, uint32_t round, void* ws, hipStream_t s);
+                             int gamma, int V, int r, int k, int n_steps, int path,
+                             float temperature, uint64_t seed, uint32_t round, void* ws,
+                             hipStream_t s);
 
 hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
                              const int32_t* tok, const float* w, const float* T,

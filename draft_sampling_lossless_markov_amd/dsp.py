@@ -23,7 +23,7 @@ DSP_WS_DRAFT, DSP_WS_VERIFY = 0, 1
 DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING, DSP_DRAFT_PERSISTENT = 0, 1, 2
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
-            "dsp_set_draft_path", "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
+            "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
 
 _lib = None
 
@@ -58,10 +58,8 @@ def lib():
     L.dsp_workspace_size.argtypes = [I, I, I, I, I]
     L.dsp_workspace_size.restype = SZ
     I64 = C.c_int64
-    L.dsp_set_draft_path.argtypes = [I]
-    L.dsp_set_draft_path.restype = I
-    L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, I, F, U64, U32,
-                                 P, SZ, P]
+    L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, I, U32, F, U64,
+                                 U32, P, SZ, P]
     L.dsp_confidence.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
     L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
@@ -106,21 +104,16 @@ def dsp_workspace_size(which: int, R: int, gamma: int, V: int, r: int) -> int:
     return int(lib().dsp_workspace_size(which, R, gamma, V, r))
 
 
-def dsp_set_draft_path(path):
-    """Process-wide dsp_draft_step implementation: DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING
-    or DSP_DRAFT_PERSISTENT."""
-    _check(lib().dsp_set_draft_path(int(path)))
-
-
 def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_, ws,
-                   stream=None, n_steps=1):
-    """Draft positions k .. k + n_steps - 1 of every request."""
+                   stream=None, n_steps=1, flags=DSP_DRAFT_AUTO):
+    """Draft positions k .. k + n_steps - 1 of every request; flags selects the
+    implementation (DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING or DSP_DRAFT_PERSISTENT)."""
     R, gamma, V = base.shape
     r = E.shape[1]
     rs, ps = _rows(base, "base")
     _check(lib().dsp_draft_step(_ptr(base), _dtype(base), rs, ps, _ptr(E), _ptr(W2), _ptr(anchor),
                                 _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V, r, int(k),
-                                int(n_steps), float(temperature), int(seed), int(round_),
+                                int(n_steps), int(flags), float(temperature), int(seed), int(round_),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 

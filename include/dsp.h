@@ -45,8 +45,8 @@
  * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
  * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
  *
- * ABI version 300: dsp_draft_step draws n_steps consecutive positions per call;
- * dsp_set_draft_path selects its implementation.  (200: element strides.)
+ * ABI version 300: dsp_draft_step draws n_steps consecutive positions per call
+ * and takes flags that select its implementation.  (200: element strides.)
  */
 #ifndef DSP_H
 #define DSP_H
@@ -114,31 +114,28 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  * q      [R, gamma] f32     columns k .. k+n_steps-1 written
  * stats  [R, gamma, 2] f64  columns k .. k+n_steps-1 written
  * k, n_steps   0 <= k, 1 <= n_steps, k + n_steps <= gamma
+ * flags  implementation (the results do not depend on it):
+ *        DSP_DRAFT_AUTO        one persistent cooperative launch for every position
+ *                              where it applies (bf16 logits in 16-byte rows, R <= 2048
+ *                              and a vocabulary whose W2 slice fits on chip: V <= 163840
+ *                              for r <= 256 on 256 CUs), W2 read once; two streaming
+ *                              launches per position elsewhere, W2 read per position
+ *        DSP_DRAFT_STREAMING   the streaming launches always (for callers sharing the
+ *                              GPU with work that must not wait behind a launch that
+ *                              occupies every CU)
+ *        DSP_DRAFT_PERSISTENT  the persistent launch only; where it does not apply
+ *                              the call returns DSP_ERR_HIP (hipErrorNotSupported)
+ *        anything else: DSP_ERR_INVALID_ARG
+ *        While a persistent launch runs, tok[:, k .. k+n_steps-1] also carries its
+ *        progress: the call overwrites those columns (and the workspace) only.
  * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
- *
- * Implementation (results do not depend on it): with bf16 logits in 16-byte
- * rows and a vocabulary whose W2 slice fits on chip (V <= 163840 for r <= 256 on
- * 256 CUs), one persistent cooperative launch runs every position with W2 read
- * once; otherwise each position is two streaming launches that read W2 again.
  */
+typedef enum { DSP_DRAFT_AUTO = 0, DSP_DRAFT_STREAMING = 1, DSP_DRAFT_PERSISTENT = 2 } dsp_draft_flags;
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
                           const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
                           double* stats, int R, int gamma, int V, int r, int k, int n_steps,
-                          float temperature, uint64_t seed, uint32_t round, void* ws,
+                          unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream);
-
-/*
- * dsp_set_draft_path -- process-wide choice of the dsp_draft_step implementation:
- *   DSP_DRAFT_AUTO        persistent launch where it applies, streaming elsewhere
- *   DSP_DRAFT_STREAMING   two launches per position always (for callers that
- *                         share the GPU with work that must not wait behind a
- *                         launch occupying every CU)
- *   DSP_DRAFT_PERSISTENT  persistent launch only; calls it cannot serve return
- *                         DSP_ERR_HIP (hipErrorNotSupported)
- * Returns DSP_ERR_INVALID_ARG for any other value.  Takes effect on later calls.
- */
-typedef enum { DSP_DRAFT_AUTO = 0, DSP_DRAFT_STREAMING = 1, DSP_DRAFT_PERSISTENT = 2 } dsp_draft_path;
-dsp_status dsp_set_draft_path(int path);
 
 /*
  * dsp_confidence -- confidence head with sequential temperature scaling.

@@ -62,7 +62,8 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation returns first
 def _draft(L, **kw):
     a = dict(base=FAKE, dtype=1, base_rs=4 * 32, base_ps=32, E=FAKE, W2=FAKE, anchor=FAKE,
              tok=FAKE, q=FAKE, stats=FAKE,
-             R=4, gamma=4, V=32, r=8, k=0, n_steps=1, temperature=1.0, seed=0, round=0, ws=FAKE,
+             R=4, gamma=4, V=32, r=8, k=0, n_steps=1, flags=0, temperature=1.0, seed=0, round=0,
+             ws=FAKE,
              ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return L.dsp_draft_step(*[C.c_void_p(v) if isinstance(v, int) and k in
@@ -80,6 +81,8 @@ def test_draft_validation(L):
     assert _draft(L, n_steps=0) == 1
     assert _draft(L, k=1, n_steps=4) == 1
     assert b"n_steps" in L.dsp_last_error()
+    assert _draft(L, flags=3) == 1
+    assert b"flags" in L.dsp_last_error()
     assert _draft(L, temperature=-0.5) == 1
     assert _draft(L, temperature=float("nan")) == 1
     assert _draft(L, gamma=65) == 2
@@ -92,13 +95,6 @@ def test_draft_validation(L):
     assert _draft(L, base_ps=-32) == 1
     assert _draft(L, base=FAKE + 4) == 1
     assert b"16-byte" in L.dsp_last_error()
-
-
-def test_draft_path_selection(L):
-    assert L.dsp_set_draft_path(3) == 1
-    assert L.dsp_set_draft_path(-1) == 1
-    for p in (1, 2, 0):
-        assert L.dsp_set_draft_path(p) == 0
 
 
 def test_schedule_validation(L):

@@ -156,27 +156,21 @@ PATH_CASES = [
 ]
 
 
-@pytest.fixture
-def draft_path():
-    yield dsp.dsp_set_draft_path
-    dsp.dsp_set_draft_path(dsp.DSP_DRAFT_AUTO)
-
-
-def _draft_all(inp, rd, temp, rnd, per_position=False):
+def _draft_all(inp, rd, temp, rnd, per_position=False, flags=dsp.DSP_DRAFT_AUTO):
     g = inp["gamma"]
     if per_position:
         for k in range(g):
             dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
-                               rd.stats, k, temp, SEED, rnd, rd.ws_draft)
+                               rd.stats, k, temp, SEED, rnd, rd.ws_draft, flags=flags)
     else:
         dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
-                           rd.stats, 0, temp, SEED, rnd, rd.ws_draft, n_steps=g)
+                           rd.stats, 0, temp, SEED, rnd, rd.ws_draft, n_steps=g, flags=flags)
     torch.cuda.synchronize()
     return np_(rd.tok).copy(), np_(rd.q).copy(), np_(rd.stats).copy()
 
 
 @pytest.mark.parametrize("case", PATH_CASES, ids=lambda c: f"R{c[0]}g{c[1]}V{c[2]}r{c[3]}T{c[4]}")
-def test_draft_paths_vs_oracle(case, draft_path):
+def test_draft_paths_vs_oracle(case):
     R, gamma, V, r, temp = case
     greedy = temp == 0.0
     wl = custom(R, gamma, V, r, 8, torch.bfloat16)
@@ -185,13 +179,12 @@ def test_draft_paths_vs_oracle(case, draft_path):
         inp_cpu = make_inputs(wl, rnd, layout="position")
         inp = to_dev(inp_cpu)
         rd = Round(R, gamma, V, r)
-        draft_path(dsp.DSP_DRAFT_PERSISTENT)          # raises if the launch does not apply
-        pers = _draft_all(inp, rd, temp, rnd)
-        split = _draft_all(inp, rd, temp, rnd, per_position=True)
+        P, S_ = dsp.DSP_DRAFT_PERSISTENT, dsp.DSP_DRAFT_STREAMING
+        pers = _draft_all(inp, rd, temp, rnd, flags=P)     # raises if the launch does not apply
+        split = _draft_all(inp, rd, temp, rnd, per_position=True, flags=P)
         for a, b in zip(pers, split):
             assert np.array_equal(a, b)
-        draft_path(dsp.DSP_DRAFT_STREAMING)
-        strm = _draft_all(inp, rd, temp, rnd)
+        strm = _draft_all(inp, rd, temp, rnd, flags=S_)
         S = np.arange(R, dtype=np.int32)
         o_tok, o_q, o_stats, o_flag = orc.draft(orc.host_logits(inp_cpu["base"]),
                                                 orc.bf16_bits(inp_cpu["E"]),
@@ -207,17 +200,15 @@ def test_draft_paths_vs_oracle(case, draft_path):
     torch.cuda.empty_cache()
 
 
-def test_persistent_path_refuses_what_it_cannot_hold(draft_path):
+def test_persistent_path_refuses_what_it_cannot_hold():
     """V beyond the on-chip capacity and fp32 logits: the persistent-only setting
     reports an error; AUTO serves them with the streaming launches."""
     for V, dt in ((300000, torch.bfloat16), (1000, torch.float32)):
         wl = custom(4, 2, V, 16, 8, dt)
         inp = to_dev(make_inputs(wl, 0))
         rd = Round(4, 2, V, 16)
-        draft_path(dsp.DSP_DRAFT_PERSISTENT)
         with pytest.raises(dsp.DspError):
-            _draft_all(inp, rd, 1.0, 0)
-        draft_path(dsp.DSP_DRAFT_AUTO)
+            _draft_all(inp, rd, 1.0, 0, flags=dsp.DSP_DRAFT_PERSISTENT)
         _draft_all(inp, rd, 1.0, 0)
 
 

@@ -67,9 +67,9 @@ def draft_call_bytes(inp):
 
 def probe_draft_path(call):
     """'persistent' when the persistent draft launch serves this workload (what
-    DSP_DRAFT_AUTO then runs), else 'streaming'."""
+    DSP_PATH_AUTO then runs), else 'streaming'."""
     try:
-        call(dsp.DSP_DRAFT_PERSISTENT)
+        call(dsp.DSP_PATH_PERSISTENT)
         path = "persistent"
     except dsp.DspError:
         path = "streaming"
@@ -180,7 +180,7 @@ def main():
     stream = torch.cuda.current_stream()
     seed = 0
 
-    def draft(i, s=stream, flags=dsp.DSP_DRAFT_AUTO):
+    def draft(i, s=stream, flags=dsp.DSP_PATH_AUTO):
         inp = sets[i % len(sets)]
         dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
                            rd.stats, 0, temp, seed, i, rd.ws_draft, s, n_steps=g, flags=flags)
@@ -271,24 +271,24 @@ def main():
         draft_avg_s = float(draft_ms.mean()) * 1e-3
         draft_timing = "eager launches, events around each call"
     else:
-        # the draft call alone, replayed from a graph, events on the launch stream:
-        # its kernels back to back (what the kernel trace's durations add up to)
+        # K draft calls captured back to back in one graph, replayed with events
+        # on the launch stream: the calls' kernels back to back (what the kernel
+        # trace's durations add up to)
         cap = torch.cuda.Stream()
         gd = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gd, stream=cap):
-            draft(args.warmup, s=cap)
-        for _ in range(2):
-            gd.replay()
+            for i in range(K):
+                draft(args.warmup + i, s=cap)
+        gd.replay()
         torch.cuda.synchronize()
         d0 = torch.cuda.Event(enable_timing=True)
         d1 = torch.cuda.Event(enable_timing=True)
         d0.record(stream)
-        for _ in range(K):
-            gd.replay()
+        gd.replay()
         d1.record(stream)
         torch.cuda.synchronize()
         draft_avg_s = d0.elapsed_time(d1) / K * 1e-3
-        draft_timing = "graph replays of the draft call alone"
+        draft_timing = "one graph of K draft calls back to back"
     achieved = call_bytes / draft_avg_s / 1e9
     traffic = profiled_traffic(wl.name, draft_path)
     kernels = ("draft_run_kernel (one cooperative launch, all gamma positions)"

@@ -68,6 +68,15 @@ dsp_status check_markov(int R, int gamma, int V, int r)
     return DSP_OK;
 }
 
+static_assert(DSP_PATH_AUTO == dsp::kPathAuto && DSP_PATH_STREAMING == dsp::kPathStream &&
+                  DSP_PATH_PERSISTENT == dsp::kPathPersistent,
+              "path codes");
+
+bool known_path(unsigned f)
+{
+    return f == DSP_PATH_AUTO || f == DSP_PATH_STREAMING || f == DSP_PATH_PERSISTENT;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,10 +119,7 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
     if (st != DSP_OK) return st;
     if (k < 0 || k >= gamma)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: k = %d outside [0, gamma)", k);
-    static_assert(DSP_DRAFT_AUTO == dsp::kDraftPathAuto && DSP_DRAFT_STREAMING == dsp::kDraftPathStream &&
-                      DSP_DRAFT_PERSISTENT == dsp::kDraftPathPersistent,
-                  "path codes");
-    if (flags != DSP_DRAFT_AUTO && flags != DSP_DRAFT_STREAMING && flags != DSP_DRAFT_PERSISTENT)
+    if (!known_path(flags))
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: unknown flags %u", flags);
     if (n_steps < 1 || n_steps > gamma - k)
         return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: n_steps = %d outside [1, gamma - k] (k = %d)",
@@ -182,7 +188,7 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                       const float* q, const double* stats, const int32_t* len, int8_t* accept,
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
-                      float temperature, uint64_t seed, uint32_t round, void* ws,
+                      unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
                       size_t ws_bytes, void* stream)
 {
     if (!target || !base || !E || !W2 || !anchor || !tok || !q || !stats || !len || !accept ||
@@ -194,6 +200,7 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
     if (st != DSP_OK) return st;
     if (!(temperature >= 0.0f) || std::isinf(temperature))
         return fail(DSP_ERR_INVALID_ARG, "dsp_verify: temperature must be finite and >= 0");
+    if (!known_path(flags)) return fail(DSP_ERR_INVALID_ARG, "dsp_verify: unknown flags %u", flags);
     st = check_strides("dsp_verify", "target", target_rs, target_ps);
     if (st != DSP_OK) return st;
     st = check_strides("dsp_verify", "base", base_rs, base_ps);
@@ -205,7 +212,8 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
         return fail(DSP_ERR_WORKSPACE, "dsp_verify: workspace of %zu bytes, %zu needed", ws_bytes,
                     need);
     return hip_status(dsp::launch_verify(target, dsp::RowStrides{target_rs, target_ps}, base,
-                                         dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16, E,
+                                         dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16,
+                                         (int)flags, E,
                                          W2, anchor, tok, q,
                                          stats, len, accept, n_accept, y, p, R, gamma, V, r,
                                          temperature, seed, round, ws,

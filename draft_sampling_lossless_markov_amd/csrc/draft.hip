@@ -195,30 +195,37 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
 // ---------------------------------------------------------------------------
 // persistent path
 // ---------------------------------------------------------------------------
+// Marks every partial slot of a launch and the tokens of its positions empty,
+// and clears the error word.
+__global__ void run_clear_kernel(uint64_t* slots, int64_t n_slots, int32_t* tok, int R, int gamma,
+                                 int k0, int n_steps, unsigned* ctl)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = i0; i < n_slots; i += stride) slots[i] = kRunSlotEmpty;
+    const int64_t n_tok = (int64_t)R * n_steps;
+    for (int64_t i = i0; i < n_tok; i += stride)
+        tok[(i / n_steps) * gamma + k0 + (i % n_steps)] = kRunTokEmpty;
+    if (i0 == 0) ctl[0] = 0u;
+}
+
 namespace {
 
-struct DevInfo {
-    int ncu, coop;
-};
-
-// compute units and cooperative-launch support of the current device (cached)
-DevInfo device_info()
+// compute units of the current device (cached per device)
+int device_cus()
 {
     constexpr int kDevs = 64;
-    static std::atomic<int> ncu[kDevs], coop[kDevs], known[kDevs];
+    static std::atomic<int> ncu[kDevs];
     int d = 0;
-    if (hipGetDevice(&d) != hipSuccess) return DevInfo{0, 0};
-    if (d >= 0 && d < kDevs && known[d].load(std::memory_order_acquire))
-        return DevInfo{ncu[d].load(std::memory_order_relaxed), coop[d].load(std::memory_order_relaxed)};
-    int n = 0, c = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) n = 0;
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeCooperativeLaunch, d) != hipSuccess) c = 0;
+    if (hipGetDevice(&d) != hipSuccess) return 0;
     if (d >= 0 && d < kDevs) {
-        ncu[d].store(n, std::memory_order_relaxed);
-        coop[d].store(c, std::memory_order_relaxed);
-        known[d].store(1, std::memory_order_release);
+        const int c = ncu[d].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
-    return DevInfo{n, c};
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) n = 0;
+    if (d >= 0 && d < kDevs && n > 0) ncu[d].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // the fewest 32-column units per wave for which the tiles (four per
@@ -255,10 +262,12 @@ hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, hipStream_t s, bool* 
                        ra.gamma, ra.k0, ra.n_steps, ra.ctl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    RunArgs arg = ra;
-    void* args[] = {&arg};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&draft_run_kernel<GREEDY, TU>),
-                                   dim3(G), dim3(256), args, 0, s);
+    // an ordinary launch: the grid has at most one workgroup per CU and the
+    // kernel's registers and LDS admit exactly one, so every workgroup is
+    // resident at once (a cooperative launch would guarantee the same at ~18 us
+    // more per launch, measured on MI355X)
+    hipLaunchKernelGGL((draft_run_kernel<GREEDY, TU>), dim3(G), dim3(256), 0, s, ra);
+    e = hipGetLastError();
     if (e == hipSuccess) *launched = true;
     return e;
 }
@@ -271,10 +280,9 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
 {
     *launched = false;
     if (!rows_vec(bs, V, 8) || R > kRunReqMax) return hipSuccess;
-    const DevInfo di = device_info();
-    int n_t = 0;
-    const int tu = run_units(V, di.ncu, &n_t);
-    if (!di.coop || tu == 0) return hipSuccess;
+    RunGeometry geo;
+    if (!run_geometry(V, &geo)) return hipSuccess;
+    const int tu = geo.tu, n_t = geo.n_t;
     const bool greedy = (temperature == 0.0f);
     RunArgs ra{};
     ra.base = base; ra.bs = bs; ra.E = E; ra.W2 = W2; ra.anchor = anchor; ra.tok = tok; ra.q = q;
@@ -285,8 +293,8 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
     ra.ctl = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + draft_part_bytes(R, V));
     const int G = (n_t + 3) / 4;
 #define DSP_RUN(TU)                                                                            \
-    return greedy ? launch_run_t<true, TU>(ra, G, di.ncu, s, launched)                         \
-                  : launch_run_t<false, TU>(ra, G, di.ncu, s, launched)
+    return greedy ? launch_run_t<true, TU>(ra, G, geo.ncu, s, launched)                        \
+                  : launch_run_t<false, TU>(ra, G, geo.ncu, s, launched)
     switch (tu) {
     case 1: DSP_RUN(1);
     case 2: DSP_RUN(2);
@@ -299,6 +307,15 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
 
 }  // namespace
 
+bool run_geometry(int V, RunGeometry* g)
+{
+    const int ncu = device_cus();
+    int n_t = 0;
+    const int tu = run_units(V, ncu, &n_t);
+    *g = RunGeometry{tu, n_t, ncu};
+    return tu > 0;
+}
+
 hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
@@ -306,14 +323,14 @@ hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const u
                              float temperature, uint64_t seed, uint32_t round, void* ws,
                              hipStream_t s)
 {
-    if (path != kDraftPathStream && bf16) {
+    if (path != kPathStream && bf16) {
         bool launched = false;
         const hipError_t e = try_launch_run(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok,
                                             q, stats, R, gamma, V, r, k, n_steps, temperature, seed,
                                             round, ws, s, &launched);
         if (launched || e != hipSuccess) return e;
     }
-    if (path == kDraftPathPersistent) return hipErrorNotSupported;
+    if (path == kPathPersistent) return hipErrorNotSupported;
     for (int i = 0; i < n_steps; ++i) {
         const hipError_t e =
             bf16 ? launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,

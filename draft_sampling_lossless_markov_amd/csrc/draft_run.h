@@ -4,7 +4,8 @@
 // so the positions of a round run in sequence, and each one needs the bias
 // E[x_{k-1}] . W2^T over the whole vocabulary.  Re-reading W2 (V x r bf16) for
 // every position dominates the traffic of a small batch, so this kernel reads it
-// once per call: one workgroup per CU (co-resident by a cooperative launch), each
+// once per call: one workgroup per CU (all resident at once: the grid has at most
+// one per CU and the kernel's registers and LDS admit exactly one), each
 // holding its slice of W2 on chip -- three 32-column units per wave in VGPRs as
 // MFMA fragments and up to two in LDS.  Per position:
 //   phase 1 (every workgroup): the previous tokens of all requests, then per
@@ -31,7 +32,7 @@
 // relaxed atomics, which gfx950 performs coherently across its XCDs (no L2
 // writeback or invalidate is needed).  Every wait is bounded: one that exceeds
 // the limit sets the error word, and every later wait then returns at once, so
-// the grid always drains (a co-resident launch never gets there).
+// the grid always drains (a resident grid never gets there).
 #pragma once
 
 #include "tile_pass.h"
@@ -138,18 +139,58 @@ struct RunLds {
     PickScratch sh;
 };
 
-// Marks every partial slot of a launch and the tokens of its positions empty,
-// and clears the error word.
-__global__ void run_clear_kernel(uint64_t* slots, int64_t n_slots, int32_t* tok, int R, int gamma,
-                                 int k0, int n_steps, unsigned* ctl)
+// The wave's W2 units (the 32 TU columns from v_tile): units 0 .. NR-1 into
+// MFMA A fragments, the others into the wave's LDS slots (unit NR + i in slot
+// i).  Each unit is read contiguously (an instruction covers two whole rows)
+// into the wave's first LDS slot and the fragments are read from there; the
+// LDS-resident units are written straight to their slots.  Called by every
+// wave of the workgroup (it holds workgroup barriers).
+template <int TU, int NR, int NLA>
+__device__ __forceinline__ void stage_w2_slice(const uint16_t* __restrict__ W2, int V, int r, int v_tile,
+                                               uint4 (&w2)[NLA][32][kRankMax / 8],
+                                               bf16x8 (&afrag)[NR][kKSteps])
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t i = i0; i < n_slots; i += stride) slots[i] = kRunSlotEmpty;
-    const int64_t n_tok = (int64_t)R * n_steps;
-    for (int64_t i = i0; i < n_tok; i += stride)
-        tok[(i / n_steps) * gamma + k0 + (i % n_steps)] = kRunTokEmpty;
-    if (i0 == 0) ctl[0] = 0u;
+    constexpr int kWordsRow = kRankMax / 8;   // 16-byte words of a staged W2 row
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int prow = unit_row_col(lane & 31);
+    uint4 cur[16], nxt[16];
+    auto fetch = [&](int u, uint4* w) {
+        const int v0 = v_tile + 32 * u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int f = i * 64 + lane, rho = f / kWordsRow, c = f % kWordsRow;
+            const int v = v0 + rho;
+            w[i] = (v < V && 8 * c < r) ? *reinterpret_cast<const uint4*>(W2 + (int64_t)v * r + 8 * c)
+                                        : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto put = [&](int slot, const uint4* w) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int f = i * 64 + lane, rho = f / kWordsRow, c = f % kWordsRow;
+            w2[slot][rho][w2_slot(rho, c)] = w[i];
+        }
+    };
+    fetch(0, cur);
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+        if (u + 1 < TU) fetch(u + 1, nxt);
+        if (u < NR) {
+            put(0, cur);
+            lds_barrier();
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks)
+                afrag[u < NR ? u : 0][ks] = as_bf16x8(w2[0][prow][w2_slot(prow, 2 * ks + h)]);
+            lds_barrier();
+        } else {
+            put(u - NR, cur);
+        }
+        if (u + 1 < TU) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
+        }
+    }
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -162,7 +203,6 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
 {
     constexpr int NR = TU < kRunRegUnits ? TU : kRunRegUnits;
     constexpr int NL = TU - NR;
-    constexpr int kWordsRow = kRankMax / 8;   // 16-byte words of a staged W2 row
     __shared__ RunLds<NL> L;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -174,52 +214,8 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
     const float itL = fold_itl(a.inv_temp);
     const int prow = unit_row_col(c32);   // unit row of this lane's A fragments
 
-    // ---- the wave's W2 units: each read contiguously (an instruction covers
-    // two whole rows) into the wave's first LDS slot, then into fragments; the
-    // LDS-resident units are written straight to their slots
     bf16x8 afrag[NR][kKSteps];
-    {
-        uint4 cur[16], nxt[16];
-        auto fetch = [&](int u, uint4* w) {
-            const int v0 = v_tile + 32 * u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int f = i * 64 + lane, rho = f / kWordsRow, c = f % kWordsRow;
-                const int v = v0 + rho;
-                w[i] = (v < V && 8 * c < r)
-                           ? *reinterpret_cast<const uint4*>(a.W2 + (int64_t)v * r + 8 * c)
-                           : make_uint4(0, 0, 0, 0);
-            }
-        };
-        auto put = [&](int slot, const uint4* w) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int f = i * 64 + lane, rho = f / kWordsRow, c = f % kWordsRow;
-                L.w2[wave][slot][rho][w2_slot(rho, c)] = w[i];
-            }
-        };
-        fetch(0, cur);
-#pragma unroll
-        for (int u = 0; u < TU; ++u) {
-            if (u + 1 < TU) fetch(u + 1, nxt);
-            if (u < NR) {
-                put(0, cur);
-                lds_barrier();
-#pragma unroll
-                for (int ks = 0; ks < kKSteps; ++ks)
-                    afrag[u < NR ? u : 0][ks] =
-                        as_bf16x8(L.w2[wave][0][prow][w2_slot(prow, 2 * ks + h)]);
-                lds_barrier();
-            } else {
-                put(u - NR, cur);
-            }
-            if (u + 1 < TU) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
-            }
-        }
-        lds_barrier();
-    }
+    stage_w2_slice<TU, NR>(a.W2, V, r, v_tile, L.w2[wave], afrag);
 
     const int srow = tid & 31, sq = tid >> 5;   // embedding staging: row, word group
     const int RB = (R + kPassBlock - 1) / kPassBlock;

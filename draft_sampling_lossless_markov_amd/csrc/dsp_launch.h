@@ -29,11 +29,19 @@ size_t draft_workspace_bytes(int R, int V);
 size_t verify_workspace_bytes(int R, int gamma, int V);
 int pass_req_per_wg(int count_max, int n_vt);
 
-// draft paths: automatic (persistent where it fits), streaming only,
-// persistent only (hipErrorNotSupported where it does not fit)
-constexpr int kDraftPathAuto = 0;
-constexpr int kDraftPathStream = 1;
-constexpr int kDraftPathPersistent = 2;
+// implementation paths of the draft and the residual draws: automatic
+// (persistent where it fits), streaming only, persistent only
+// (hipErrorNotSupported where it does not fit)
+constexpr int kPathAuto = 0;
+constexpr int kPathStream = 1;
+constexpr int kPathPersistent = 2;
+
+// Geometry of a persistent launch for vocabulary V on the current device:
+// units per wave (0: none fits), tiles, compute units; false when none fits.
+struct RunGeometry {
+    int tu, n_t, ncu;
+};
+bool run_geometry(int V, RunGeometry* g);
 
 hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
                              const uint16_t* W2,
@@ -51,7 +59,7 @@ hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t
                            int32_t* len, float* a, int32_t* B, int R, int gamma, hipStream_t s);
 
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
-                         bool bf16, const uint16_t* E,
+                         bool bf16, int path, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,

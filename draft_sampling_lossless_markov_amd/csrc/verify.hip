@@ -18,10 +18,16 @@
 //                    rebuilt with the draft step's MFMA bias
 //   verify_pick      one workgroup per request: locate the tile of the residual
 //                    (or of the bonus / zero-residual fallback row) and scan it
+// Where the draft's W2 slice fits on chip (bf16 rows), resid_run_kernel
+// (resid_run.h) replaces the last two launches with one persistent launch.
 #include "bias_tile.h"
 #include "dsp_device.h"
 #include "dsp_launch.h"
+#include "resid_run.h"
 #include "tile_pass.h"
+
+#include <atomic>
+#include <type_traits>
 
 namespace dsp {
 
@@ -41,6 +47,8 @@ struct VerifyWs {
     double* row_z;       // [R] normaliser of target row n_accept (rejecting requests)
     float* row_m;        // [R] max logit of that row
     Part* resid_part;    // [R, n_vt]
+    uint64_t* run_slots; // [R, n_t] residual mass of the persistent residual launch
+    unsigned* run_ctl;   // its error word
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -63,6 +71,9 @@ inline VerifyWs carve(void* ws, int R, int gamma, int V, size_t* total)
     w.row_z = reinterpret_cast<double*>(p + off);     off += align256((size_t)R * sizeof(double));
     w.row_m = reinterpret_cast<float*>(p + off);      off += align256((size_t)R * sizeof(float));
     w.resid_part = reinterpret_cast<Part*>(p + off);  off += align256((size_t)R * n_vt * sizeof(Part));
+    const size_t n_run = std::min<size_t>((size_t)((V + 31) / 32), (size_t)kRunTilesMax);
+    w.run_slots = reinterpret_cast<uint64_t*>(p + off); off += align256((size_t)R * n_run * sizeof(uint64_t));
+    w.run_ctl = reinterpret_cast<unsigned*>(p + off); off += 256;
     if (total) *total = off;
     return w;
 }
@@ -89,7 +100,10 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
     constexpr int RW = Logit<LT>::kRaw;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const float itL = fold_itl(inv_temp);
-    if (blockIdx.x == 0 && tid == 0) *ws.resid_cnt = 0;
+    if (blockIdx.x == 0 && tid == 0) {
+        *ws.resid_cnt = 0;
+        ws.run_ctl[0] = 0u;
+    }
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int per_req = (gamma + 1) * spans;
     const bool vec_ok = rows_vec(ts, V, Logit<LT>::kVecAlign);
@@ -181,8 +195,9 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
     const int32_t* __restrict__ tok, const float* __restrict__ q, const int32_t* __restrict__ len,
     int8_t* __restrict__ accept, int32_t* __restrict__ n_accept, int32_t* __restrict__ y,
     float* __restrict__ p_out, int R, int gamma, float inv_temp, uint64_t seed, uint32_t round,
-    int n_vt, VerifyWs ws)
+    int n_vt, VerifyWs ws, int run_n_t)
 {
+    __shared__ int slot_s;
     __shared__ int acc_s[kGammaMax + 1];
     __shared__ float pj_s[kGammaMax + 1];
     __shared__ float m_s[kGammaMax + 1];
@@ -247,11 +262,13 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
     }
     if (tid == 0) {
         n_accept[n] = nacc;
+        slot_s = -1;
         if constexpr (GREEDY) {
             y[n] = am_s[nacc];
         } else {
             if (nacc < l) {
                 const int slot = atomicAdd(ws.resid_cnt, 1);
+                slot_s = slot;
                 ws.resid_list[slot] = n;
                 ws.resid_m[slot] = nacc;
                 ws.resid_prev[slot] = prev_token(anchor, tok, n, gamma, nacc, V);
@@ -261,6 +278,15 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
             } else {
                 ws.resid_slot[n] = -1;
             }
+        }
+    }
+    if constexpr (!GREEDY) {
+        // a persistent residual launch follows: its slots of this request start empty
+        if (run_n_t > 0) {
+            __syncthreads();
+            const int slot = slot_s;
+            if (slot >= 0)
+                for (int t = tid; t < run_n_t; t += 256) ws.run_slots[(int64_t)slot * run_n_t + t] = kRunSlotEmpty;
         }
     }
 }
@@ -383,13 +409,14 @@ template <bool GREEDY>
 static void launch_accept(const int32_t* anchor, int V, const int32_t* tok, const float* q,
                           const int32_t* len, int8_t* accept, int32_t* n_accept, int32_t* y,
                           float* p, int R, int gamma, float it, uint64_t seed, uint32_t round,
-                          int n_vt, const VerifyWs& ws, hipStream_t s)
+                          int n_vt, const VerifyWs& ws, hipStream_t s, int run_n_t = 0)
 {
     const int np = 4 * ((n_vt + kSpanTiles - 1) / kSpanTiles);
     const int per = (np + kWave - 1) / kWave;     // <= 4 for V <= kVocabMax
 #define DSP_ACCEPT(P)                                                                          \
     hipLaunchKernelGGL((verify_accept_kernel<GREEDY, P>), dim3(R), dim3(256), 0, s, anchor, V, \
-                       tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws)
+                       tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws,  \
+                       run_n_t)
     if (per <= 1) DSP_ACCEPT(1);
     else if (per <= 2) DSP_ACCEPT(2);
     else if (per <= 4) DSP_ACCEPT(4);
@@ -413,9 +440,29 @@ static void launch_vpick(const LT* target, RowStrides ts, const LT* base, RowStr
                        ws);
 }
 
+template <int TU>
+static hipError_t launch_resid_t(const ResidArgs& ra, int G, int ncu, hipStream_t s, bool* launched)
+{
+    *launched = false;
+    static std::atomic<int> occ{-1};
+    if (occ.load(std::memory_order_relaxed) < 0) {
+        int o = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, resid_run_kernel<TU>, 256, 0) != hipSuccess)
+            o = 0;
+        occ.store(o, std::memory_order_relaxed);
+    }
+    if (G > occ.load(std::memory_order_relaxed) * ncu) return hipSuccess;
+    // an ordinary launch with every workgroup resident at once (at most one per
+    // CU, and the kernel admits exactly one), as for draft_run_kernel
+    hipLaunchKernelGGL((resid_run_kernel<TU>), dim3(G), dim3(256), 0, s, ra);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) *launched = true;
+    return e;
+}
+
 template <typename LT>
 static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
-                                  const uint16_t* E,
+                                  int path, const uint16_t* E,
                                   const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                                   const float* q, const double* stats, const int32_t* len,
                                   int8_t* accept, int32_t* n_accept, int32_t* y, float* p, int R,
@@ -429,6 +476,7 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int64_t items = (int64_t)R * (gamma + 1) * spans;
     const dim3 g1((unsigned)items);
+    if (path == kPathPersistent && !std::is_same<LT, uint16_t>::value) return hipErrorNotSupported;
     if (greedy) {
         hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, ts, tok, len,
                            R, gamma, V, it, n_vt, ws);
@@ -436,10 +484,41 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
                             round, n_vt, ws, s);
         return hipGetLastError();
     }
+    // the persistent residual launch, where the draft's geometry applies
+    RunGeometry geo{0, 0, 0};
+    bool run = false;
+    if constexpr (std::is_same<LT, uint16_t>::value)
+        run = path != kPathStream && rows_vec(bs, V, 8) && rows_vec(ts, V, 8) && R <= kRunReqMax &&
+              run_geometry(V, &geo);
+    if (path == kPathPersistent && !run) return hipErrorNotSupported;
     hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, ts, tok, len, R,
                        gamma, V, it, n_vt, ws);
     launch_accept<false>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round,
-                         n_vt, ws, s);
+                         n_vt, ws, s, run ? geo.n_t : 0);
+    if constexpr (std::is_same<LT, uint16_t>::value) {
+        if (run) {
+            ResidArgs ra{};
+            ra.base = base; ra.bs = bs; ra.target = target; ra.ts = ts; ra.E = E; ra.W2 = W2;
+            ra.stats = stats; ra.len = len; ra.n_accept = n_accept; ra.y = y;
+            ra.R = R; ra.gamma = gamma; ra.V = V; ra.r = r; ra.inv_temp = it; ra.seed = seed;
+            ra.round = round; ra.n_t = geo.n_t; ra.n_vt = n_vt;
+            ra.count = ws.resid_cnt; ra.list = ws.resid_list; ra.list_m = ws.resid_m;
+            ra.list_prev = ws.resid_prev; ra.slot_of = ws.resid_slot; ra.row_m = ws.row_m;
+            ra.row_z = ws.row_z; ra.rowpart = ws.rowpart; ra.slots = ws.run_slots; ra.ctl = ws.run_ctl;
+            const int G = (geo.n_t + 3) / 4;
+            bool launched = false;
+            hipError_t e = hipSuccess;
+            switch (geo.tu) {
+            case 1: e = launch_resid_t<1>(ra, G, geo.ncu, s, &launched); break;
+            case 2: e = launch_resid_t<2>(ra, G, geo.ncu, s, &launched); break;
+            case 3: e = launch_resid_t<3>(ra, G, geo.ncu, s, &launched); break;
+            case 4: e = launch_resid_t<4>(ra, G, geo.ncu, s, &launched); break;
+            default: e = launch_resid_t<5>(ra, G, geo.ncu, s, &launched); break;
+            }
+            if (launched || e != hipSuccess) return e;
+            if (path == kPathPersistent) return hipErrorNotSupported;
+        }
+    }
     PassArgs a{};
     a.base = base; a.target = target; a.bs = bs; a.ts = ts;
     a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
@@ -464,7 +543,7 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
 }
 
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
-                         bool bf16, const uint16_t* E,
+                         bool bf16, int path, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
@@ -472,11 +551,11 @@ hipError_t launch_verify(const void* target, RowStrides ts, const void* base, Ro
 {
     if (bf16)
         return launch_verify_t(static_cast<const uint16_t*>(target), ts,
-                               static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,
+                               static_cast<const uint16_t*>(base), bs, path, E, W2, anchor, tok, q, stats,
                                len, accept, n_accept, y, p, R, gamma, V, r, temperature, seed, round,
                                ws, s);
     return launch_verify_t(static_cast<const float*>(target), ts, static_cast<const float*>(base), bs,
-                           E, W2,
+                           path, E, W2,
                            anchor, tok, q, stats, len, accept, n_accept, y, p, R, gamma, V, r,
                            temperature, seed, round, ws, s);
 }

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libdsp.so")
 DSP_OK, DSP_ERR_INVALID_ARG, DSP_ERR_UNSUPPORTED, DSP_ERR_WORKSPACE, DSP_ERR_HIP = range(5)
 DSP_F32, DSP_BF16 = 0, 1
 DSP_WS_DRAFT, DSP_WS_VERIFY = 0, 1
-DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING, DSP_DRAFT_PERSISTENT = 0, 1, 2
+DSP_PATH_AUTO, DSP_PATH_STREAMING, DSP_PATH_PERSISTENT = 0, 1, 2
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
             "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
@@ -63,7 +63,7 @@ def lib():
     L.dsp_confidence.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
     L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
-                             I, I, F, U64, U32, P, SZ, P]
+                             I, I, U32, F, U64, U32, P, SZ, P]
     for f in ("dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify"):
         getattr(L, f).restype = I
     _lib = L
@@ -105,9 +105,9 @@ def dsp_workspace_size(which: int, R: int, gamma: int, V: int, r: int) -> int:
 
 
 def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_, ws,
-                   stream=None, n_steps=1, flags=DSP_DRAFT_AUTO):
+                   stream=None, n_steps=1, flags=DSP_PATH_AUTO):
     """Draft positions k .. k + n_steps - 1 of every request; flags selects the
-    implementation (DSP_DRAFT_AUTO, DSP_DRAFT_STREAMING or DSP_DRAFT_PERSISTENT)."""
+    implementation (DSP_PATH_AUTO, DSP_PATH_STREAMING or DSP_PATH_PERSISTENT)."""
     R, gamma, V = base.shape
     r = E.shape[1]
     rs, ps = _rows(base, "base")
@@ -131,7 +131,7 @@ def dsp_schedule(c, sps, B_max, tau0, mode, length, a, B, stream=None):
 
 
 def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_accept, y, p,
-               temperature, seed, round_, ws, stream=None):
+               temperature, seed, round_, ws, stream=None, flags=DSP_PATH_AUTO):
     R, g1, V = target.shape
     r = E.shape[1]
     trs, tps = _rows(target, "target")
@@ -142,5 +142,5 @@ def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_acc
                             _ptr(E), _ptr(W2),
                             _ptr(anchor), _ptr(tok), _ptr(q), _ptr(stats), _ptr(length),
                             _ptr(accept), _ptr(n_accept), _ptr(y), _ptr(p), R, g1 - 1, V, r,
-                            float(temperature), int(seed), int(round_), _ptr(ws),
+                            int(flags), float(temperature), int(seed), int(round_), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)))

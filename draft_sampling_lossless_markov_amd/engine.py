@@ -47,10 +47,10 @@ class Round:
         dsp.dsp_schedule(self.c, inp["sps"], inp["B_max"], tau0, mode, self.len, self.a, self.B,
                          stream)
 
-    def verify(self, inp, temperature, seed, rnd, stream=None):
+    def verify(self, inp, temperature, seed, rnd, stream=None, flags=dsp.DSP_PATH_AUTO):
         dsp.dsp_verify(inp["target"], inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok,
                        self.q, self.stats, self.len, self.accept, self.n_accept, self.y, self.p,
-                       temperature, seed, rnd, self.ws_verify, stream)
+                       temperature, seed, rnd, self.ws_verify, stream, flags=flags)
 
     def run(self, inp, temperature, seed, rnd, mode=None, tau0=None, stream=None):
         self.draft(inp, temperature, seed, rnd, stream)

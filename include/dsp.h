@@ -45,8 +45,9 @@
  * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
  * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
  *
- * ABI version 300: dsp_draft_step draws n_steps consecutive positions per call
- * and takes flags that select its implementation.  (200: element strides.)
+ * ABI version 300: dsp_draft_step draws n_steps consecutive positions per call;
+ * dsp_draft_step and dsp_verify take flags that select their implementation.
+ * (200: element strides.)
  */
 #ifndef DSP_H
 #define DSP_H
@@ -114,23 +115,26 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  * q      [R, gamma] f32     columns k .. k+n_steps-1 written
  * stats  [R, gamma, 2] f64  columns k .. k+n_steps-1 written
  * k, n_steps   0 <= k, 1 <= n_steps, k + n_steps <= gamma
- * flags  implementation (the results do not depend on it):
- *        DSP_DRAFT_AUTO        one persistent cooperative launch for every position
+ * flags  implementation, a dsp_path_flags value (the results do not depend on it):
+ *        DSP_PATH_AUTO         one persistent launch for every position
  *                              where it applies (bf16 logits in 16-byte rows, R <= 2048
  *                              and a vocabulary whose W2 slice fits on chip: V <= 163840
  *                              for r <= 256 on 256 CUs), W2 read once; two streaming
  *                              launches per position elsewhere, W2 read per position
- *        DSP_DRAFT_STREAMING   the streaming launches always (for callers sharing the
- *                              GPU with work that must not wait behind a launch that
- *                              occupies every CU)
- *        DSP_DRAFT_PERSISTENT  the persistent launch only; where it does not apply
+ *        DSP_PATH_STREAMING    the streaming launches always (for callers sharing the
+ *                              GPU with concurrent work: a persistent launch holds one
+ *                              workgroup on every CU and relies on all of them being
+ *                              resident; work on other streams can only delay it, and
+ *                              a wait that outlasts a few seconds gives up, leaving
+ *                              the outputs undefined)
+ *        DSP_PATH_PERSISTENT   the persistent launch only; where it does not apply
  *                              the call returns DSP_ERR_HIP (hipErrorNotSupported)
  *        anything else: DSP_ERR_INVALID_ARG
  *        While a persistent launch runs, tok[:, k .. k+n_steps-1] also carries its
  *        progress: the call overwrites those columns (and the workspace) only.
  * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
  */
-typedef enum { DSP_DRAFT_AUTO = 0, DSP_DRAFT_STREAMING = 1, DSP_DRAFT_PERSISTENT = 2 } dsp_draft_flags;
+typedef enum { DSP_PATH_AUTO = 0, DSP_PATH_STREAMING = 1, DSP_PATH_PERSISTENT = 2 } dsp_path_flags;
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
                           const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
                           double* stats, int R, int gamma, int V, int r, int k, int n_steps,
@@ -214,6 +218,12 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
  * [R, gamma, 2] (f64) as
  * written by dsp_draft_step; len [R]; outputs accept [R, gamma] int8,
  * n_accept [R] int32, y [R] int32, p [R, gamma] f32.
+ * flags: a dsp_path_flags value for the residual draws (sampling; the results do
+ * not depend on it): DSP_PATH_AUTO draws them in one persistent launch
+ * that holds the W2 slice on chip where the draft's does (see dsp_draft_step), with
+ * a streaming pass and a pick launch elsewhere; DSP_PATH_STREAMING always the latter;
+ * DSP_PATH_PERSISTENT the former only (DSP_ERR_HIP, hipErrorNotSupported, where it
+ * does not apply; greedy verification draws no residual and ignores it).
  * ws >= dsp_workspace_size(DSP_WS_VERIFY, R, gamma, V, r) bytes.
  */
 dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
@@ -221,7 +231,7 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                       const float* q, const double* stats, const int32_t* len, int8_t* accept,
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
-                      float temperature, uint64_t seed, uint32_t round, void* ws,
+                      unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -116,16 +116,18 @@ def test_confidence_and_verify_validation(L):
                             4, 4, -1, 32, 8, None) == 1
     # target (rs, ps) = (5 * 32, 32), base (4 * 32, 32): contiguous [R, gamma(+1), V]
     two = [P(FAKE), 5 * 32, 32, P(FAKE), 4 * 32, 32]
-    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0, 0, 0, P(FAKE), 16, None)
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0, 1.0, 0, 0, P(FAKE), 16, None)
     assert v == 3   # workspace too small
-    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 12, 1.0, 0, 0, P(FAKE), 1 << 20, None)
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 12, 0, 1.0, 0, 0, P(FAKE), 1 << 20, None)
     assert v == 2
-    v = L.dsp_verify(P(0), 5 * 32, 32, P(FAKE), 4 * 32, 32, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0,
+    v = L.dsp_verify(P(0), 5 * 32, 32, P(FAKE), 4 * 32, 32, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0, 1.0,
                      0, 0, P(FAKE), 1 << 20, None)
     assert v == 1
-    v = L.dsp_verify(P(FAKE), -1, 32, P(FAKE), 4 * 32, 32, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 1.0,
+    v = L.dsp_verify(P(FAKE), -1, 32, P(FAKE), 4 * 32, 32, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0, 1.0,
                      0, 0, P(FAKE), 1 << 20, None)
     assert v == 1 and b"target strides" in L.dsp_last_error()
     v = L.dsp_verify(P(FAKE), 5 * 32, 32, P(FAKE), 4 * 32, -5, 1, *[P(FAKE)] * 11, 4, 4, 32, 8,
-                     1.0, 0, 0, P(FAKE), 1 << 20, None)
+                     0, 1.0, 0, 0, P(FAKE), 1 << 20, None)
     assert v == 1 and b"base strides" in L.dsp_last_error()
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 7, 1.0, 0, 0, P(FAKE), 1 << 20, None)
+    assert v == 1 and b"flags" in L.dsp_last_error()

@@ -156,7 +156,7 @@ PATH_CASES = [
 ]
 
 
-def _draft_all(inp, rd, temp, rnd, per_position=False, flags=dsp.DSP_DRAFT_AUTO):
+def _draft_all(inp, rd, temp, rnd, per_position=False, flags=dsp.DSP_PATH_AUTO):
     g = inp["gamma"]
     if per_position:
         for k in range(g):
@@ -179,7 +179,7 @@ def test_draft_paths_vs_oracle(case):
         inp_cpu = make_inputs(wl, rnd, layout="position")
         inp = to_dev(inp_cpu)
         rd = Round(R, gamma, V, r)
-        P, S_ = dsp.DSP_DRAFT_PERSISTENT, dsp.DSP_DRAFT_STREAMING
+        P, S_ = dsp.DSP_PATH_PERSISTENT, dsp.DSP_PATH_STREAMING
         pers = _draft_all(inp, rd, temp, rnd, flags=P)     # raises if the launch does not apply
         split = _draft_all(inp, rd, temp, rnd, per_position=True, flags=P)
         for a, b in zip(pers, split):
@@ -200,6 +200,50 @@ def test_draft_paths_vs_oracle(case):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("case", [c for c in PATH_CASES if c[4] > 0],
+                         ids=lambda c: f"R{c[0]}g{c[1]}V{c[2]}r{c[3]}T{c[4]}")
+def test_residual_paths_vs_oracle(case):
+    """Verification with the persistent residual launch and with the streaming
+    residual pass + pick, on the oracle's draft and seeded prefix lengths: both
+    against the oracle's verification."""
+    R, gamma, V, r, temp = case
+    wl = custom(R, gamma, V, r, 8, torch.bfloat16)
+    for rnd in range(2):
+        _say(f"residual paths {case} round {rnd}")
+        inp_cpu = make_inputs(wl, rnd, layout="position")
+        inp = to_dev(inp_cpu)
+        E_h, W2_h = orc.bf16_bits(inp_cpu["E"]), orc.bf16_bits(inp_cpu["W2"])
+        anchor = np_(inp_cpu["anchor"])
+        base_h, tgt_h = orc.host_logits(inp_cpu["base"]), orc.host_logits(inp_cpu["target"])
+        S = np.arange(R, dtype=np.int32)
+        o_tok, o_q, o_stats, _ = orc.draft(base_h, E_h, W2_h, anchor, S, temp, SEED, rnd)
+        gen = torch.Generator(device="cpu").manual_seed(100 + rnd)
+        lens = torch.randint(0, gamma + 1, (R,), generator=gen, dtype=torch.int32)
+        lens[0] = gamma
+        lens[-1] = 0
+        o_v = orc.verify(tgt_h, base_h, E_h, W2_h, anchor, o_tok, o_q, lens.numpy(), S, temp,
+                         SEED, rnd)
+        rd = Round(R, gamma, V, r)
+        rd.tok.copy_(torch.from_numpy(o_tok))
+        rd.q.copy_(torch.from_numpy(o_q.astype(np.float32)))
+        rd.stats.copy_(torch.from_numpy(o_stats))
+        rd.len.copy_(lens)
+        ys = []
+        for flags in (dsp.DSP_PATH_PERSISTENT, dsp.DSP_PATH_STREAMING):
+            rd.y.fill_(-7)
+            rd.verify(inp, temp, SEED, rnd, flags=flags)
+            torch.cuda.synchronize()
+            g_v = {k: np_(getattr(rd, k)).copy() for k in ("accept", "n_accept", "y", "p")}
+            t = compare_verify(g_v, o_v, lens.numpy(), False, S)
+            assert t.ok(), (flags, t.summary())
+            assert t.mismatch_rate() <= 1e-3, (flags, t.summary())
+            ys.append(g_v["y"])
+        n_rej = int((ys[0] >= 0).sum())
+        _say(f"  {n_rej} draws, paths differ on {int((ys[0] != ys[1]).sum())}")
+        del rd, inp
+    torch.cuda.empty_cache()
+
+
 def test_persistent_path_refuses_what_it_cannot_hold():
     """V beyond the on-chip capacity and fp32 logits: the persistent-only setting
     reports an error; AUTO serves them with the streaming launches."""
@@ -208,8 +252,12 @@ def test_persistent_path_refuses_what_it_cannot_hold():
         inp = to_dev(make_inputs(wl, 0))
         rd = Round(4, 2, V, 16)
         with pytest.raises(dsp.DspError):
-            _draft_all(inp, rd, 1.0, 0, flags=dsp.DSP_DRAFT_PERSISTENT)
+            _draft_all(inp, rd, 1.0, 0, flags=dsp.DSP_PATH_PERSISTENT)
         _draft_all(inp, rd, 1.0, 0)
+        with pytest.raises(dsp.DspError):
+            rd.verify(inp, 1.0, SEED, 0, flags=dsp.DSP_PATH_PERSISTENT)
+        rd.verify(inp, 1.0, SEED, 0)
+        torch.cuda.synchronize()
 
 
 def test_tiny_workload_1000_rounds():

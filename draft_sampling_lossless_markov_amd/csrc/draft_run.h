@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
             }
         };
         // base words of this lane's request: its two 8-column words of each unit
-        constexpr int RING = (TU >= 4) ? 1 : 2;
+        constexpr int RING = (TU >= 5) ? 1 : 2;
         uint4 bw[RING][TU][2];
         auto load_base = [&](int n0, auto SL) {
             constexpr int sl = decltype(SL)::value % RING;

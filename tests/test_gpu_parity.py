@@ -153,6 +153,9 @@ PATH_CASES = [
     (17, 3, 100000, 200, 0.0),    # 4 units (one in LDS); r not a multiple of 16
     (9, 4, 160000, 256, 1.0),     # 5 units (two in LDS), 250 workgroups
     (9, 4, 160000, 256, 0.0),
+    (130, 2, 80000, 64, 0.8),     # 3 units, five request blocks through the base-word ring
+    (100, 2, 110000, 256, 1.0),   # 4 units, four request blocks
+    (100, 2, 110000, 256, 0.0),
 ]
 
 
@@ -192,8 +195,11 @@ def test_draft_paths_vs_oracle(case):
                                                 np_(inp_cpu["anchor"]), S, temp, SEED, rnd)
         for name, (tok, q, st) in (("persistent", pers), ("streaming", strm)):
             t, _ = compare_draft(tok, q, st, o_tok, o_q, o_stats, o_flag, greedy, S)
+            # every differing draw lies within 1e-6 of a boundary of the oracle's CDF
+            # (t.ok()); their count stays within 1e-3 of the draws, or two in a case
+            # this small
             assert t.ok(), (name, t.summary())
-            assert t.mismatch_rate() <= 1e-3, (name, t.summary())
+            assert t.diverged <= max(2, 1e-3 * t.decisions), (name, t.summary())
         if greedy:
             assert np.array_equal(pers[0], strm[0])
         del rd, inp
@@ -236,7 +242,7 @@ def test_residual_paths_vs_oracle(case):
             g_v = {k: np_(getattr(rd, k)).copy() for k in ("accept", "n_accept", "y", "p")}
             t = compare_verify(g_v, o_v, lens.numpy(), False, S)
             assert t.ok(), (flags, t.summary())
-            assert t.mismatch_rate() <= 1e-3, (flags, t.summary())
+            assert t.diverged <= max(2, 1e-3 * t.decisions), (flags, t.summary())
             ys.append(g_v["y"])
         n_rej = int((ys[0] >= 0).sum())
         _say(f"  {n_rej} draws, paths differ on {int((ys[0] != ys[1]).sum())}")

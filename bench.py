@@ -291,7 +291,7 @@ def main():
         draft_timing = "one graph of K draft calls back to back"
     achieved = call_bytes / draft_avg_s / 1e9
     traffic = profiled_traffic(wl.name, draft_path)
-    kernels = ("draft_run_kernel (one cooperative launch, all gamma positions)"
+    kernels = ("run_clear_kernel + draft_run_kernel (one persistent launch, all gamma positions)"
                if draft_path == "persistent" else
                "bias_pass_kernel + draft_pick_kernel per position")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

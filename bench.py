@@ -133,6 +133,73 @@ def cpu_baseline(wl, inp, temp, budget_s):
                       f"{spent:.1f} s on one host thread"}
 
 
+def cpu_baseline_threads(wl, inp, temp, budget_s):
+    """The same oracle calls, requests sharded over the host threads this process may
+    use, at most 16 (the oracle is plain C called through ctypes, which releases the GIL),
+    on whole requests of set 0: host copies prepared first, wall time measured."""
+    import concurrent.futures as cf
+    import oracle
+    E = oracle.bf16_bits(inp["E"])
+    W2 = oracle.bf16_bits(inp["W2"])
+    anchor = inp["anchor"].cpu().numpy()
+    w, T = inp["w"].cpu().numpy(), inp["T"].cpu().numpy()
+    off = None if inp["offset"] is None else inp["offset"].cpu().numpy()
+    g, R = inp["gamma"], inp["R"]
+    # the host threads this process may use, at most 16 (a GPU's share of its host)
+    threads = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count())
+    n_req = min(R, max(threads, 1) * 4)
+    rows = [(oracle.host_logits(inp["base"][n:n + 1]), oracle.host_logits(inp["target"][n:n + 1]),
+             oracle.bf16_bits(inp["h"][n:n + 1])) for n in range(n_req)]
+
+    def one(n):
+        base, target, h = rows[n]
+        sl = slice(n, n + 1)
+        tok, q, _, _ = oracle.draft(base, E, W2, anchor[sl], np.array([n], np.int32), temp, 0, 0)
+        oracle.confidence(h, E, anchor[sl], tok, w, T, None if off is None else off[sl])
+        oracle.verify(target, base, E, W2, anchor[sl], tok, q, np.array([g], np.int32),
+                      np.array([n], np.int32), temp, 0, 0)
+        return g
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        positions = sum(ex.map(one, range(n_req)))
+    wall = time.perf_counter() - t0
+    return {"value": positions / wall, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"{n_req} of {R} requests of one round of {wl.name} (draft + confidence + "
+                      f"verify of all {g} positions each) sharded over {threads} host threads, "
+                      f"{wall:.1f} s wall"}
+
+
+def host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=5):
+    """Achieved bandwidth of a plain device-to-device copy (bytes read + written per
+    second): the second denominator of the roofline."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +293,7 @@ def main():
     if args.eager:
         ms_per_step = eager_ms_per_step
         timing = "eager launches"
+        round_ms = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(K)])
     else:
         cap = torch.cuda.Stream()
         graphs = []
@@ -237,14 +305,14 @@ def main():
         for gr in graphs[:2]:
             gr.replay()
         torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_start.record(stream)
-        for gr in graphs:
+        t_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        t_ev[0].record(stream)
+        for i, gr in enumerate(graphs):
             gr.replay()
-        t_end.record(stream)
+            t_ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        ms_per_step = t_start.elapsed_time(t_end) / K
+        ms_per_step = t_ev[0].elapsed_time(t_ev[K]) / K
+        round_ms = np.array([t_ev[i].elapsed_time(t_ev[i + 1]) for i in range(K)])
         timing = "HIP graph replay, one graph per round"
 
     # per entry point (event-bracketed) average durations, in ms
@@ -319,10 +387,19 @@ def main():
         "verified_per_round": len_per_round, "drafted_per_round": R * g,
         "timing": timing, "eager_ms_per_step": round(eager_ms_per_step, 5),
         "roofline": roof,
+        "round_us_percentiles": {"p10": round(float(np.percentile(round_ms, 10)) * 1e3, 2),
+                                 "median": round(float(np.median(round_ms)) * 1e3, 2),
+                                 "p90": round(float(np.percentile(round_ms, 90)) * 1e3, 2)},
     }
+    copy_gbs = copy_bandwidth()
+    result["copy_bandwidth"] = {"GBs": round(copy_gbs, 1),
+                                "round_frac_of_copy": round(A / (copy_gbs * 1e9) / (ms_per_step * 1e-3), 4),
+                                "what": "1 GiB device-to-device copy, bytes read + written per second"}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, inp0, temp, args.cpu_seconds)
+        result["cpu_baseline_threads"] = cpu_baseline_threads(wl, inp0, temp, args.cpu_seconds)
+        result["cpu_host"] = {"model": host_cpu(), "threads": len(os.sched_getaffinity(0))}
     print(json.dumps(result), flush=True)
 
 

@@ -31,7 +31,8 @@ from draft_sampling_lossless_markov_amd.workloads import (BENCH_LAYOUT, WORKLOAD
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # sources of the draft-step kernels; the profiled HBM traffic is reported only
 # while they are byte-for-byte the profiled ones
-DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/csrc/draft.hip",
+DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/build.py",
+                 "draft_sampling_lossless_markov_amd/csrc/draft.hip",
                  "draft_sampling_lossless_markov_amd/csrc/draft_run.h",
                  "draft_sampling_lossless_markov_amd/csrc/tile_pass.h",
                  "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",

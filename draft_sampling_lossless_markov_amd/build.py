@@ -23,9 +23,12 @@ def _hipcc():
 
 def _flags(extra=()):
     # packed-fp32 instructions are disabled: the compiler must not form
-    # v_pk_{add,mul,fma}_f32 from scalar fp32 code.
+    # v_pk_{add,mul,fma}_f32 from scalar fp32 code.  MFMA results go to VGPRs
+    # rather than AGPRs: the softmax epilogues read every accumulator with VALU
+    # instructions, and the accumulator moves cost more than the AGPR form saves.
     return [*extra, "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-result"]
 
 

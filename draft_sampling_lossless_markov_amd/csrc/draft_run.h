@@ -497,21 +497,25 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
 #pragma unroll
                     for (int ks = 0; ks < kKSteps; ++ks) bf[ks] = b_frag(ks);
                 }
+                // the wave's units as independent MFMA chains issued side by side
+                // (a wave without a second unit runs its chain on zero fragments)
+                floatx16 acc[NU];
+#pragma unroll
+                for (int j = 0; j < NU; ++j)
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) acc[j][jj] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < kKSteps; ++ks) {
+                    const uint4 bu = kBfHeld ? bf[kBfHeld ? ks : 0] : b_frag(ks);
+#pragma unroll
+                    for (int j = 0; j < NU; ++j) acc[j] = mfma32_bf16(as_bf16x8(af[j][ks]), as_bf16x8(bu), acc[j]);
+                }
 #pragma unroll
                 for (int j = 0; j < NU; ++j) {
                     const int uu = wave + 4 * j;
-                    if (uu < TU) {
-                        floatx16 acc;
+                    if (uu < TU && c32 == 0) {
 #pragma unroll
-                        for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.0f;
-#pragma unroll
-                        for (int ks = 0; ks < kKSteps; ++ks)
-                            acc = mfma32_bf16(as_bf16x8(af[j][ks]),
-                                              as_bf16x8(kBfHeld ? bf[kBfHeld ? ks : 0] : b_frag(ks)), acc);
-                        if (c32 == 0) {
-#pragma unroll
-                            for (int jj = 0; jj < 16; ++jj) L.sh.lg[32 * uu + unit_acc_col(h, jj)] = acc[jj];
-                        }
+                        for (int jj = 0; jj < 16; ++jj) L.sh.lg[32 * uu + unit_acc_col(h, jj)] = acc[j][jj];
                     }
                 }
                 lds_barrier();

@@ -225,24 +225,26 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
                 }
                 if (tid < kRankMax / 8) *reinterpret_cast<uint4*>(L.e_row + 8 * tid) = ev;
                 lds_barrier();
+                // the wave's units as independent MFMA chains issued side by side
+                // (a wave without a second unit runs its chain on zero fragments)
+                floatx16 acc[NU];
+#pragma unroll
+                for (int j = 0; j < NU; ++j)
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) acc[j][jj] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < kKSteps; ++ks) {
+                    const uint4 bu = (c32 == 0) ? *reinterpret_cast<const uint4*>(L.e_row + ks * kKStep + 8 * h)
+                                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < NU; ++j) acc[j] = mfma32_bf16(as_bf16x8(af[j][ks]), as_bf16x8(bu), acc[j]);
+                }
 #pragma unroll
                 for (int j = 0; j < NU; ++j) {
                     const int uu = wave + 4 * j;
-                    if (uu < TU) {
-                        floatx16 acc;
+                    if (uu < TU && c32 == 0) {
 #pragma unroll
-                        for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.0f;
-#pragma unroll
-                        for (int ks = 0; ks < kKSteps; ++ks) {
-                            const uint4 bu = (c32 == 0)
-                                                 ? *reinterpret_cast<const uint4*>(L.e_row + ks * kKStep + 8 * h)
-                                                 : make_uint4(0, 0, 0, 0);
-                            acc = mfma32_bf16(as_bf16x8(af[j][ks]), as_bf16x8(bu), acc);
-                        }
-                        if (c32 == 0) {
-#pragma unroll
-                            for (int jj = 0; jj < 16; ++jj) L.sh.lg[32 * uu + unit_acc_col(h, jj)] = acc[jj];
-                        }
+                        for (int jj = 0; jj < 16; ++jj) L.sh.lg[32 * uu + unit_acc_col(h, jj)] = acc[j][jj];
                     }
                 }
                 lds_barrier();

@@ -2,7 +2,10 @@
 
 One step = one decode round over a batch of synthetic inputs already resident in
 HBM: dsp_draft_step (all gamma positions), dsp_confidence, dsp_schedule, dsp_verify, issued
-back to back on one stream.  The throughput (`value`) times K rounds replayed
+back to back on one stream.  A workload without scheduling (every position verified)
+has no consumer for the confidence head: its round is dsp_draft_step + dsp_verify with
+l_r = gamma set once, and dsp_confidence and dsp_schedule are timed in a loop of their
+own for the per-entry-point breakdown.  The throughput (`value`) times K rounds replayed
 from HIP graphs, one graph captured per round (its own round index and input
 set), so kernel launch gaps are not counted; a second, eager pass over the same
 K rounds times every entry point with HIP events on the launch stream and gives
@@ -50,11 +53,13 @@ def log(*a):
 def round_bytes(wl, inp, len_sum, n_rej, greedy):
     """Algorithmic HBM bytes of one round: logit rows streamed once (draft base
     rows, verified and bonus target rows, the p and base rows re-read for each
-    residual draw), W2 once, hidden states and embedding rows once."""
+    residual draw), W2 once, hidden states (read by the confidence head, only
+    where a scheduler consumes it) and embedding rows once."""
     s = inp["base"].element_size()
     R, g, V, r, d = inp["R"], inp["gamma"], inp["V"], inp["r"], inp["d"]
     rows = R * g + (R + len_sum) + (0 if greedy else 2 * n_rej)
-    return s * V * rows + 2 * r * V + 2 * R * g * (d + r)
+    hid = d if wl.mode != 0 else 0
+    return s * V * rows + 2 * r * V + 2 * R * g * (hid + r)
 
 
 def draft_call_bytes(inp):
@@ -103,6 +108,11 @@ def profiled_traffic(workload, path):
     return int(kv["draft_call_bytes"])
 
 
+def steps_of(wl):
+    """The entry points of one round of workload wl."""
+    return "draft + confidence + verify" if wl.mode != 0 else "draft + verify"
+
+
 def cpu_baseline(wl, inp, temp, budget_s):
     """The oracle as it stands, one thread, on whole requests of set 0 until about
     budget_s seconds of CPU work; every position of a sampled request verified."""
@@ -122,7 +132,8 @@ def cpu_baseline(wl, inp, temp, budget_s):
         h = oracle.bf16_bits(inp["h"][sl])
         t0 = time.perf_counter()
         tok, q, _, _ = oracle.draft(base, E, W2, anchor[sl], np.array([n], np.int32), temp, 0, 0)
-        oracle.confidence(h, E, anchor[sl], tok, w, T, None if off is None else off[sl])
+        if wl.mode != 0:
+            oracle.confidence(h, E, anchor[sl], tok, w, T, None if off is None else off[sl])
         oracle.verify(target, base, E, W2, anchor[sl], tok, q, np.array([g], np.int32),
                       np.array([n], np.int32), temp, 0, 0)
         spent += time.perf_counter() - t0
@@ -130,7 +141,7 @@ def cpu_baseline(wl, inp, temp, budget_s):
         positions += g
     return {"value": positions / spent, "unit": UNIT, "cores": 1, "kind": "oracle",
             "sample": f"{done} of {inp['R']} requests of one round of {wl.name} "
-                      f"(draft + confidence + verify of all {g} positions each), "
+                      f"({steps_of(wl)} of all {g} positions each), "
                       f"{spent:.1f} s on one host thread"}
 
 
@@ -156,7 +167,8 @@ def cpu_baseline_threads(wl, inp, temp, budget_s):
         base, target, h = rows[n]
         sl = slice(n, n + 1)
         tok, q, _, _ = oracle.draft(base, E, W2, anchor[sl], np.array([n], np.int32), temp, 0, 0)
-        oracle.confidence(h, E, anchor[sl], tok, w, T, None if off is None else off[sl])
+        if wl.mode != 0:
+            oracle.confidence(h, E, anchor[sl], tok, w, T, None if off is None else off[sl])
         oracle.verify(target, base, E, W2, anchor[sl], tok, q, np.array([g], np.int32),
                       np.array([n], np.int32), temp, 0, 0)
         return g
@@ -166,8 +178,8 @@ def cpu_baseline_threads(wl, inp, temp, budget_s):
         positions = sum(ex.map(one, range(n_req)))
     wall = time.perf_counter() - t0
     return {"value": positions / wall, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": f"{n_req} of {R} requests of one round of {wl.name} (draft + confidence + "
-                      f"verify of all {g} positions each) sharded over {threads} host threads, "
+            "sample": f"{n_req} of {R} requests of one round of {wl.name} ({steps_of(wl)} "
+                      f"of all {g} positions each) sharded over {threads} host threads, "
                       f"{wall:.1f} s wall"}
 
 
@@ -253,6 +265,12 @@ def main():
         dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
                            rd.stats, 0, temp, seed, i, rd.ws_draft, s, n_steps=g, flags=flags)
 
+    # with the scheduler off every position is verified: l_r = gamma, set once
+    scheduled = wl.mode != 0
+    if not scheduled:
+        rd.schedule(inp0)
+        torch.cuda.synchronize()
+
     def one_round(i, ev=None, s=stream):
         inp = sets[i % len(sets)]
         if ev is not None:
@@ -260,10 +278,12 @@ def main():
         draft(i, s)
         if ev is not None:
             ev[1].record(s)
-        rd.confidence(inp, s)
+        if scheduled:
+            rd.confidence(inp, s)
         if ev is not None:
             ev[2].record(s)
-        rd.schedule(inp, stream=s)
+        if scheduled:
+            rd.schedule(inp, stream=s)
         if ev is not None:
             ev[3].record(s)
         rd.verify(inp, temp, seed, i, s)
@@ -321,6 +341,20 @@ def main():
     conf_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
     sched_ms = np.array([evs[i][2].elapsed_time(evs[i][3]) for i in range(K)])
     ver_ms = np.array([evs[i][3].elapsed_time(evs[i][4]) for i in range(K)])
+    if not scheduled:
+        # not in the round: timed in a loop of their own (the schedule in the
+        # workload's mode, which sets l_r = gamma again)
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for i in range(K):
+            inp = sets[(args.warmup + i) % len(sets)]
+            ce[i][0].record(stream)
+            rd.confidence(inp, stream)
+            ce[i][1].record(stream)
+            rd.schedule(inp, stream=stream)
+            ce[i][2].record(stream)
+        torch.cuda.synchronize()
+        conf_ms = np.array([ce[i][0].elapsed_time(ce[i][1]) for i in range(K)])
+        sched_ms = np.array([ce[i][1].elapsed_time(ce[i][2]) for i in range(K)])
 
     # replay the timed rounds (deterministic) to count verified positions
     len_sum = rej = 0
@@ -376,12 +410,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "R": R, "gamma": g, "V": V, "r": r, "d": inp0["d"],
                    "mode": mode, "scheduler": "on" if wl.mode == 1 else "off (every position verified)",
+                   "round": ("dsp_draft_step + dsp_confidence + dsp_schedule + dsp_verify" if scheduled
+                             else "dsp_draft_step + dsp_verify (no scheduler: the confidence head has "
+                                  "no consumer; l_r = gamma)"),
                    "base_layout": BENCH_LAYOUT + "-major [gamma, R, V]",
                    "draft_path": draft_path,
                    "parallelism": "single GPU"},
         "round_roofline": {"algorithmic_bytes": int(A), "t_roof_us": round(A / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                            "frac": round(A / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)},
-        "entry_points_us": {"draft_step_all_positions": round(float(draft_ms.mean()) * 1e3, 2),
+        "entry_points_us": {"in_round": (["draft_step_all_positions", "confidence", "schedule", "verify"]
+                                         if scheduled else ["draft_step_all_positions", "verify"]),
+                            "draft_step_all_positions": round(float(draft_ms.mean()) * 1e3, 2),
                             "confidence": round(float(conf_ms.mean()) * 1e3, 2),
                             "schedule": round(float(sched_ms.mean()) * 1e3, 2),
                             "verify": round(float(ver_ms.mean()) * 1e3, 2)},

@@ -76,50 +76,85 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
     const float itL = fold_itl(a.inv_temp);
     const int prow = unit_row_col(c32);
 
-    bf16x8 afrag[NR][kKSteps];
-    stage_w2_slice<TU, NR>(a.W2, V, r, v_tile, L.w2[wave], afrag);
-
     // ================= phase 1: residual mass of every (queued request, tile) ====
+    // Loads run ahead so that no block waits on a chain of them: the queue entries
+    // two blocks ahead, the rows and embedding rows (which need the entries) one
+    // block ahead, under the MFMAs of the block before (two-slot register rings).
     const int count = *a.count;
     const int srow = tid & 31, sq = tid >> 5;
-    for (int n0 = 0; n0 < count; n0 += kPassBlock) {
-        // embedding rows of the tokens before the block's rejections
-        uint4 eu[4];
-        {
-            const int e = n0 + srow;
-            const int p = (e < count) ? a.list_prev[e] : -1;
-            const bool pok = p >= 0 && p < V;
+    // queue entries of a block: this lane's request and rejection (row c32) and
+    // the token before the rejection of row srow
+    int qn[2], qm[2], qp[2];
+    auto load_entries = [&](int n0, auto SL) {
+        constexpr int sl = decltype(SL)::value & 1;
+        const int ee = n0 + c32, e = n0 + srow;
+        qn[sl] = (ee < count) ? a.list[ee] : 0;
+        qm[sl] = (ee < count) ? a.list_m[ee] : 0;
+        qp[sl] = (e < count) ? a.list_prev[e] : -1;
+    };
+    // embedding rows of the tokens before the block's rejections
+    uint4 eu[4];
+    auto load_e = [&](int p) {
+        const bool pok = p >= 0 && p < V;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int kk = (sq * 4 + c) * 8;
-                eu[c] = (pok && kk < r) ? *reinterpret_cast<const uint4*>(a.E + (int64_t)p * r + kk)
-                                        : make_uint4(0, 0, 0, 0);
-            }
+        for (int c = 0; c < 4; ++c) {
+            const int kk = (sq * 4 + c) * 8;
+            eu[c] = (pok && kk < r) ? *reinterpret_cast<const uint4*>(a.E + (int64_t)p * r + kk)
+                                    : make_uint4(0, 0, 0, 0);
         }
-        // this lane's queue entry: its draft and target words, its row statistics
-        const int ee = n0 + c32;
-        const bool ok = ee < count;
-        const int n = ok ? a.list[ee] : 0;
-        const int m = ok ? a.list_m[ee] : 0;
+    };
+    // this lane's draft and target words, its row statistics (two slots up to
+    // four units per wave; at five the registers hold one, and the next block's
+    // rows are requested after this block's epilogue)
+    constexpr int RING = (TU >= 5) ? 1 : 2;
+    uint4 dw[RING][TU][2], xw[RING][TU][2];
+    float Md[RING], invZd[RING], Mt[RING], invZt[RING];
+    auto load_rows = [&](int n0, int n, int m, auto SL) {
+        constexpr int sl = decltype(SL)::value % RING;
+        const bool ok = n0 + c32 < count;
         const uint16_t* drow = a.base + (int64_t)n * a.bs.rs + (int64_t)m * a.bs.ps;
         const uint16_t* trow = a.target + (int64_t)n * a.ts.rs + (int64_t)m * a.ts.ps;
-        uint4 dw[TU][2], xw[TU][2];
 #pragma unroll
         for (int u = 0; u < TU; ++u)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
-                load8_any<uint16_t, true>(drow, v0, V, ok, v0 + 8 <= V, &dw[u][c]);
-                load8_any<uint16_t, true>(trow, v0, V, ok, v0 + 8 <= V, &xw[u][c]);
+                load8_any<uint16_t, true>(drow, v0, V, ok, v0 + 8 <= V, &dw[sl][u][c]);
+                load8_any<uint16_t, true>(trow, v0, V, ok, v0 + 8 <= V, &xw[sl][u][c]);
             }
-        const float Md = ok ? (float)a.stats[2 * ((int64_t)n * gamma + m)] : 0.0f;
-        const float invZd = ok ? (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]) : 0.0f;
-        const float Mt = ok ? a.row_m[n] : 0.0f;
-        const float invZt = ok ? (float)(1.0 / a.row_z[n]) : 0.0f;
+        Md[sl] = ok ? (float)a.stats[2 * ((int64_t)n * gamma + m)] : 0.0f;
+        invZd[sl] = ok ? (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]) : 0.0f;
+        Mt[sl] = ok ? a.row_m[n] : 0.0f;
+        invZt[sl] = ok ? (float)(1.0 / a.row_z[n]) : 0.0f;
+    };
+    load_entries(0, std::integral_constant<int, 0>{});
+    load_entries(kPassBlock, std::integral_constant<int, 1>{});
+
+    bf16x8 afrag[NR][kKSteps];
+    stage_w2_slice<TU, NR>(a.W2, V, r, v_tile, L.w2[wave], afrag);
+
+    if (count > 0) {
+        load_e(qp[0]);
+        load_rows(0, qn[0], qm[0], std::integral_constant<int, 0>{});
+    }
+
+    auto block = [&](int n0, auto SL) {
+        constexpr int sl = decltype(SL)::value % RING;
+        const int ee = n0 + c32;
+        const bool ok = ee < count;
         lds_barrier();   // the previous block's embedding tile is read
 #pragma unroll
         for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&L.e[srow][(sq * 4 + c) * 8]) = eu[c];
         lds_barrier();
+        constexpr int qs = decltype(SL)::value & 1;   // entry slot of this block
+        if (n0 + kPassBlock < count) {
+            // block b + 1 from the entries in slot qs ^ 1; then block b + 2's
+            // entries into slot qs (this block's are used up)
+            load_e(qp[qs ^ 1]);
+            if constexpr (RING == 2)
+                load_rows(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, sl ^ 1>{});
+            if (n0 + 2 * kPassBlock < count) load_entries(n0 + 2 * kPassBlock, std::integral_constant<int, qs>{});
+        }
 
         floatx16 acc[TU];
 #pragma unroll
@@ -144,13 +179,21 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
         for (int u = 0; u < TU; ++u)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float zd = Logit<uint16_t>::raw_at(&dw[u][j >> 3], j & 7) + acc[u][j];
-                const float xt = Logit<uint16_t>::raw_at(&xw[u][j >> 3], j & 7);
-                d4[j & 3] += fmaxf(wexp(xt - Mt, itL) * invZt - wexp(zd - Md, itL) * invZd, 0.0f);
+                const float zd = Logit<uint16_t>::raw_at(&dw[sl][u][j >> 3], j & 7) + acc[u][j];
+                const float xt = Logit<uint16_t>::raw_at(&xw[sl][u][j >> 3], j & 7);
+                d4[j & 3] += fmaxf(wexp(xt - Mt[sl], itL) * invZt[sl] - wexp(zd - Md[sl], itL) * invZd[sl], 0.0f);
             }
         const double sum = xsum<32>((double)((d4[0] + d4[1]) + (d4[2] + d4[3])));
         if (h == 0 && ok && tw < n_t)
             dev_store_u64(a.slots + (int64_t)ee * n_t + tw, (uint64_t)__double_as_longlong(sum));
+        if constexpr (RING == 1) {
+            if (n0 + kPassBlock < count)
+                load_rows(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, 0>{});
+        }
+    };
+    for (int n0 = 0; n0 < count; n0 += 2 * kPassBlock) {
+        block(n0, std::integral_constant<int, 0>{});
+        if (n0 + kPassBlock < count) block(n0 + kPassBlock, std::integral_constant<int, 1>{});
     }
 
     // ================= phase 2: one workgroup per request ======================

@@ -156,6 +156,7 @@ PATH_CASES = [
     (130, 2, 80000, 64, 0.8),     # 3 units, five request blocks through the base-word ring
     (100, 2, 110000, 256, 1.0),   # 4 units, four request blocks
     (100, 2, 110000, 256, 0.0),
+    (110, 2, 152000, 64, 1.0),    # 5 units, four request blocks through one-slot rings
 ]
 
 

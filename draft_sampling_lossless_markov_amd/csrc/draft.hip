@@ -291,7 +291,9 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
     ra.round = round; ra.n_t = n_t;
     ra.slots = static_cast<uint64_t*>(ws);
     ra.ctl = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + draft_part_bytes(R, V));
-    const int G = (n_t + 3) / 4;
+    // one workgroup per request where CUs are free beyond the tile workgroups:
+    // no workgroup then draws two requests of a position
+    const int G = std::max((n_t + 3) / 4, std::min(R, geo.ncu));
 #define DSP_RUN(TU)                                                                            \
     return greedy ? launch_run_t<true, TU>(ra, G, geo.ncu, s, launched)                        \
                   : launch_run_t<false, TU>(ra, G, geo.ncu, s, launched)

@@ -194,9 +194,12 @@ __device__ __forceinline__ void stage_w2_slice(const uint16_t* __restrict__ W2, 
 }
 
 // ---------------------------------------------------------------------------
-// draft_run_kernel: grid ceil(n_t / 4) (at most one workgroup per CU), 256
-// threads; wave w owns tile 4 blockIdx.x + w, i.e. the 32 TU columns from
-// 32 TU (4 blockIdx.x + w).  Lane l holds request l % 32 of a 32-request block.
+// draft_run_kernel: grid max(ceil(n_t / 4), min(R, CUs)) (at most one workgroup
+// per CU), 256 threads; wave w owns tile 4 blockIdx.x + w, i.e. the 32 TU columns
+// from 32 TU (4 blockIdx.x + w).  Workgroups past the tiles (added so that no
+// workgroup draws two requests of a position where CUs are free) run phase 1 on
+// empty tiles -- guarded loads, no HBM traffic, no partials written -- and pick.
+// Lane l holds request l % 32 of a 32-request block.
 // ---------------------------------------------------------------------------
 template <bool GREEDY, int TU>
 __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)

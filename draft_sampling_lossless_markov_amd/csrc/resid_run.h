@@ -13,7 +13,9 @@
 //     of 32: q_m rebuilt by MFMA from the resident slice plus the base logits,
 //     the target row added, sum over each tile of max(0, p - q) written to the
 //     request's slot (fp64 bits) -- verify_accept marked the slots empty;
-//   phase 2: workgroup n mod G draws request n: waits for its slots, combines
+//   phase 2: workgroup n mod G draws request n (the grid has one workgroup per
+//     request where CUs are free beyond the tiles; those past the tiles run
+//     phase 1 on empty tiles, writing nothing): waits for its slots, combines
 //     them, locates the tile, rebuilds its residual with the same arithmetic
 //     as verify_pick and scans it; without a rejection (or with no residual
 //     mass) it draws from target row l (or m) through verify_rows' partials.

@@ -505,7 +505,9 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
             ra.count = ws.resid_cnt; ra.list = ws.resid_list; ra.list_m = ws.resid_m;
             ra.list_prev = ws.resid_prev; ra.slot_of = ws.resid_slot; ra.row_m = ws.row_m;
             ra.row_z = ws.row_z; ra.rowpart = ws.rowpart; ra.slots = ws.run_slots; ra.ctl = ws.run_ctl;
-            const int G = (geo.n_t + 3) / 4;
+            // one workgroup per request where CUs are free beyond the tile
+            // workgroups (those past the tiles run phase 1 on empty tiles)
+            const int G = std::max((geo.n_t + 3) / 4, std::min(R, geo.ncu));
             bool launched = false;
             hipError_t e = hipSuccess;
             switch (geo.tu) {

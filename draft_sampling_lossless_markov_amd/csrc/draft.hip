@@ -63,7 +63,6 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
         }
         return;
     } else {
-        __shared__ PassLds L;
         __shared__ __attribute__((aligned(16))) uint16_t e_row[kRankMax];
         const int prev = prev_token(anchor, tok, n, gamma, k, V);   // issued early
         float mt[PER];
@@ -101,7 +100,7 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
             if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
             *reinterpret_cast<uint4*>(e_row + kk) = ev;
         }
-        const float z = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, L, sh);
+        const float z = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, sh);
         double e1[1] = {(v < V) ? (double)wexp(z - M, fold_itl(inv_temp)) : 0.0};
         double b2;
         const int loc = block_locate<1>(e1, target - before, &b2, sh, 1);

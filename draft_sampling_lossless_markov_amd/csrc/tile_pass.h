@@ -158,7 +158,8 @@ __device__ __forceinline__ int w2_slot(int rho, int c) { return c ^ ((rho & 31) 
 // The A fragments of the workgroup's 256-row W2 tile (rows v0 .. v0 + 255; wave w
 // takes rows 64 w .. 64 w + 63): each 64-row quarter is read contiguously (a
 // wave instruction covers two whole rows) into LDS, then the owning wave reads
-// its fragments.  Same values as load_w2_frags, at the streaming rate of W2.
+// its fragments.  Same values as the direct loads of tile_logit, at the
+// streaming rate of W2.
 __device__ __forceinline__ void stage_w2_frags(const uint16_t* __restrict__ W2, int V, int r,
                                                int v0, PassLds& L, bf16x8 a[2][kKSteps])
 {
@@ -547,20 +548,33 @@ __device__ __forceinline__ int block_locate(const double (&w)[PER], double targe
     return l < 0 ? 0 : l;
 }
 
+
 // One request's logits over the 256-wide tile at v0 (thread t: column v0 + t),
-// bit-identical to the bias pass: W2 fragments staged as there, the request's
-// embedding row in column 0 of the N-tile, the same MFMA sequence from zero,
-// then the base logit added.  xb: the thread's base logit (-inf past V), loaded
-// by the caller as early as it likes; e_row: the embedding row (zeros when prev
-// selects none), in LDS and visible after the staging's first barrier.
+// bit-identical to the bias pass (same W2 fragments, same MFMA sequence, the
+// request in column 0 of the N-tile), then the base logit added.  xb: the
+// thread's base logit (-inf past V); e_row: the embedding row in LDS (zeros
+// when the previous token selects none), written before the call.  The A
+// fragments are loaded straight from W2 into registers:
+// wave w's rows v0 + 64 w + a_row_voff(t, i), k-steps 16 ks + 8 h.  Addresses
+// are clamped into the rows and the loads issued unconditionally: a clamped
+// row (past V) only feeds columns whose base logit is -inf, and a clamped
+// k-step (past r) meets zeros of the embedding row, so the products are those
+// of the staged fragments.
 __device__ __forceinline__ float tile_logit(const uint16_t* __restrict__ W2, int V, int r, int v0,
-                                            const uint16_t* e_row, float xb, PassLds& L,
-                                            PickScratch& sh)
+                                            const uint16_t* e_row, float xb, PickScratch& sh)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int h = lane >> 5, c32 = lane & 31;
-    bf16x8 afrag[2][kKSteps];
-    stage_w2_frags(W2, V, r, v0, L, afrag);
+    uint4 af[2][kKSteps];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int v = v0 + 64 * wave + a_row_voff(t, c32);
+        const uint16_t* wrow = W2 + (int64_t)min(v, V - 1) * r;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks)
+            af[t][ks] = *reinterpret_cast<const uint4*>(wrow + min(ks * kKStep + 8 * h, r - 8));
+    }
+    lds_barrier();   // e_row is written
     floatx16 acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -572,7 +586,7 @@ __device__ __forceinline__ float tile_logit(const uint16_t* __restrict__ W2, int
         if (c32 == 0) u = *reinterpret_cast<const uint4*>(e_row + ks * kKStep + 8 * h);
         const bf16x8 bv = as_bf16x8(u);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma32_bf16(afrag[t][ks], bv, acc[t]);
+        for (int t = 0; t < 2; ++t) acc[t] = mfma32_bf16(as_bf16x8(af[t][ks]), bv, acc[t]);
     }
     if (c32 == 0) {
 #pragma unroll

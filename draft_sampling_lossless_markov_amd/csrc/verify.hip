@@ -305,7 +305,6 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     uint32_t round, int n_vt, VerifyWs ws)
 {
     __shared__ PickScratch sh;
-    __shared__ PassLds L;
     __shared__ __attribute__((aligned(16))) uint16_t e_row[kRankMax];
     const int n = blockIdx.x;
     const int tid = threadIdx.x;
@@ -348,7 +347,7 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
                 if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
                 *reinterpret_cast<uint4*>(e_row + kk) = ev;
             }
-            const float zd = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, L, sh);
+            const float zd = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, sh);
             double rho[1] = {0.0};
             if (v < V && zd != -INFINITY) {
                 const double pv = (double)wexp(xt - Mt, itL) * invZt;

@@ -131,11 +131,12 @@ static size_t draft_part_bytes(int R, int V)
 size_t draft_workspace_bytes(int R, int V) { return draft_part_bytes(R, V) + kRunCtlBytes; }
 
 // requests per workgroup of a bias pass: whole 64-request blocks, split into
-// balanced chunks so the grid has about 2048 workgroups
+// balanced chunks so the grid has about 1024 workgroups (two rounds at two per
+// CU; every chunk re-reads its W2 tile, so fewer chunks move fewer bytes)
 int pass_req_per_wg(int count_max, int n_vt)
 {
     const int blocks = (count_max + kReqBlock - 1) / kReqBlock;
-    const int want = std::max(1, std::min(blocks, (2048 + n_vt - 1) / n_vt));
+    const int want = std::max(1, std::min(blocks, (1024 + n_vt - 1) / n_vt));
     return ((blocks + want - 1) / want) * kReqBlock;
 }
 

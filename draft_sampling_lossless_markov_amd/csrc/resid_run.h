@@ -105,29 +105,45 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
                                     : make_uint4(0, 0, 0, 0);
         }
     };
-    // this lane's draft and target words, its row statistics (two slots up to
-    // four units per wave; at five the registers hold one, and the next block's
-    // rows are requested after this block's epilogue)
-    constexpr int RING = (TU >= 5) ? 1 : 2;
-    uint4 dw[RING][TU][2], xw[RING][TU][2];
+    // this lane's target and draft words, its row statistics: two slots of each
+    // up to four units per wave; at five the registers hold two slots of target
+    // words but one of draft words, so the next block's draft words are requested
+    // after this block's epilogue
+    constexpr int RING = 2;                      // target words, statistics
+    constexpr int RING_D = (TU >= 5) ? 1 : 2;    // draft words
+    uint4 dw[RING_D][TU][2], xw[RING][TU][2];
     float Md[RING], invZd[RING], Mt[RING], invZt[RING];
-    auto load_rows = [&](int n0, int n, int m, auto SL) {
+    auto load_target = [&](int n0, int n, int m, auto SL) {
         constexpr int sl = decltype(SL)::value % RING;
         const bool ok = n0 + c32 < count;
-        const uint16_t* drow = a.base + (int64_t)n * a.bs.rs + (int64_t)m * a.bs.ps;
         const uint16_t* trow = a.target + (int64_t)n * a.ts.rs + (int64_t)m * a.ts.ps;
 #pragma unroll
         for (int u = 0; u < TU; ++u)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
-                load8_any<uint16_t, true>(drow, v0, V, ok, v0 + 8 <= V, &dw[sl][u][c]);
                 load8_any<uint16_t, true>(trow, v0, V, ok, v0 + 8 <= V, &xw[sl][u][c]);
             }
         Md[sl] = ok ? (float)a.stats[2 * ((int64_t)n * gamma + m)] : 0.0f;
         invZd[sl] = ok ? (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]) : 0.0f;
         Mt[sl] = ok ? a.row_m[n] : 0.0f;
         invZt[sl] = ok ? (float)(1.0 / a.row_z[n]) : 0.0f;
+    };
+    auto load_draft = [&](int n0, int n, int m, auto SL) {
+        constexpr int sl = decltype(SL)::value % RING_D;
+        const bool ok = n0 + c32 < count;
+        const uint16_t* drow = a.base + (int64_t)n * a.bs.rs + (int64_t)m * a.bs.ps;
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
+                load8_any<uint16_t, true>(drow, v0, V, ok, v0 + 8 <= V, &dw[sl][u][c]);
+            }
+    };
+    auto load_rows = [&](int n0, int n, int m, auto SL) {
+        load_draft(n0, n, m, SL);
+        load_target(n0, n, m, SL);
     };
     load_entries(0, std::integral_constant<int, 0>{});
     load_entries(kPassBlock, std::integral_constant<int, 1>{});
@@ -153,8 +169,9 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
             // block b + 1 from the entries in slot qs ^ 1; then block b + 2's
             // entries into slot qs (this block's are used up)
             load_e(qp[qs ^ 1]);
-            if constexpr (RING == 2)
-                load_rows(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, sl ^ 1>{});
+            load_target(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, sl ^ 1>{});
+            if constexpr (RING_D == 2)
+                load_draft(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, sl ^ 1>{});
             if (n0 + 2 * kPassBlock < count) load_entries(n0 + 2 * kPassBlock, std::integral_constant<int, qs>{});
         }
 
@@ -181,16 +198,16 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
         for (int u = 0; u < TU; ++u)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float zd = Logit<uint16_t>::raw_at(&dw[sl][u][j >> 3], j & 7) + acc[u][j];
+                const float zd = Logit<uint16_t>::raw_at(&dw[sl % RING_D][u][j >> 3], j & 7) + acc[u][j];
                 const float xt = Logit<uint16_t>::raw_at(&xw[sl][u][j >> 3], j & 7);
                 d4[j & 3] += fmaxf(wexp(xt - Mt[sl], itL) * invZt[sl] - wexp(zd - Md[sl], itL) * invZd[sl], 0.0f);
             }
         const double sum = xsum<32>((double)((d4[0] + d4[1]) + (d4[2] + d4[3])));
         if (h == 0 && ok && tw < n_t)
             dev_store_u64(a.slots + (int64_t)ee * n_t + tw, (uint64_t)__double_as_longlong(sum));
-        if constexpr (RING == 1) {
+        if constexpr (RING_D == 1) {
             if (n0 + kPassBlock < count)
-                load_rows(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, 0>{});
+                load_draft(n0 + kPassBlock, qn[qs ^ 1], qm[qs ^ 1], std::integral_constant<int, 0>{});
         }
     };
     for (int n0 = 0; n0 < count; n0 += 2 * kPassBlock) {

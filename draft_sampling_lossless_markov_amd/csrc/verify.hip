@@ -203,14 +203,26 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
     __shared__ float m_s[kGammaMax + 1];
     __shared__ double z_s[kGammaMax + 1];
     __shared__ int am_s[kGammaMax + 1];
+    __shared__ int tk_s[kGammaMax + 1];
     const int n = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l = clamp_len(len, n, gamma);
     const int np = 4 * ((n_vt + kSpanTiles - 1) / kSpanTiles);
     const Part* rows = ws.spanpart + (int64_t)n * (gamma + 1) * np;
     const int last_row = GREEDY ? l : l - 1;
+    const int anchor_n = (!GREEDY && tid == 0) ? anchor[n] : 0;   // x_{-1}, for the queue
     for (int j = wave; j <= last_row; j += 4) {
         const Part* pp = rows + (int64_t)j * np;
+        // the accept test's inputs, requested with the row's partials (sampling:
+        // j < l here, so (n, j) is a drafted position)
+        const int64_t o = (int64_t)n * gamma + j;
+        float zx_j = 0.0f, q_j = 0.0f;
+        int tk_j = 0;
+        if constexpr (!GREEDY) {
+            zx_j = ws.zx[o];
+            q_j = q[o];
+            tk_j = tok[o];
+        }
         Part pt[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -241,10 +253,10 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
                 if (pt[i].m != -INFINITY) Z += pt[i].s * exp(((double)pt[i].m - (double)M) * (double)inv_temp);
             Z = wave_sum_d(Z);
             if (lane == 0) {
-                const int64_t o = (int64_t)n * gamma + j;
-                const double p = exp(((double)ws.zx[o] - (double)M) * (double)inv_temp) / Z;
+                const double p = exp(((double)zx_j - (double)M) * (double)inv_temp) / Z;
                 const double u = uniform24(seed, round, (uint32_t)n, (uint32_t)j, 1u);
-                acc_s[j] = (u * (double)q[o] <= p);
+                acc_s[j] = (u * (double)q_j <= p);
+                tk_s[j] = tk_j;
                 pj_s[j] = (float)p;
                 m_s[j] = M;
                 z_s[j] = Z;
@@ -271,7 +283,9 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
                 slot_s = slot;
                 ws.resid_list[slot] = n;
                 ws.resid_m[slot] = nacc;
-                ws.resid_prev[slot] = prev_token(anchor, tok, n, gamma, nacc, V);
+                // the token before the rejection (drafted positions j < l are in tk_s)
+                const int pv = (nacc == 0) ? anchor_n : tk_s[nacc - 1];
+                ws.resid_prev[slot] = (pv >= 0 && pv < V) ? pv : -1;
                 ws.resid_slot[n] = slot;
                 ws.row_m[n] = m_s[nacc];
                 ws.row_z[n] = z_s[nacc];

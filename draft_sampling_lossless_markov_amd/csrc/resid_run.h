@@ -271,6 +271,11 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
                 const bool vin = tid < 32 * TU && v < V;
                 const float xb = vin ? Logit<uint16_t>::at(drow, v) : -INFINITY;
                 const float xt = vin ? Logit<uint16_t>::at(trow, v) : -INFINITY;
+                // the rows' statistics, requested with the tile's words
+                const double sd0 = a.stats[2 * ((int64_t)n * gamma + m)];
+                const double sd1 = a.stats[2 * ((int64_t)n * gamma + m) + 1];
+                const float Mt = a.row_m[n];
+                const double zt = a.row_z[n];
                 constexpr int NU = (TU + 3) / 4;
                 uint4 af[NU][kKSteps];
 #pragma unroll
@@ -310,10 +315,9 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
                     }
                 }
                 lds_barrier();
-                const float Md = (float)a.stats[2 * ((int64_t)n * gamma + m)];
-                const double invZd = 1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1];
-                const float Mt = a.row_m[n];
-                const double invZt = 1.0 / a.row_z[n];
+                const float Md = (float)sd0;
+                const double invZd = 1.0 / sd1;
+                const double invZt = 1.0 / zt;
                 double rho[1] = {0.0};
                 if (vin) {
                     const float zd = xb + L.sh.lg[tid];

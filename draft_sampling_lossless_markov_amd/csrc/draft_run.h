@@ -466,23 +466,24 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 uint4 ev = make_uint4(0, 0, 0, 0);
                 if (tid < kRankMax / 8 && pok && 8 * tid < r)
                     ev = *reinterpret_cast<const uint4*>(a.E + (int64_t)pv * r + 8 * tid);
+                // (the base logit's address clamped into the row and its value
+                // masked where used, so that no wait follows its load; the W2
+                // addresses clamped the same way: a clamped row only feeds masked
+                // columns, a clamped k-step meets zeros of the embedding row)
                 const uint16_t* row = a.base + (int64_t)n * a.bs.rs + (int64_t)k * a.bs.ps;
                 const int v = vt0 + tid;
                 const bool vin = tid < 32 * TU && v < V;
-                const float xb = vin ? Logit<uint16_t>::at(row, v) : -INFINITY;
+                const float xb = Logit<uint16_t>::at(row, min(v, V - 1));
                 constexpr int NU = (TU + 3) / 4;   // units per wave in a rebuild
                 uint4 af[NU][kKSteps];
 #pragma unroll
                 for (int j = 0; j < NU; ++j) {
-                    const int vr = vt0 + 32 * (wave + 4 * j) + prow;
-                    const bool uin = wave + 4 * j < TU && vr < V;
+                    const uint16_t* wrow = a.W2 + (int64_t)min(vt0 + 32 * (wave + 4 * j) + prow, V - 1) * r;
 #pragma unroll
-                    for (int ks = 0; ks < kKSteps; ++ks) {
-                        const int kk = ks * kKStep + 8 * h;
-                        af[j][ks] = (uin && kk < r)
-                                        ? *reinterpret_cast<const uint4*>(a.W2 + (int64_t)vr * r + kk)
+                    for (int ks = 0; ks < kKSteps; ++ks)
+                        af[j][ks] = (wave + 4 * j < TU)   // wave-uniform: the wave has unit j
+                                        ? *reinterpret_cast<const uint4*>(wrow + min(ks * kKStep + 8 * h, r - 8))
                                         : make_uint4(0, 0, 0, 0);
-                    }
                 }
                 if (tid < kRankMax / 8) *reinterpret_cast<uint4*>(L.e_row + 8 * tid) = ev;
                 lds_barrier();

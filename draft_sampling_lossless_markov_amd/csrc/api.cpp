@@ -134,6 +134,8 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
     if (!ws || ws_bytes < need)
         return fail(DSP_ERR_WORKSPACE, "dsp_draft_step: workspace of %zu bytes, %zu needed",
                     ws_bytes, need);
+    if (!aligned16(ws))
+        return fail(DSP_ERR_WORKSPACE, "dsp_draft_step: the workspace must be 16-byte aligned");
     return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
                                              dtype == DSP_BF16, E, W2, anchor, tok, q,
                                              stats, R, gamma, V, r, k, n_steps, (int)flags, temperature,
@@ -211,6 +213,8 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
     if (!ws || ws_bytes < need)
         return fail(DSP_ERR_WORKSPACE, "dsp_verify: workspace of %zu bytes, %zu needed", ws_bytes,
                     need);
+    if (!aligned16(ws))
+        return fail(DSP_ERR_WORKSPACE, "dsp_verify: the workspace must be 16-byte aligned");
     return hip_status(dsp::launch_verify(target, dsp::RowStrides{target_rs, target_ps}, base,
                                          dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16,
                                          (int)flags, E,

@@ -13,7 +13,8 @@
  *     the last index contiguous and no padding, except the logit tensors (base,
  *     target), whose rows are placed by element strides (below).  The library
  *     never allocates or frees memory; scratch comes from a caller workspace
- *     sized by dsp_workspace_size().
+ *     sized by dsp_workspace_size() and 16-byte aligned (DSP_ERR_WORKSPACE
+ *     otherwise; device allocations are).
  *   - Logit rows: element (n, k, v) -- request n, position k, vocabulary id v --
  *     of a logit tensor p with strides (rs, ps) is p[n * rs + k * ps + v]
  *     (strides in elements, >= 0; the vocabulary is contiguous).  A contiguous

@@ -90,6 +90,8 @@ def test_draft_validation(L):
     assert _draft(L, r=264) == 2
     assert _draft(L, ws_bytes=8) == 3
     assert _draft(L, ws=0) == 3
+    assert _draft(L, ws=FAKE + 8) == 3
+    assert b"aligned" in L.dsp_last_error()
     assert _draft(L, base_rs=-1) == 1
     assert b"strides" in L.dsp_last_error()
     assert _draft(L, base_ps=-32) == 1
@@ -131,3 +133,5 @@ def test_confidence_and_verify_validation(L):
     assert v == 1 and b"base strides" in L.dsp_last_error()
     v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 7, 1.0, 0, 0, P(FAKE), 1 << 20, None)
     assert v == 1 and b"flags" in L.dsp_last_error()
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0, 1.0, 0, 0, P(FAKE + 8), 1 << 20, None)
+    assert v == 3 and b"aligned" in L.dsp_last_error()

@@ -156,13 +156,17 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
         const float mref = (m == -INFINITY) ? 0.0f : m;
-        double s = 0.0;
+        // a pairwise fp32 tree over the lane's 32 weights, then fp64 across lanes
+        float w[32];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; e += 2)
-                s += (double)(wexp(Logit<LT>::raw_at(raw[k], e) - mref, itL) +
-                              wexp(Logit<LT>::raw_at(raw[k], e + 1) - mref, itL));
+            for (int e = 0; e < 8; ++e) w[8 * k + e] = wexp(Logit<LT>::raw_at(raw[k], e) - mref, itL);
+#pragma unroll
+        for (int hw = 16; hw >= 1; hw >>= 1)
+#pragma unroll
+            for (int i = 0; i < hw; ++i) w[i] = w[i] + w[i + hw];
+        double s = (double)w[0];
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
         if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
@@ -170,7 +174,8 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
         // summed: one partial per wave
         float mw = fmaxf(m, __shfl_xor(m, 8, kWave));
         mw = xmax<32>(xmax<16>(mw));
-        double sw = (m == -INFINITY) ? 0.0 : s * exp(((double)m - (double)mw) * (double)inv_temp);
+        // (the rescale factor in fp32, as the persistent draft merges its groups)
+        double sw = (m == -INFINITY) ? 0.0 : s * (double)wexp(m - mw, itL);
         sw += __shfl_xor(sw, 8, kWave);
         sw = xsum<32>(xsum<16>(sw));
         if (lane == 0)

@@ -72,10 +72,15 @@ static_assert(DSP_PATH_AUTO == dsp::kPathAuto && DSP_PATH_STREAMING == dsp::kPat
                   DSP_PATH_PERSISTENT == dsp::kPathPersistent,
               "path codes");
 
+// a dsp_path_flags value, optionally with the give-up test hook
 bool known_path(unsigned f)
 {
-    return f == DSP_PATH_AUTO || f == DSP_PATH_STREAMING || f == DSP_PATH_PERSISTENT;
+    const unsigned p = f & ~DSP_FLAG_TEST_GIVE_UP;
+    return p == DSP_PATH_AUTO || p == DSP_PATH_STREAMING || p == DSP_PATH_PERSISTENT;
 }
+
+int path_of(unsigned f) { return (int)(f & ~DSP_FLAG_TEST_GIVE_UP); }
+bool give_up_of(unsigned f) { return (f & DSP_FLAG_TEST_GIVE_UP) != 0u; }
 
 }  // namespace
 
@@ -89,13 +94,14 @@ const char* dsp_status_string(dsp_status s)
     case DSP_ERR_UNSUPPORTED: return "DSP_ERR_UNSUPPORTED";
     case DSP_ERR_WORKSPACE: return "DSP_ERR_WORKSPACE";
     case DSP_ERR_HIP: return "DSP_ERR_HIP";
+    case DSP_ERR_TIMEOUT: return "DSP_ERR_TIMEOUT";
     }
     return "DSP_ERR_UNKNOWN";
 }
 
 const char* dsp_last_error(void) { return g_err; }
 
-int dsp_version(void) { return 300; }
+int dsp_version(void) { return 400; }
 
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 {
@@ -103,6 +109,33 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
     if (which == DSP_WS_DRAFT) return dsp::draft_workspace_bytes(R, V);
     if (which == DSP_WS_VERIFY) return dsp::verify_workspace_bytes(R, gamma, V);
     return 0;
+}
+
+dsp_status dsp_workspace_status(dsp_ws_kind which, const void* ws, size_t ws_bytes, int R,
+                                int gamma, int V, int r, void* stream)
+{
+    if (which != DSP_WS_DRAFT && which != DSP_WS_VERIFY)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_workspace_status: unknown workspace kind %d", (int)which);
+    if (!ws) return fail(DSP_ERR_INVALID_ARG, "dsp_workspace_status: null workspace");
+    dsp_status st = check_markov(R, gamma, V, r);
+    if (st != DSP_OK) return st;
+    const size_t need = which == DSP_WS_DRAFT ? dsp::draft_workspace_bytes(R, V)
+                                              : dsp::verify_workspace_bytes(R, gamma, V);
+    if (ws_bytes < need)
+        return fail(DSP_ERR_WORKSPACE, "dsp_workspace_status: workspace of %zu bytes, %zu needed",
+                    ws_bytes, need);
+    const unsigned* word = which == DSP_WS_DRAFT ? dsp::draft_error_word(ws, R, V)
+                                                 : dsp::verify_error_word(ws, R, gamma, V);
+    unsigned v = 0;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "dsp_workspace_status");
+    if (v != 0u)
+        return fail(DSP_ERR_TIMEOUT,
+                    "a bounded wait of the last persistent launch on this workspace gave up; "
+                    "its outputs are undefined");
+    return ok();
 }
 
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
@@ -138,7 +171,8 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
         return fail(DSP_ERR_WORKSPACE, "dsp_draft_step: the workspace must be 16-byte aligned");
     return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
                                              dtype == DSP_BF16, E, W2, anchor, tok, q,
-                                             stats, R, gamma, V, r, k, n_steps, (int)flags, temperature,
+                                             stats, R, gamma, V, r, k, n_steps, path_of(flags),
+                                             give_up_of(flags), temperature,
                                              seed, round,
                                              ws, static_cast<hipStream_t>(stream)),
                       "dsp_draft_step launch");
@@ -174,8 +208,9 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
         return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: mode must be 0 or 1 (got %d)", mode);
     if (mode == 1 && B_max < R)
         return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: B_max = %d < R = %d", B_max, R);
-    if (!(tau0 >= 0.0) || !(tau0 < 1e6))
-        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: tau0 must be in [0, 1e6)");
+    // tau0 2^48 plus the admitted sum (below R gamma 2^48 <= 2^62) must fit 64 bits
+    if (!(tau0 >= 0.0) || !(tau0 < 16384.0))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule: tau0 must be in [0, 2^14)");
     if (mode == 1 && (int64_t)R * gamma > dsp::kSchedMaxCand)
         return fail(DSP_ERR_UNSUPPORTED, "dsp_schedule: R * gamma = %lld exceeds %d",
                     (long long)R * gamma, dsp::kSchedMaxCand);
@@ -217,7 +252,7 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
         return fail(DSP_ERR_WORKSPACE, "dsp_verify: the workspace must be 16-byte aligned");
     return hip_status(dsp::launch_verify(target, dsp::RowStrides{target_rs, target_ps}, base,
                                          dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16,
-                                         (int)flags, E,
+                                         path_of(flags), give_up_of(flags), E,
                                          W2, anchor, tok, q,
                                          stats, len, accept, n_accept, y, p, R, gamma, V, r,
                                          temperature, seed, round, ws,

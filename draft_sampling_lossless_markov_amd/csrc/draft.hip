@@ -130,6 +130,11 @@ static size_t draft_part_bytes(int R, int V)
 
 size_t draft_workspace_bytes(int R, int V) { return draft_part_bytes(R, V) + kRunCtlBytes; }
 
+const unsigned* draft_error_word(const void* ws, int R, int V)
+{
+    return reinterpret_cast<const unsigned*>(static_cast<const char*>(ws) + draft_part_bytes(R, V));
+}
+
 // requests per workgroup of a bias pass: whole 64-request blocks, split into
 // balanced chunks so the grid has about 1024 workgroups (two rounds at two per
 // CU; every chunk re-reads its W2 tile, so fewer chunks move fewer bytes)
@@ -154,7 +159,8 @@ template <typename LT>
 static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
                                  const int32_t* anchor, int32_t* tok, float* q, double* stats,
                                  int R, int gamma, int V, int r, int k, float temperature,
-                                 uint64_t seed, uint32_t round, void* ws, hipStream_t s)
+                                 uint64_t seed, uint32_t round, void* ws, unsigned* ctl,
+                                 hipStream_t s)
 {
     const int n_vt = (V + kVocabTile - 1) / kVocabTile;
     Part* part = static_cast<Part*>(ws);
@@ -166,6 +172,7 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     a.n_vt = n_vt;
     a.req_per_wg = pass_req_per_wg(R, n_vt);
     a.part = part;
+    a.ctl = ctl;
     const dim3 g1(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
     const bool vec = rows_vec(bs, V, 8);
     if (greedy && vec)
@@ -196,9 +203,10 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
 // persistent path
 // ---------------------------------------------------------------------------
 // Marks every partial slot of a launch and the tokens of its positions empty,
-// and clears the error word.
+// and sets the error word: 0, or 1 under the give-up test hook (every wait of
+// the launch then returns at once).
 __global__ void run_clear_kernel(uint64_t* slots, int64_t n_slots, int32_t* tok, int R, int gamma,
-                                 int k0, int n_steps, unsigned* ctl)
+                                 int k0, int n_steps, unsigned* ctl, unsigned ctl0)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -206,7 +214,7 @@ __global__ void run_clear_kernel(uint64_t* slots, int64_t n_slots, int32_t* tok,
     const int64_t n_tok = (int64_t)R * n_steps;
     for (int64_t i = i0; i < n_tok; i += stride)
         tok[(i / n_steps) * gamma + k0 + (i % n_steps)] = kRunTokEmpty;
-    if (i0 == 0) ctl[0] = 0u;
+    if (i0 == 0) ctl[0] = ctl0;
 }
 
 namespace {
@@ -243,7 +251,8 @@ int run_units(int V, int ncu, int* n_t)
 }
 
 template <bool GREEDY, int TU>
-hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, hipStream_t s, bool* launched)
+hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, bool give_up, hipStream_t s,
+                        bool* launched)
 {
     *launched = false;
     static std::atomic<int> occ{-1};
@@ -259,7 +268,7 @@ hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, hipStream_t s, bool* 
     const int64_t n_clear = std::max<int64_t>(n_slots, (int64_t)ra.R * ra.n_steps);
     const int cg = (int)std::min<int64_t>(1024, (n_clear + 255) / 256);
     hipLaunchKernelGGL(run_clear_kernel, dim3(cg), dim3(256), 0, s, ra.slots, n_slots, ra.tok, ra.R,
-                       ra.gamma, ra.k0, ra.n_steps, ra.ctl);
+                       ra.gamma, ra.k0, ra.n_steps, ra.ctl, give_up ? 1u : 0u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // an ordinary launch: the grid has at most one workgroup per CU and the
@@ -276,7 +285,8 @@ hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, hipStream_t s, bool* 
 hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
                           const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                           int gamma, int V, int r, int k0, int n_steps, float temperature,
-                          uint64_t seed, uint32_t round, void* ws, hipStream_t s, bool* launched)
+                          uint64_t seed, uint32_t round, void* ws, bool give_up, hipStream_t s,
+                          bool* launched)
 {
     *launched = false;
     if (!rows_vec(bs, V, 8) || R > kRunReqMax) return hipSuccess;
@@ -295,8 +305,8 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
     // no workgroup then draws two requests of a position
     const int G = std::max((n_t + 3) / 4, std::min(R, geo.ncu));
 #define DSP_RUN(TU)                                                                            \
-    return greedy ? launch_run_t<true, TU>(ra, G, geo.ncu, s, launched)                        \
-                  : launch_run_t<false, TU>(ra, G, geo.ncu, s, launched)
+    return greedy ? launch_run_t<true, TU>(ra, G, geo.ncu, give_up, s, launched)               \
+                  : launch_run_t<false, TU>(ra, G, geo.ncu, give_up, s, launched)
     switch (tu) {
     case 1: DSP_RUN(1);
     case 2: DSP_RUN(2);
@@ -322,23 +332,26 @@ hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const u
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, int n_steps, int path,
-                             float temperature, uint64_t seed, uint32_t round, void* ws,
-                             hipStream_t s)
+                             bool give_up, float temperature, uint64_t seed, uint32_t round,
+                             void* ws, hipStream_t s)
 {
     if (path != kPathStream && bf16) {
         bool launched = false;
         const hipError_t e = try_launch_run(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok,
                                             q, stats, R, gamma, V, r, k, n_steps, temperature, seed,
-                                            round, ws, s, &launched);
+                                            round, ws, give_up, s, &launched);
         if (launched || e != hipSuccess) return e;
     }
     if (path == kPathPersistent) return hipErrorNotSupported;
+    // the streaming launches have no waits: the first pass clears the error word
+    unsigned* ctl = const_cast<unsigned*>(draft_error_word(ws, R, V));
     for (int i = 0; i < n_steps; ++i) {
+        unsigned* c = (i == 0) ? ctl : nullptr;
         const hipError_t e =
             bf16 ? launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,
-                                  R, gamma, V, r, k + i, temperature, seed, round, ws, s)
+                                  R, gamma, V, r, k + i, temperature, seed, round, ws, c, s)
                  : launch_draft_t(static_cast<const float*>(base), bs, E, W2, anchor, tok, q, stats,
-                                  R, gamma, V, r, k + i, temperature, seed, round, ws, s);
+                                  R, gamma, V, r, k + i, temperature, seed, round, ws, c, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

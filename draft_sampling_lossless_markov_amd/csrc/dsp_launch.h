@@ -27,6 +27,10 @@ __host__ __device__ inline bool rows_vec(RowStrides s, int V, int align)
 
 size_t draft_workspace_bytes(int R, int V);
 size_t verify_workspace_bytes(int R, int gamma, int V);
+// the error word of a workspace: nonzero when a bounded wait of the last call
+// on it gave up
+const unsigned* draft_error_word(const void* ws, int R, int V);
+const unsigned* verify_error_word(const void* ws, int R, int gamma, int V);
 int pass_req_per_wg(int count_max, int n_vt);
 
 // implementation paths of the draft and the residual draws: automatic
@@ -47,8 +51,8 @@ hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const u
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, int n_steps, int path,
-                             float temperature, uint64_t seed, uint32_t round, void* ws,
-                             hipStream_t s);
+                             bool give_up, float temperature, uint64_t seed, uint32_t round,
+                             void* ws, hipStream_t s);
 
 hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
                              const int32_t* tok, const float* w, const float* T,
@@ -59,7 +63,7 @@ hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t
                            int32_t* len, float* a, int32_t* B, int R, int gamma, hipStream_t s);
 
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
-                         bool bf16, int path, const uint16_t* E,
+                         bool bf16, int path, bool give_up, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,

@@ -76,6 +76,8 @@ struct PassArgs {
     float inv_temp;
     int n_vt, req_per_wg;
     Part* part;              // [R, n_vt] (kResidual: [queue slot, n_vt])
+    unsigned* ctl;           // error word of the call's workspace, set to 0 by the
+                             // first pass of a call (nullptr: left alone)
 };
 
 // ---------------------------------------------------------------------------
@@ -212,6 +214,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
     constexpr int RW = Logit<LT>::kRaw;
     constexpr bool RES = (KIND == kResidual);
 
+    if (a.ctl && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ctl[0] = 0u;
     const int count = RES ? *a.count : a.R;
     const int n_begin = blockIdx.y * a.req_per_wg;
     if (n_begin >= count) return;   // workgroup-uniform

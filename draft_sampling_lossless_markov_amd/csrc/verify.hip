@@ -95,14 +95,16 @@ template <typename LT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_rows_kernel(
     const LT* __restrict__ target, RowStrides ts, const int32_t* __restrict__ tok,
     const int32_t* __restrict__ len, int R, int gamma, int V, float inv_temp, int n_vt,
-    VerifyWs ws)
+    VerifyWs ws, unsigned ctl0)
 {
     constexpr int RW = Logit<LT>::kRaw;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const float itL = fold_itl(inv_temp);
+    // the error word of the call: 0, or 1 under the give-up test hook (every wait
+    // of the persistent residual launch then returns at once)
     if (blockIdx.x == 0 && tid == 0) {
         *ws.resid_cnt = 0;
-        ws.run_ctl[0] = 0u;
+        ws.run_ctl[0] = ctl0;
     }
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int per_req = (gamma + 1) * spans;
@@ -423,6 +425,11 @@ size_t verify_workspace_bytes(int R, int gamma, int V)
     return total;
 }
 
+const unsigned* verify_error_word(const void* ws, int R, int gamma, int V)
+{
+    return carve(const_cast<void*>(ws), R, gamma, V, nullptr).run_ctl;
+}
+
 template <bool GREEDY>
 static void launch_accept(const int32_t* anchor, int V, const int32_t* tok, const float* q,
                           const int32_t* len, int8_t* accept, int32_t* n_accept, int32_t* y,
@@ -480,7 +487,7 @@ static hipError_t launch_resid_t(const ResidArgs& ra, int G, int ncu, hipStream_
 
 template <typename LT>
 static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
-                                  int path, const uint16_t* E,
+                                  int path, bool give_up, const uint16_t* E,
                                   const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                                   const float* q, const double* stats, const int32_t* len,
                                   int8_t* accept, int32_t* n_accept, int32_t* y, float* p, int R,
@@ -497,7 +504,7 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     if (path == kPathPersistent && !std::is_same<LT, uint16_t>::value) return hipErrorNotSupported;
     if (greedy) {
         hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, ts, tok, len,
-                           R, gamma, V, it, n_vt, ws);
+                           R, gamma, V, it, n_vt, ws, 0u);
         launch_accept<true>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed,
                             round, n_vt, ws, s);
         return hipGetLastError();
@@ -510,7 +517,7 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
               run_geometry(V, &geo);
     if (path == kPathPersistent && !run) return hipErrorNotSupported;
     hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, ts, tok, len, R,
-                       gamma, V, it, n_vt, ws);
+                       gamma, V, it, n_vt, ws, (run && give_up) ? 1u : 0u);
     launch_accept<false>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round,
                          n_vt, ws, s, run ? geo.n_t : 0);
     if constexpr (std::is_same<LT, uint16_t>::value) {
@@ -563,7 +570,7 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
 }
 
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
-                         bool bf16, int path, const uint16_t* E,
+                         bool bf16, int path, bool give_up, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
@@ -571,11 +578,11 @@ hipError_t launch_verify(const void* target, RowStrides ts, const void* base, Ro
 {
     if (bf16)
         return launch_verify_t(static_cast<const uint16_t*>(target), ts,
-                               static_cast<const uint16_t*>(base), bs, path, E, W2, anchor, tok, q, stats,
+                               static_cast<const uint16_t*>(base), bs, path, give_up, E, W2, anchor, tok, q, stats,
                                len, accept, n_accept, y, p, R, gamma, V, r, temperature, seed, round,
                                ws, s);
     return launch_verify_t(static_cast<const float*>(target), ts, static_cast<const float*>(base), bs,
-                           path, E, W2,
+                           path, give_up, E, W2,
                            anchor, tok, q, stats, len, accept, n_accept, y, p, R, gamma, V, r,
                            temperature, seed, round, ws, s);
 }

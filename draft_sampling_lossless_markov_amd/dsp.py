@@ -17,13 +17,18 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsp.so")
 
-DSP_OK, DSP_ERR_INVALID_ARG, DSP_ERR_UNSUPPORTED, DSP_ERR_WORKSPACE, DSP_ERR_HIP = range(5)
+(DSP_OK, DSP_ERR_INVALID_ARG, DSP_ERR_UNSUPPORTED, DSP_ERR_WORKSPACE, DSP_ERR_HIP,
+ DSP_ERR_TIMEOUT) = range(6)
+_STATUS_NAMES = ("DSP_OK", "DSP_ERR_INVALID_ARG", "DSP_ERR_UNSUPPORTED", "DSP_ERR_WORKSPACE",
+                 "DSP_ERR_HIP", "DSP_ERR_TIMEOUT")
 DSP_F32, DSP_BF16 = 0, 1
 DSP_WS_DRAFT, DSP_WS_VERIFY = 0, 1
 DSP_PATH_AUTO, DSP_PATH_STREAMING, DSP_PATH_PERSISTENT = 0, 1, 2
+DSP_FLAG_TEST_GIVE_UP = 0x100
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
-            "dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify")
+            "dsp_workspace_status", "dsp_draft_step", "dsp_confidence", "dsp_schedule",
+            "dsp_verify")
 
 _lib = None
 
@@ -35,8 +40,7 @@ class DspError(RuntimeError):
 
 
 def _status_name(s):
-    return ["DSP_OK", "DSP_ERR_INVALID_ARG", "DSP_ERR_UNSUPPORTED", "DSP_ERR_WORKSPACE",
-            "DSP_ERR_HIP"][s] if 0 <= s < 5 else f"status {s}"
+    return _STATUS_NAMES[s] if 0 <= s < len(_STATUS_NAMES) else f"status {s}"
 
 
 def lib():
@@ -57,6 +61,8 @@ def lib():
     L.dsp_version.restype = I
     L.dsp_workspace_size.argtypes = [I, I, I, I, I]
     L.dsp_workspace_size.restype = SZ
+    L.dsp_workspace_status.argtypes = [I, P, SZ, I, I, I, I, P]
+    L.dsp_workspace_status.restype = I
     I64 = C.c_int64
     L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, I, U32, F, U64,
                                  U32, P, SZ, P]
@@ -102,6 +108,13 @@ def _rows(t: torch.Tensor, name: str):
 
 def dsp_workspace_size(which: int, R: int, gamma: int, V: int, r: int) -> int:
     return int(lib().dsp_workspace_size(which, R, gamma, V, r))
+
+
+def dsp_workspace_status(which: int, ws, R: int, gamma: int, V: int, r: int, stream=None):
+    """Wait for the stream; raise DspError(DSP_ERR_TIMEOUT) if a bounded wait of the
+    last call on workspace ws gave up (its outputs are then undefined)."""
+    _check(lib().dsp_workspace_status(int(which), _ptr(ws), ws.numel() * ws.element_size(), R,
+                                      gamma, V, r, _stream(stream)))
 
 
 def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_, ws,

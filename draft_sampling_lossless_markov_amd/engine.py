@@ -52,6 +52,13 @@ class Round:
                        self.q, self.stats, self.len, self.accept, self.n_accept, self.y, self.p,
                        temperature, seed, rnd, self.ws_verify, stream, flags=flags)
 
+    def check(self, stream=None):
+        """Wait for the stream and raise DspError(DSP_ERR_TIMEOUT) if a bounded wait
+        of the last draft or verify call gave up."""
+        args = (self.R, self.gamma, self.V, self.r)
+        dsp.dsp_workspace_status(dsp.DSP_WS_DRAFT, self.ws_draft, *args, stream=stream)
+        dsp.dsp_workspace_status(dsp.DSP_WS_VERIFY, self.ws_verify, *args, stream=stream)
+
     def run(self, inp, temperature, seed, rnd, mode=None, tau0=None, stream=None):
         self.draft(inp, temperature, seed, rnd, stream)
         self.confidence(inp, stream)

@@ -27,9 +27,16 @@
  *     step; a position-major base tensor (each draft step reads one contiguous
  *     [R, V] slab) or a row pitch padded off a power of two avoids it.
  *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is the
- *     default stream).  No call synchronises the host; lengths and batch sizes
- *     stay on the device.  Calls on different streams with different workspaces
- *     may run concurrently; two calls sharing a workspace must be ordered.
+ *     default stream).  No call synchronises the host except
+ *     dsp_workspace_status(); lengths and batch sizes stay on the device.  Two
+ *     calls sharing a workspace must be ordered.  Calls on different streams
+ *     with different workspaces may run concurrently only where neither takes a
+ *     persistent launch (DSP_PATH_STREAMING, or shapes where DSP_PATH_AUTO does
+ *     not apply one): a persistent launch holds one workgroup on every compute
+ *     unit and needs all of them resident together, so work beside it can only
+ *     delay it, and two persistent launches that overlap can starve each other
+ *     until their bounded waits give up.  A wait that gives up leaves that
+ *     call's outputs undefined and is reported by dsp_workspace_status().
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - Token ids and lengths are int32; V < 2^31.  seed is 64-bit, round 32-bit.
  *   - Randomness: u(seed, round, request, position, purpose) in [0, 1) is the top
@@ -40,15 +47,17 @@
  *     kernels' support DSP_ERR_UNSUPPORTED, both before any HIP call; a workspace
  *     that is too small returns DSP_ERR_WORKSPACE; a failed launch returns
  *     DSP_ERR_HIP.  dsp_last_error() gives a thread-local explanation.  Faults
- *     inside kernels surface at the caller's next synchronisation.  No C++
- *     exception crosses this boundary.
+ *     inside kernels surface at the caller's next synchronisation; a bounded
+ *     wait of a persistent launch that gave up is reported as DSP_ERR_TIMEOUT by
+ *     dsp_workspace_status().  No C++ exception crosses this boundary.
  *
  * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
  * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
  *
- * ABI version 300: dsp_draft_step draws n_steps consecutive positions per call;
- * dsp_draft_step and dsp_verify take flags that select their implementation.
- * (200: element strides.)
+ * ABI version 400: DSP_ERR_TIMEOUT and dsp_workspace_status(); the scheduler's
+ * tau0 is bounded by 2^14.  (300: dsp_draft_step draws n_steps consecutive
+ * positions per call; dsp_draft_step and dsp_verify take flags that select their
+ * implementation.  200: element strides.)
  */
 #ifndef DSP_H
 #define DSP_H
@@ -65,7 +74,8 @@ typedef enum {
     DSP_ERR_INVALID_ARG = 1,
     DSP_ERR_UNSUPPORTED = 2,
     DSP_ERR_WORKSPACE = 3,
-    DSP_ERR_HIP = 4
+    DSP_ERR_HIP = 4,
+    DSP_ERR_TIMEOUT = 5
 } dsp_status;
 
 typedef enum { DSP_F32 = 0, DSP_BF16 = 1 } dsp_dtype;
@@ -84,6 +94,22 @@ int dsp_version(void);
 /* Bytes of workspace dsp_draft_step (DSP_WS_DRAFT) or dsp_verify (DSP_WS_VERIFY)
  * needs for these sizes; 0 for invalid sizes. */
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
+
+/*
+ * dsp_workspace_status -- did the last call on this workspace complete every
+ * bounded wait?
+ *
+ * Waits for `stream` (the host blocks), then reads the error word that the last
+ * dsp_draft_step (which = DSP_WS_DRAFT) or dsp_verify (DSP_WS_VERIFY) issued with
+ * workspace ws wrote: DSP_OK when its waits all completed (and for calls that
+ * have none), DSP_ERR_TIMEOUT when a wait of a persistent launch gave up -- the
+ * outputs of that call are then undefined (tokens, q, stats, or the correction
+ * and bonus tokens) though every kernel ran to its end.  The sizes are the ones
+ * of that call; ws and ws_bytes as passed to it.  Undefined before the
+ * workspace's first call.  A failing synchronisation returns DSP_ERR_HIP.
+ */
+dsp_status dsp_workspace_status(dsp_ws_kind which, const void* ws, size_t ws_bytes, int R,
+                                int gamma, int V, int r, void* stream);
 
 /*
  * dsp_draft_step -- draft positions k, k+1, ..., k+n_steps-1 for all R requests,
@@ -130,12 +156,19 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
  *                              the outputs undefined)
  *        DSP_PATH_PERSISTENT   the persistent launch only; where it does not apply
  *                              the call returns DSP_ERR_HIP (hipErrorNotSupported)
- *        anything else: DSP_ERR_INVALID_ARG
- *        While a persistent launch runs, tok[:, k .. k+n_steps-1] also carries its
+ *        optionally or-ed with DSP_FLAG_TEST_GIVE_UP; anything else:
+ *        DSP_ERR_INVALID_ARG.  While a persistent launch runs, tok[:, k .. k+n_steps-1] also carries its
  *        progress: the call overwrites those columns (and the workspace) only.
  * ws     >= dsp_workspace_size(DSP_WS_DRAFT, R, gamma, V, r) bytes
  */
 typedef enum { DSP_PATH_AUTO = 0, DSP_PATH_STREAMING = 1, DSP_PATH_PERSISTENT = 2 } dsp_path_flags;
+/* Test hook, or-ed into flags of dsp_draft_step / dsp_verify: a persistent launch
+ * starts as if one of its waits had already given up, so every wait returns at
+ * once, every kernel still runs to its end, the outputs are undefined and
+ * dsp_workspace_status() reports DSP_ERR_TIMEOUT.  It lets callers test their
+ * handling of that report without starving the GPU; calls without a
+ * persistent launch ignore it. */
+#define DSP_FLAG_TEST_GIVE_UP 0x100u
 dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
                           const uint16_t* E, const uint16_t* W2, const int32_t* anchor, int32_t* tok, float* q,
                           double* stats, int R, int gamma, int V, int r, int k, int n_steps,
@@ -183,7 +216,9 @@ dsp_status dsp_confidence(const uint16_t* h, const uint16_t* E, const int32_t* a
  * mode 0 verifies everything: len[r] = gamma, *B = R (1 + gamma); a still written.
  *
  * c [R, gamma] f32 in [0, 1]; sps [B_max] f32 with sps[B-1] = SPS(B); B_max >= R;
- * tau0 >= 0; len [R] int32; a [R, gamma] f32; B [1] int32 (all device memory).
+ * 0 <= tau0 < 2^14 (so tau0 2^48 plus the admitted sum fits 64 bits;
+ * DSP_ERR_INVALID_ARG otherwise); len [R] int32; a [R, gamma] f32; B [1] int32
+ * (all device memory).
  * Runs as one workgroup; mode 1 needs R * gamma <= 16384.
  */
 dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0, int mode,
@@ -224,7 +259,8 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
  * that holds the W2 slice on chip where the draft's does (see dsp_draft_step), with
  * a streaming pass and a pick launch elsewhere; DSP_PATH_STREAMING always the latter;
  * DSP_PATH_PERSISTENT the former only (DSP_ERR_HIP, hipErrorNotSupported, where it
- * does not apply; greedy verification draws no residual and ignores it).
+ * does not apply; greedy verification draws no residual and ignores it),
+ * optionally or-ed with DSP_FLAG_TEST_GIVE_UP.
  * ws >= dsp_workspace_size(DSP_WS_VERIFY, R, gamma, V, r) bytes.
  */
 dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, const void* base,

@@ -34,14 +34,14 @@ def lib():
         _lib.orc_softmax.argtypes = [C.c_int, P, C.c_double, P, P]
         _lib.orc_inverse_cdf.argtypes = [C.c_int, P, C.c_double, C.c_double, P]
         _lib.orc_draft.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P, P, P,
-                                   C.c_double, C.c_uint64, C.c_uint32, P, P, P, P]
+                                   C.c_double, C.c_uint64, C.c_uint32, P, P, P, P, P]
         _lib.orc_confidence.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P,
                                         P, P, P, P, P]
         _lib.orc_schedule.argtypes = [C.c_int, C.c_int, P, P, C.c_int, C.c_double, C.c_int,
                                       P, P, P, P]
         _lib.orc_verify.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P,
                                     P, P, P, P, P, C.c_double, C.c_uint64, C.c_uint32,
-                                    P, P, P, P, P, P]
+                                    P, P, P, P, P, P, P]
     return _lib
 
 
@@ -107,8 +107,10 @@ def inverse_cdf(w, u, window=1e-6):
     return x, bool(near.value)
 
 
-def draft(base, E, W2, anchor, req_id, temperature, seed, rnd):
-    """base [n, gamma, V] (float32 or bf16 bits).  Returns tok, q, stats, flag."""
+def draft(base, E, W2, anchor, req_id, temperature, seed, rnd, force=None):
+    """base [n, gamma, V] (float32 or bf16 bits).  Returns tok, q, stats, flag.
+    force [n, gamma] int32 (optional): tokens >= 0 taken instead of the oracle's
+    own draw at those positions (teacher forcing at a flagged decision)."""
     base, dt = _logits(base)
     n, gamma, V = base.shape
     E = _c(E, np.uint16)
@@ -120,9 +122,10 @@ def draft(base, E, W2, anchor, req_id, temperature, seed, rnd):
     q = np.zeros((n, gamma), np.float64)
     stats = np.zeros((n, gamma, 2), np.float64)
     flag = np.zeros((n, gamma), np.int8)
+    force = None if force is None else _c(force, np.int32)
     _check(lib().orc_draft(n, gamma, V, r, _p(base), dt, _p(E), _p(W2), _p(anchor), _p(req_id),
                            float(temperature), int(seed), int(rnd), _p(tok), _p(q), _p(stats),
-                           _p(flag)), "draft")
+                           _p(flag), _p(force)), "draft")
     return tok, q, stats, flag
 
 
@@ -157,7 +160,10 @@ def schedule(c32, sps, B_max, tau0, mode):
     return length, a, int(B[0]), int(ev[0])
 
 
-def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, seed, rnd):
+def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, seed, rnd,
+           force_acc=None):
+    """force_acc [n, gamma] int8 (optional): 0/1 adopted as the accept decision at
+    those positions, -1 elsewhere (teacher forcing at a flagged accept test)."""
     target, dt = _logits(target)
     base, dt2 = _logits(base)
     assert dt == dt2
@@ -177,10 +183,11 @@ def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, see
     p = np.zeros((n, gamma), np.float64)
     fa = np.zeros((n, gamma), np.int8)
     fy = np.zeros(n, np.int8)
+    force_acc = None if force_acc is None else _c(force_acc, np.int8)
     _check(lib().orc_verify(n, gamma, V, r, _p(target), _p(base), dt, _p(E), _p(W2),
                             _p(anchor), _p(tok), _p(q), _p(length), _p(req_id),
                             float(temperature), int(seed), int(rnd), _p(accept), _p(n_acc),
-                            _p(y), _p(p), _p(fa), _p(fy)), "verify")
+                            _p(y), _p(p), _p(fa), _p(fy), _p(force_acc)), "verify")
     return dict(accept=accept, n_accept=n_acc, y=y, p=p, flag_acc=fa, flag_y=fy)
 
 

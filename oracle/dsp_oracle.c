@@ -213,13 +213,19 @@ static int argmax_f32(int V, const float* x)
 /* flag[i,k] = 1 when the decision is within rounding reach of a boundary:   */
 /*   sampling: u within 1e-6 of the CDF on either side of x_k;               */
 /*   greedy: top-2 logit gap within the bias summation bound plus 2 ulp.     */
+/* force (optional, [n, gamma]): where force[i,k] >= 0 the chain continues   */
+/* from that token instead of its own draw (q and stats are still those of   */
+/* this row's law, q = prob of the forced token).  This is how a comparison  */
+/* adopts the other side's choice at a flagged decision, so that the later   */
+/* positions of the chain stay comparable; flag is computed as usual.        */
 /* ------------------------------------------------------------------------- */
 
 int orc_draft(int n, int gamma, int V, int r,
               const void* base, int dtype, const uint16_t* E, const uint16_t* W2,
               const int32_t* anchor, const int32_t* req_id,
               double temperature, uint64_t seed, uint32_t round,
-              int32_t* tok, double* q, double* stats, int8_t* flag)
+              int32_t* tok, double* q, double* stats, int8_t* flag,
+              const int32_t* force)
 {
     if (n < 0 || gamma <= 0 || V <= 0 || r <= 0 || temperature < 0.0) return 1;
     float* logit = (float*)malloc(sizeof(float) * (size_t)V);
@@ -250,8 +256,9 @@ int orc_draft(int n, int gamma, int V, int r,
                                          (double)(r + 1) * eps * (absdot[x] + absdot[second]);
                     fl = gap <= bound;
                 }
-                q[ik] = 1.0;
                 stats[2 * ik] = (double)logit[x];
+                if (force && force[ik] >= 0 && force[ik] < V) x = force[ik];
+                q[ik] = 1.0;
                 stats[2 * ik + 1] = 0.0;
             } else {
                 double st[2];
@@ -261,6 +268,7 @@ int orc_draft(int n, int gamma, int V, int r,
                 int near = 0;
                 x = orc_inverse_cdf(V, prob, u, SAMPLE_WINDOW, &near);
                 fl = (int8_t)near;
+                if (force && force[ik] >= 0 && force[ik] < V) x = force[ik];
                 q[ik] = prob[x];
                 stats[2 * ik] = st[0];
                 stats[2 * ik + 1] = st[1];
@@ -342,7 +350,10 @@ int orc_schedule(int R, int gamma, const float* c, const float* sps, int B_max,
                  double tau0, int mode, int32_t* len, float* a, int32_t* B_out,
                  int32_t* n_theta_evals)
 {
-    if (R <= 0 || gamma <= 0 || B_max < R || tau0 < 0.0) return 1;
+    /* tau0 < 2^14 keeps tau0 * 2^48 plus the admitted sum (below R gamma 2^48,
+     * R gamma <= 2^14) inside 64 bits */
+    if (R <= 0 || gamma <= 0 || B_max < R || !(tau0 >= 0.0) || !(tau0 < 16384.0)) return 1;
+    if ((int64_t)R * gamma > 16384 && mode != 0) return 1;
     for (int r = 0; r < R; ++r) {
         float prod = 1.0f;
         for (int j = 0; j < gamma; ++j) {
@@ -403,6 +414,9 @@ int orc_schedule(int R, int gamma, const float* c, const float* sps, int B_max,
 /*   both draws use u(seed, round, req, n, purpose 2).                       */
 /* accept[i,j] is 1/0 for j < l and -1 for unverified positions.            */
 /* flag_acc marks |u - p/q| < 1e-6; flag_y marks a near-boundary draw of y.  */
+/* force_acc (optional, [n, gamma]): where force_acc[i,j] is 0 or 1 that     */
+/* decision is adopted instead of this side's (a comparison taking the other */
+/* side's choice at a flagged accept test); -1 leaves it alone.              */
 /* ------------------------------------------------------------------------- */
 
 int orc_verify(int n_req, int gamma, int V, int r,
@@ -412,7 +426,7 @@ int orc_verify(int n_req, int gamma, int V, int r,
                const int32_t* len, const int32_t* req_id,
                double temperature, uint64_t seed, uint32_t round,
                int8_t* accept, int32_t* n_accept, int32_t* y, double* p_out,
-               int8_t* flag_acc, int8_t* flag_y)
+               int8_t* flag_acc, int8_t* flag_y, const int8_t* force_acc)
 {
     if (n_req < 0 || gamma <= 0 || V <= 0 || r <= 0 || temperature < 0.0) return 1;
     float* tl = (float*)malloc(sizeof(float) * (size_t)V);
@@ -446,6 +460,7 @@ int orc_verify(int n_req, int gamma, int V, int r,
                 p_out[ij] = px;
                 flag_acc[ij] = fabs(u - ratio) < ACCEPT_WINDOW;
             }
+            if (force_acc && (force_acc[ij] == 0 || force_acc[ij] == 1)) acc = force_acc[ij];
             accept[ij] = (int8_t)acc;
             if (!acc && n == l) n = j;
         }

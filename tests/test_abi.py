@@ -41,7 +41,8 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings_and_version(L):
     assert L.dsp_status_string(0) == b"DSP_OK"
     assert L.dsp_status_string(3) == b"DSP_ERR_WORKSPACE"
-    assert L.dsp_version() == 300
+    assert L.dsp_status_string(5) == b"DSP_ERR_TIMEOUT"
+    assert L.dsp_version() == 400
 
 
 def test_workspace_sizes(L):
@@ -108,6 +109,31 @@ def test_schedule_validation(L):
     assert f(P(FAKE), P(FAKE), 20, 0.0, 2, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
     assert f(P(FAKE), P(FAKE), 10 ** 6, 0.0, 1, P(FAKE), P(FAKE), P(FAKE), 4097, 4, None) == 2
     assert b"16384" in L.dsp_last_error()
+    # tau0 * 2^48 plus the admitted sum must fit 64 bits: tau0 < 2^14
+    assert f(P(FAKE), P(FAKE), 20, 16384.0, 1, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
+    assert b"tau0" in L.dsp_last_error()
+    assert f(P(FAKE), P(FAKE), 20, float("nan"), 1, P(FAKE), P(FAKE), P(FAKE), 4, 4, None) == 1
+
+
+def test_schedule_tau0_bound_in_oracle(orc):
+    import numpy as np
+    c = np.full((4, 4), 0.9, np.float32)
+    sps = np.ones(20, np.float32)
+    with pytest.raises(RuntimeError):
+        orc.schedule(c, sps, 20, 16384.0, 1)
+    length, _, B, _ = orc.schedule(c, sps, 20, 16383.0, 1)
+    assert B == 4 + int(length.sum())
+
+
+def test_workspace_status_validation(L):
+    P = C.c_void_p
+    f = L.dsp_workspace_status
+    f.argtypes = [C.c_int, P, C.c_size_t, C.c_int, C.c_int, C.c_int, C.c_int, P]
+    assert f(2, P(FAKE), 1 << 20, 4, 4, 32, 8, None) == 1            # unknown kind
+    assert f(0, P(0), 1 << 20, 4, 4, 32, 8, None) == 1               # null workspace
+    assert f(0, P(FAKE), 16, 4, 4, 32, 8, None) == 3                 # too small
+    assert f(1, P(FAKE), 1 << 20, 4, 4, 32, 12, None) == 2           # r unsupported
+    assert f(1, P(FAKE), 1 << 20, 0, 4, 32, 8, None) == 1            # bad R
 
 
 def test_confidence_and_verify_validation(L):
@@ -132,6 +158,10 @@ def test_confidence_and_verify_validation(L):
                      0, 1.0, 0, 0, P(FAKE), 1 << 20, None)
     assert v == 1 and b"base strides" in L.dsp_last_error()
     v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 7, 1.0, 0, 0, P(FAKE), 1 << 20, None)
+    assert v == 1 and b"flags" in L.dsp_last_error()
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0x200, 1.0, 0, 0, P(FAKE), 1 << 20, None)
+    assert v == 1 and b"flags" in L.dsp_last_error()
+    v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0x103, 1.0, 0, 0, P(FAKE), 1 << 20, None)
     assert v == 1 and b"flags" in L.dsp_last_error()
     v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0, 1.0, 0, 0, P(FAKE + 8), 1 << 20, None)
     assert v == 3 and b"aligned" in L.dsp_last_error()

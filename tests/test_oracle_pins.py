@@ -296,6 +296,206 @@ def test_confidence_concatenation_and_temperature(orc):
                                rtol=1e-9, atol=1e-9)
 
 
+def test_confidence_is_a_linear_layer_and_sigmoid(orc):
+    """The head of page "DeepSeek联合北大最新文章DSpark" section 2.1 as the library
+    layers it is made of: torch's Linear (no bias) over the concatenation
+    [h_k; W1[x_{k-1}]] in float64, the offset added, divided by T_k, torch's
+    sigmoid.  Every (request, position) has its own hidden row and its own
+    previous token, so reading another row, another request's token or the
+    token of another position changes the result."""
+    rng = np.random.default_rng(16)
+    n, g, d, V, r = 7, 5, 24, 40, 8
+    h = bf16(rng.normal(0, 1, (n, g, d)))
+    E = bf16(rng.normal(0, 0.5, (V, r)))
+    w = rng.normal(0, 0.3, d + r).astype(np.float32)
+    T = np.array([1.0, 1.3, 0.7, 2.0, 1.1], np.float32)
+    off = rng.uniform(-2, 2, n).astype(np.float32)
+    anchor = rng.integers(0, V, n).astype(np.int32)
+    anchor[2] = -1
+    tok = rng.integers(0, V, (n, g)).astype(np.int32)
+    c, _ = orc.confidence(h, E, anchor, tok, w, T, off)
+    lin = torch.nn.Linear(d + r, 1, bias=False).double()
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(w.astype(np.float64))[None, :])
+    ref = np.zeros((n, g))
+    for i in range(n):
+        for k in range(g):
+            prev = anchor[i] if k == 0 else tok[i, k - 1]
+            e = bf16_val(E[prev]) if prev >= 0 else np.zeros(r)
+            x = torch.from_numpy(np.concatenate([bf16_val(h[i, k]), e]))
+            with torch.no_grad():
+                y = lin(x[None, :])[0, 0] + float(off[i])
+                ref[i, k] = torch.sigmoid(y / float(T[k])).item()
+    np.testing.assert_allclose(c, ref, rtol=1e-13, atol=0)
+    # closed form: a one-hot w reads a single hidden coordinate of row (i, k)
+    for idx in (0, 5, d - 1):
+        w1 = np.zeros(d + r, np.float32)
+        w1[idx] = 1.0
+        c1, _ = orc.confidence(h, E, anchor, tok, w1, T)
+        hv = bf16_val(h[:, :, idx])
+        np.testing.assert_allclose(c1, 1.0 / (1.0 + np.exp(-hv / T[None, :].astype(np.float64))),
+                                   rtol=1e-15)
+    # one-hot on an embedding coordinate reads E of the previous token
+    w1 = np.zeros(d + r, np.float32)
+    w1[d + 3] = 1.0
+    c1, _ = orc.confidence(h, E, anchor, tok, w1, np.ones(g, np.float32))
+    prev = np.concatenate([anchor[:, None], tok[:, :-1]], axis=1)
+    ev = np.where(prev >= 0, bf16_val(E[np.maximum(prev, 0), 3]), 0.0)
+    np.testing.assert_allclose(c1, 1.0 / (1.0 + np.exp(-ev)), rtol=1e-15)
+
+
+def test_confidence_flag_marks_fp32_rounding_midpoints(orc):
+    """c = sigma(y): y = 2^-23 puts c at 1/2 + 2^-25 (to within 1e-21), the
+    midpoint between the fp32 neighbours 1/2 and 1/2 + 2^-24, so the flag fires;
+    y = 2^-22 puts c at 1/2 + 2^-24 (less 2e-21), an fp32 value, so it does not."""
+    d, V, r = 1, 4, 8
+    E = bf16(np.zeros((V, r)))
+    h = bf16(np.ones((1, 2, d)))
+    anchor = np.array([-1], np.int32)
+    tok = np.array([[-1, -1]], np.int32)
+    T = np.ones(2, np.float32)
+    for y, want in ((2.0 ** -23, 1), (2.0 ** -22, 0)):
+        w = np.zeros(d + r, np.float32)
+        w[0] = y
+        c, fl = orc.confidence(h, E, anchor, tok, w, T)
+        assert abs(c[0, 0] - (0.5 + y / 4)) < 1e-20
+        assert list(fl[0]) == [want, want], (y, fl)
+    # generic values are not flagged
+    rng = np.random.default_rng(17)
+    h = bf16(rng.normal(0, 1, (50, 4, 16)))
+    E = bf16(rng.normal(0, 0.1, (V, r)))
+    w = rng.normal(0, 0.1, 16 + r).astype(np.float32)
+    _, fl = orc.confidence(h, E, rng.integers(0, V, 50).astype(np.int32),
+                           rng.integers(0, V, (50, 4)).astype(np.int32), w, np.ones(4, np.float32))
+    assert fl.sum() == 0
+
+
+# ---------------------------------------------------------------------------
+# Near-boundary flags: where a differing decision is allowed
+# ---------------------------------------------------------------------------
+
+def _two_logit_row(p0):
+    """fp32 logits (0, l1) whose fp64 softmax puts mass close to p0 on token 0, and
+    that mass exactly as the oracle's fp64 softmax computes it."""
+    l1 = np.float32(np.log(1.0 / p0 - 1.0))
+    row = np.array([0.0, l1], np.float32)
+    p0_exact = 1.0 / (1.0 + np.exp(np.float64(l1)))
+    return row, p0_exact
+
+
+def test_sampling_flag_window(orc):
+    """A draft draw is flagged exactly when u lies within 1e-6 of a boundary of the
+    fp64 CDF: rows built so that the boundary after token 0 sits at known
+    distances from the draw's u."""
+    E = bf16(np.zeros((2, 8)))
+    W2 = bf16(np.zeros((2, 8)))
+    seed, rnd = 3, 4
+    checked = 0
+    for req in range(40):
+        u = orc.uniform(seed, rnd, req, 0, 0)
+        if not 0.05 < u < 0.95:
+            continue
+        for dist in (-3e-6, -1.5e-6, -0.6e-6, -0.2e-6, 0.2e-6, 0.6e-6, 1.5e-6, 3e-6):
+            row, p0 = _two_logit_row(u + dist)
+            gap = p0 - u                      # the boundary's actual distance from u
+            if abs(abs(gap) - 1e-6) < 5e-8:
+                continue                      # too close to the window's edge to call
+            tok, _, _, fl = orc.draft(row[None, None, :], E, W2, np.array([-1], np.int32),
+                                      np.array([req], np.int32), 1.0, seed, rnd)
+            assert tok[0, 0] == (0 if u < p0 else 1)
+            assert fl[0, 0] == (abs(gap) < 1e-6), (req, dist, gap)
+            checked += 1
+    assert checked > 100
+
+
+def test_greedy_near_tie_flag(orc):
+    """Greedy flag: the top-2 gap is within 2 ulp of the maximum plus the bound on
+    the bias's summation order.  Without a bias the bound is 2 ulp: gaps of 0, 1
+    and 2 ulp at 1.5 (ulp 2^-23) are flagged, 3 and more are not; with a bias the
+    window widens by (r + 1) 2^-24 times the two columns' sums of |E W2|."""
+    ulp = 2.0 ** -23
+    E = bf16(np.zeros((3, 8)))
+    W2 = bf16(np.zeros((3, 8)))
+    for k_ulp, want in ((0, 1), (1, 1), (2, 1), (3, 0), (40, 0)):
+        row = np.array([-5.0, 1.5 - k_ulp * ulp, 1.5], np.float32)
+        tok, q, _, fl = orc.draft(row[None, None, :], E, W2, np.array([-1], np.int32),
+                                  np.array([0], np.int32), 0.0, 0, 0)
+        assert tok[0, 0] == (1 if k_ulp == 0 else 2) and q[0, 0] == 1.0   # ties: lowest index
+        assert fl[0, 0] == want, k_ulp
+    # with a bias: E[0] = 1 everywhere, W2 columns of +-1/8: |bias| sums of 1 per column
+    r = 8
+    E = bf16(np.ones((3, r)))
+    W2 = bf16(np.concatenate([np.zeros((1, r)), np.full((1, r), 0.125), np.full((1, r), -0.125)]))
+    # biases: column 1 +1, column 2 -1; window = 2 ulp + 9 * 2^-24 * 2 = 2 ulp(2.5) + 1.07e-6
+    for gap, want in ((0.5e-6, 1), (1.4e-6, 1), (4e-6, 0)):
+        row = np.array([-5.0, 1.5, np.float32(3.5 + gap)], np.float32)
+        lg, absdot = orc.markov_logits(row, E, W2, 0)
+        real_gap = float(lg[2]) - float(lg[1])
+        bound = 2 * 2.0 ** -22 + 9 * 2.0 ** -24 * (absdot[1] + absdot[2])
+        tok, _, _, fl = orc.draft(row[None, None, :], E, W2, np.array([0], np.int32),
+                                  np.array([0], np.int32), 0.0, 0, 0)
+        assert fl[0, 0] == (real_gap <= bound) == bool(want), (gap, real_gap, bound)
+
+
+def test_accept_flag_window(orc):
+    """An accept test is flagged exactly when |u - p/q| < 1e-6: q chosen so that the
+    ratio p/q sits at known distances from the test's u."""
+    E = bf16(np.zeros((2, 8)))
+    W2 = bf16(np.zeros((2, 8)))
+    seed, rnd = 1, 2
+    target = np.array([[[0.3, -0.4], [0.0, 0.0]]], np.float32)
+    p0 = sp_softmax(target[0, 0].astype(np.float64))[0]
+    base = np.zeros((1, 1, 2), np.float32)
+    checked = 0
+    for req in range(30):
+        u = orc.uniform(seed, rnd, req, 0, 1)
+        if not 0.05 < u < 0.95:
+            continue
+        for dist in (-4e-6, -0.5e-6, 0.5e-6, 4e-6):
+            q = np.array([[p0 / (u + dist)]])
+            ratio = p0 / q[0, 0]
+            v = orc.verify(target, base, E, W2, np.array([-1], np.int32),
+                           np.array([[0]], np.int32), q, np.array([1], np.int32),
+                           np.array([req], np.int32), 1.0, seed, rnd)
+            assert v["accept"][0, 0] == int(u <= ratio)
+            assert v["flag_acc"][0, 0] == (abs(u - ratio) < 1e-6), (req, dist)
+            checked += 1
+    assert checked > 40
+
+
+def test_teacher_forcing_hooks(orc):
+    """The comparison hooks: a forced draft token is the chain's token from then on
+    (the next position's bias and draw use it), and a forced accept decision is
+    the one the first rejection follows."""
+    rng = np.random.default_rng(18)
+    V, r, g = 30, 8, 3
+    base = rng.normal(0, 1, (1, g, V)).astype(np.float32)
+    E = bf16(rng.normal(0, 0.3, (V, r)))
+    W2 = bf16(rng.normal(0, 0.3, (V, r)))
+    anchor = np.array([4], np.int32)
+    req = np.array([9], np.int32)
+    tok, q, _, _ = orc.draft(base, E, W2, anchor, req, 1.0, 0, 5)
+    forced = (tok[0, 0] + 7) % V
+    force = np.array([[forced, -1, -1]], np.int32)
+    tf, qf, _, _ = orc.draft(base, E, W2, anchor, req, 1.0, 0, 5, force=force)
+    assert tf[0, 0] == forced
+    lg0, _ = orc.markov_logits(base[0, 0], E, W2, 4)
+    p0, _ = orc.softmax(lg0, 1.0)
+    assert qf[0, 0] == p0[forced]
+    lg1, _ = orc.markov_logits(base[0, 1], E, W2, forced)
+    p1, _ = orc.softmax(lg1, 1.0)
+    x1, _ = orc.inverse_cdf(p1, orc.uniform(0, 5, 9, 1, 0))
+    assert tf[0, 1] == x1 and qf[0, 1] == p1[x1]
+    # accept forcing: force a rejection at position 1 of a fully accepted block
+    tgt = np.concatenate([base, base[:, :1]], axis=1)   # p = q: every test accepts
+    v = orc.verify(tgt, base, E, W2, anchor, tok, q, np.array([g], np.int32), req, 1.0, 0, 5)
+    assert v["n_accept"][0] == g
+    fa = np.array([[-1, 0, -1]], np.int8)
+    v2 = orc.verify(tgt, base, E, W2, anchor, tok, q, np.array([g], np.int32), req, 1.0, 0, 5,
+                    force_acc=fa)
+    assert v2["n_accept"][0] == 1 and v2["accept"][0, 1] == 0
+
+
 # ---------------------------------------------------------------------------
 # Prefix scheduler
 # ---------------------------------------------------------------------------

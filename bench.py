@@ -41,8 +41,10 @@ DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/build.py",
                  "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_device.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_launch.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_call_traffic_qwen3-4b-R64-g7-V151936.txt")
 METRIC = "verified draft positions/sec (draft+verify) and % of MI355X HBM roofline"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+HEADLINE_WORKLOAD = 4            # the largest single-GPU configuration
+PER_WORKLOAD = ((1, "sampling"), (2, "sampling"), (3, "sampling"), (4, "greedy"))
 UNIT = "verified draft positions/s"
 
 
@@ -92,12 +94,17 @@ def draft_sources_digest():
     return h.hexdigest()
 
 
+def traffic_file(workload):
+    short = workload.split("-r256")[0]
+    return os.path.join(ROOT, "profiles", f"draft_call_traffic_{short}.txt")
+
+
 def profiled_traffic(workload, path):
     """HBM bytes of one dsp_draft_step call (FETCH_SIZE and WRITE_SIZE of its
     kernels, scaled by a plain copy) from the committed profile, or None when that
     profile is of other kernel sources, another workload or another draft path."""
     try:
-        kv = dict(line.split(None, 1) for line in open(TRAFFIC_FILE).read().splitlines()
+        kv = dict(line.split(None, 1) for line in open(traffic_file(workload)).read().splitlines()
                   if line and not line.startswith("#"))
     except OSError:
         return None
@@ -213,46 +220,12 @@ def copy_bandwidth(nbytes=1 << 30, reps=5):
     return gbs
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--mode", choices=["sampling", "greedy"], default=None)
-    ap.add_argument("--sets", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the rounds as eager launches instead of graph replays")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy five times (the known-size "
-                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}), flush=True)
-        return
-
-    if args.gpus != 1:
-        print(f"bench.py measures the one-GPU path only; --gpus {args.gpus} is not supported "
-              "(the path shards by request; see the multi-GPU design notes)", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-
-    wl = WORKLOADS[args.workload]
-    mode = args.mode or wl.modes[-1]
+def measure(wl, mode, args, steps, warmup, with_cpu, log_prefix=""):
+    """Time one workload: K graph-replayed rounds (value), an eager pass with per-entry-
+    point events, the draft call's roofline and the bias GEMM's MFMA rate."""
     greedy = mode == "greedy"
     temp = 0.0 if greedy else wl.temperature
-    dsp.lib()
-    log(f"workload {wl.name}, {mode}, building {args.sets} input sets")
+    log(f"{log_prefix}workload {wl.name}, {mode}, building {args.sets} input sets")
     sets = [make_inputs(wl, s, device="cuda", layout=BENCH_LAYOUT) for s in range(args.sets)]
     inp0 = sets[0]
     R, g, V, r = inp0["R"], inp0["gamma"], inp0["V"], inp0["r"]
@@ -291,12 +264,12 @@ def main():
             ev[4].record(s)
 
     draft_path = probe_draft_path(lambda f: draft(0, flags=f))
-    log(f"draft path: {draft_path}")
+    log(f"{log_prefix}draft path: {draft_path}")
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         one_round(i)
     torch.cuda.synchronize()
-    K = args.steps
+    K = steps
 
     # eager pass: per entry point event timing (roofline, breakdown)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
@@ -305,10 +278,11 @@ def main():
     torch.cuda.synchronize()
     e_start.record(stream)
     for i in range(K):
-        one_round(args.warmup + i, evs[i])
+        one_round(warmup + i, evs[i])
     e_end.record(stream)
     torch.cuda.synchronize()
     eager_ms_per_step = e_start.elapsed_time(e_end) / K
+    rd.check()
 
     # throughput pass: the same K rounds replayed from one captured graph each
     if args.eager:
@@ -321,7 +295,7 @@ def main():
         for i in range(K):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr, stream=cap):
-                one_round(args.warmup + i, s=cap)
+                one_round(warmup + i, s=cap)
             graphs.append(gr)
         for gr in graphs[:2]:
             gr.replay()
@@ -335,6 +309,8 @@ def main():
         ms_per_step = t_ev[0].elapsed_time(t_ev[K]) / K
         round_ms = np.array([t_ev[i].elapsed_time(t_ev[i + 1]) for i in range(K)])
         timing = "HIP graph replay, one graph per round"
+        rd.check()
+        del graphs
 
     # per entry point (event-bracketed) average durations, in ms
     draft_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
@@ -346,7 +322,7 @@ def main():
         # workload's mode, which sets l_r = gamma again)
         ce = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         for i in range(K):
-            inp = sets[(args.warmup + i) % len(sets)]
+            inp = sets[(warmup + i) % len(sets)]
             ce[i][0].record(stream)
             rd.confidence(inp, stream)
             ce[i][1].record(stream)
@@ -359,11 +335,12 @@ def main():
     # replay the timed rounds (deterministic) to count verified positions
     len_sum = rej = 0
     for i in range(K):
-        one_round(args.warmup + i)
+        one_round(warmup + i)
         L = rd.len.cpu().numpy()
         na = rd.n_accept.cpu().numpy()
         len_sum += int(L.sum())
         rej += int((na < L).sum())
+    rd.check()
     len_per_round = len_sum / K
     rej_per_round = rej / K
     value = len_per_round / (ms_per_step * 1e-3)
@@ -381,7 +358,7 @@ def main():
         gd = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gd, stream=cap):
             for i in range(K):
-                draft(args.warmup + i, s=cap)
+                draft(warmup + i, s=cap)
         gd.replay()
         torch.cuda.synchronize()
         d0 = torch.cuda.Event(enable_timing=True)
@@ -390,8 +367,10 @@ def main():
         gd.replay()
         d1.record(stream)
         torch.cuda.synchronize()
+        rd.check()
         draft_avg_s = d0.elapsed_time(d1) / K * 1e-3
         draft_timing = "one graph of K draft calls back to back"
+        del gd
     achieved = call_bytes / draft_avg_s / 1e9
     traffic = profiled_traffic(wl.name, draft_path)
     kernels = ("run_clear_kernel + draft_run_kernel (one persistent launch, all gamma positions)"
@@ -402,11 +381,19 @@ def main():
             "kernel": f"dsp_draft_step, {g} positions: {kernels}",
             "bytes_per_launch": int(call_bytes), "avg_launch_us": round(draft_avg_s * 1e6, 2),
             "timing": draft_timing}
+    # the Markov-bias contraction [R x r] . [r x V] per draft position, bf16 MFMA
+    bias_flop = 2.0 * R * r * V * g
+    mfma = {"flop_per_call": bias_flop,
+            "achieved_tflops": round(bias_flop / draft_avg_s / 1e12, 1),
+            "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "utilisation": round(bias_flop / draft_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "what": "2 R r V flop per draft position over the whole draft call's time"}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if inp0["base"].dtype == torch.bfloat16 else "f32",
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if inp0["base"].dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "R": R, "gamma": g, "V": V, "r": r, "d": inp0["d"],
                    "mode": mode, "scheduler": "on" if wl.mode == 1 else "off (every position verified)",
@@ -425,21 +412,80 @@ def main():
                             "schedule": round(float(sched_ms.mean()) * 1e3, 2),
                             "verify": round(float(ver_ms.mean()) * 1e3, 2)},
         "verified_per_round": len_per_round, "drafted_per_round": R * g,
+        "rejections_per_round": rej_per_round,
         "timing": timing, "eager_ms_per_step": round(eager_ms_per_step, 5),
         "roofline": roof,
+        "bias_gemm_mfma": mfma,
         "round_us_percentiles": {"p10": round(float(np.percentile(round_ms, 10)) * 1e3, 2),
                                  "median": round(float(np.median(round_ms)) * 1e3, 2),
                                  "p90": round(float(np.percentile(round_ms, 90)) * 1e3, 2)},
     }
-    copy_gbs = copy_bandwidth()
-    result["copy_bandwidth"] = {"GBs": round(copy_gbs, 1),
-                                "round_frac_of_copy": round(A / (copy_gbs * 1e9) / (ms_per_step * 1e-3), 4),
-                                "what": "1 GiB device-to-device copy, bytes read + written per second"}
-    if not args.no_cpu_baseline:
+    if with_cpu:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, inp0, temp, args.cpu_seconds)
         result["cpu_baseline_threads"] = cpu_baseline_threads(wl, inp0, temp, args.cpu_seconds)
         result["cpu_host"] = {"model": host_cpu(), "threads": len(os.sched_getaffinity(0))}
+    del sets, inp0, rd
+    torch.cuda.empty_cache()
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=HEADLINE_WORKLOAD)
+    ap.add_argument("--mode", choices=["sampling", "greedy"], default=None)
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-workload", action="store_true",
+                    help="time only the headline workload")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the rounds as eager launches instead of graph replays")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy five times (the known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}), flush=True)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py measures the one-GPU path only; --gpus {args.gpus} is not supported "
+              "(the path shards by request; see the multi-GPU design notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    dsp.lib()
+    wl = WORKLOADS[args.workload]
+    mode = args.mode or wl.modes[-1]
+    result = measure(wl, mode, args, args.steps, args.warmup, not args.no_cpu_baseline)
+    if not args.no_per_workload and args.workload == HEADLINE_WORKLOAD and args.mode is None:
+        per = {}
+        for wid, m in PER_WORKLOAD:
+            w2 = WORKLOADS[wid]
+            r2 = measure(w2, m, args, max(10, args.steps // 2), max(3, args.warmup // 2), False,
+                         log_prefix="  ")
+            per[f"{w2.name}/{m}"] = {k: r2[k] for k in (
+                "value", "unit", "ms_per_step", "round_roofline", "roofline", "bias_gemm_mfma",
+                "entry_points_us", "verified_per_round", "round_us_percentiles")}
+            per[f"{w2.name}/{m}"]["draft_path"] = r2["config"]["draft_path"]
+        result["per_workload"] = per
+    copy_gbs = copy_bandwidth()
+    A = result["round_roofline"]["algorithmic_bytes"]
+    result["copy_bandwidth"] = {"GBs": round(copy_gbs, 1),
+                                "round_frac_of_copy": round(A / (copy_gbs * 1e9) / (result["ms_per_step"] * 1e-3), 4),
+                                "what": "1 GiB device-to-device copy, bytes read + written per second"}
     print(json.dumps(result), flush=True)
 
 

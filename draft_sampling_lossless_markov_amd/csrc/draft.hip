@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
         double ls = 0.0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            w[i] = (mt[i] == -INFINITY) ? 0.0 : st[i] * exp(((double)mt[i] - (double)M) * (double)inv_temp);
+            w[i] = st[i] * rescale64(mt[i], M, inv_temp);
             ls += w[i];
         }
         const double Z = block_sum256(ls, sh);
@@ -100,8 +100,13 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
             if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
             *reinterpret_cast<uint4*>(e_row + kk) = ev;
         }
+        const float m_t = pp[tsel].m;   // the tile's reference in the partial
         const float z = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, sh);
-        double e1[1] = {(v < V) ? (double)wexp(z - M, fold_itl(inv_temp)) : 0.0};
+        // the pass's own weights: relative to the tile maximum, moved onto the
+        // row's reference by the partials' fp64 factor
+        const float mref = (m_t == -INFINITY) ? 0.0f : m_t;
+        double e1[1] = {(v < V) ? (double)wexp(z - mref, fold_itl(inv_temp)) * rescale64(m_t, M, inv_temp)
+                                : 0.0};
         double b2;
         const int loc = block_locate<1>(e1, target - before, &b2, sh, 1);
         if (tid == loc) {
@@ -118,13 +123,14 @@ __global__ __launch_bounds__(256) void draft_pick_kernel(
 // ---------------------------------------------------------------------------
 constexpr size_t kRunCtlBytes = 256;
 
-// partials of either path (the streaming path's 256-column tiles or a
-// persistent run's tiles), then the run's barrier words
+// partials of either path (the streaming path's 256-column tiles, 16 bytes each,
+// or a persistent run's tiles: two positions' slots of two 8-byte words), then
+// the error word
 static size_t draft_part_bytes(int R, int V)
 {
     const size_t n_vt = (size_t)((V + kVocabTile - 1) / kVocabTile);
     const size_t n_run = std::min<size_t>((size_t)((V + 31) / 32), (size_t)kRunTilesMax);
-    const size_t b = (size_t)R * std::max(n_vt, n_run) * sizeof(Part);
+    const size_t b = (size_t)R * std::max(n_vt * sizeof(Part), n_run * 4 * sizeof(uint64_t));
     return (b + 255) / 256 * 256;
 }
 
@@ -264,7 +270,7 @@ hipError_t launch_run_t(const RunArgs& ra, int G, int ncu, bool give_up, hipStre
         occ.store(o, std::memory_order_relaxed);
     }
     if (G > occ.load(std::memory_order_relaxed) * ncu) return hipSuccess;
-    const int64_t n_slots = 2 * (int64_t)ra.R * ra.n_t;
+    const int64_t n_slots = 4 * (int64_t)ra.R * ra.n_t;
     const int64_t n_clear = std::max<int64_t>(n_slots, (int64_t)ra.R * ra.n_steps);
     const int cg = (int)std::min<int64_t>(1024, (n_clear + 255) / 256);
     hipLaunchKernelGGL(run_clear_kernel, dim3(cg), dim3(256), 0, s, ra.slots, n_slots, ra.tok, ra.R,

@@ -61,7 +61,8 @@ struct RunArgs {
     uint64_t seed;
     uint32_t round;
     int n_t;                 // tiles of 32 * TU columns
-    uint64_t* slots;         // [2][R][n_t] partials: (max, sum) or (max, index)
+    uint64_t* slots;         // [2][R][n_t][2] partials: words (max, 0) and the fp64 sum
+                             // of weights relative to the max, or (max, index) and 0
     unsigned* ctl;           // [0] error word
 };
 
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
     const int G = gridDim.x;
     const int tw = 4 * (int)blockIdx.x + wave;
     const int v_tile = tw * 32 * TU;
-    const float itL = fold_itl(a.inv_temp);
+    const Itl itL = fold_itl(a.inv_temp);
     const int prow = unit_row_col(c32);   // unit row of this lane's A fragments
 
     bf16x8 afrag[NR][kKSteps];
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
     const int RB = (R + kPassBlock - 1) / kPassBlock;
     for (int s = 0; s < a.n_steps; ++s) {
         const int k = a.k0 + s;
-        uint64_t* slots = a.slots + (int64_t)(k & 1) * R * n_t;
+        uint64_t* slots = a.slots + (int64_t)(k & 1) * R * n_t * 2;
 
         // ---- the previous token of every request (drawn in this launch: wait
         // for it; the anchor or an earlier call's token: read it)
@@ -335,20 +336,18 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                     gi[gidx] = best < V ? best : 0x7fffffff;
                 } else {
                     m = xmax<32>(m);
+                    // fp32 weights relative to the group maximum (a pick's rescan forms
+                    // the same ones), summed in fp64 element by element.  A reference
+                    // at the group's maximum keeps the dominant weights' exponents near
+                    // 0, where the argument's rounding (relative to its size) costs least
                     const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked group
-                    // per unit a pairwise fp32 tree over the lane's 16 weights,
-                    // then fp64 across units and the lane pair
                     double sd = 0.0;
 #pragma unroll
                     for (int u = 0; u < nu; ++u) {
-                        float w[16];
+                        float zu[16];
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) w[j] = wexp(acc[u][j] - mref, itL);
-#pragma unroll
-                        for (int hw = 8; hw >= 1; hw >>= 1)
-#pragma unroll
-                            for (int j = 0; j < hw; ++j) w[j] = w[j] + w[j + hw];
-                        sd += (double)w[0];
+                        for (int j = 0; j < 16; ++j) zu[j] = acc[u][j];
+                        sd += sum_w64(zu, mref, itL);
                     }
                     gm[gidx] = m;
                     gs[gidx] = xsum<32>(sd);
@@ -357,25 +356,34 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
             group(std::integral_constant<int, 0>{}, std::integral_constant<int, NR>{});
             if constexpr (NL > 0) group(std::integral_constant<int, NR>{}, std::integral_constant<int, TU>{});
 
-            uint64_t word;
+            uint64_t word, word2;
             if constexpr (GREEDY) {
                 ArgMax am{gm[0], gi[0]};
                 if constexpr (NL > 0) am = argmax_merge(am, ArgMax{gm[1], gi[1]});
                 am = xargmax<32>(am);
                 word = pack2(am.v, (uint32_t)am.i);
+                word2 = 0ull;
             } else {
                 float m = gm[0];
                 double sum = gs[0];
                 if constexpr (NL > 0) {
-                    const float mm = fmaxf(gm[0], gm[1]);
-                    if (mm != -INFINITY)
-                        sum = gs[0] * (double)wexp(gm[0] - mm, itL) + gs[1] * (double)wexp(gm[1] - mm, itL);
+                    // the group holding the maximum keeps its sum, the other is moved
+                    // onto that reference (one fp64 exponential)
+                    const bool first = gm[0] >= gm[1];
+                    const float mm = first ? gm[0] : gm[1];
+                    const double f = rescale64(first ? gm[1] : gm[0], mm, a.inv_temp);
+                    if (mm != -INFINITY) sum = first ? gs[0] + gs[1] * f : gs[0] * f + gs[1];
                     m = mm;
                 }
-                word = pack2(m, __float_as_uint((float)sum));
+                word = pack2(m, 0u);
+                word2 = (uint64_t)__double_as_longlong(sum);
             }
             const int n = n0 + c32;
-            if (h == 0 && n < R && tw < n_t) dev_store_u64(slots + (int64_t)n * n_t + tw, word);
+            if (h == 0 && n < R && tw < n_t) {
+                uint64_t* sp = slots + 2 * ((int64_t)n * n_t + tw);
+                dev_store_u64(sp, word);
+                dev_store_u64(sp + 1, word2);
+            }
             if constexpr (RING == 1) {
                 if (b + 1 < RB) load_base(n0 + kPassBlock, std::integral_constant<int, 0>{});
             }
@@ -388,17 +396,19 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
         // ================= phase 2: one workgroup per request ==================
         for (int n = blockIdx.x; n < R; n += G) {
             const int64_t out = (int64_t)n * gamma + k;
-            uint64_t* ps = slots + (int64_t)n * n_t;
+            uint64_t* ps = slots + 2 * (int64_t)n * n_t;
             constexpr int PER = kRunTilesMax / 256;
-            // the request's partials: wait until every tile's has landed
-            uint64_t wv[PER];
+            // the request's partials: wait until both words of every tile's have
+            // landed (word 2 i + 1 of thread t belongs to tile t PER + i)
+            uint64_t wv[PER], ws2[PER];
             {
                 bool miss = false;
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
                     const int t = tid * PER + i;
-                    wv[i] = (t < n_t) ? dev_load_u64(ps + t) : 0ull;
-                    miss |= (wv[i] == kRunSlotEmpty);
+                    wv[i] = (t < n_t) ? dev_load_u64(ps + 2 * t) : 0ull;
+                    ws2[i] = (t < n_t) ? dev_load_u64(ps + 2 * t + 1) : 0ull;
+                    miss |= (wv[i] == kRunSlotEmpty) || (ws2[i] == kRunSlotEmpty);
                 }
                 for (unsigned spins = 1; miss; ++spins) {
                     __builtin_amdgcn_s_sleep(2);
@@ -407,8 +417,9 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
 #pragma unroll
                     for (int i = 0; i < PER; ++i) {
                         const int t = tid * PER + i;
-                        if (wv[i] == kRunSlotEmpty) wv[i] = dev_load_u64(ps + t);
-                        miss |= (wv[i] == kRunSlotEmpty);
+                        if (wv[i] == kRunSlotEmpty) wv[i] = dev_load_u64(ps + 2 * t);
+                        if (ws2[i] == kRunSlotEmpty) ws2[i] = dev_load_u64(ps + 2 * t + 1);
+                        miss |= (wv[i] == kRunSlotEmpty) || (ws2[i] == kRunSlotEmpty);
                     }
                 }
             }
@@ -437,18 +448,17 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 float M = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
-                    const bool in = tid * PER + i < n_t;
+                    // (a word left empty by a wait that gave up reads as an empty tile)
+                    const bool in = tid * PER + i < n_t && wv[i] != kRunSlotEmpty && ws2[i] != kRunSlotEmpty;
                     mt[i] = in ? slot_m(wv[i]) : -INFINITY;
-                    sw[i] = in ? (double)__uint_as_float(slot_x(wv[i])) : 0.0;
+                    sw[i] = in ? __longlong_as_double((long long)ws2[i]) : 0.0;
                     M = fmaxf(M, mt[i]);
                 }
                 M = block_max256(M, L.sh);
                 double ls = 0.0;
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
-                    sw[i] = (mt[i] == -INFINITY)
-                                ? 0.0
-                                : sw[i] * exp(((double)mt[i] - (double)M) * (double)a.inv_temp);
+                    sw[i] = sw[i] * rescale64(mt[i], M, a.inv_temp);
                     ls += sw[i];
                 }
                 const double Z = block_sum256(ls, L.sh);
@@ -524,7 +534,20 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 }
                 lds_barrier();
                 const float z = vin ? xb + L.sh.lg[tid] : -INFINITY;
-                double e1[1] = {vin ? (double)wexp(z - M, itL) : 0.0};
+                // the pass's own weights: relative to the maximum of the column's
+                // unit group (units 0 .. NR-1 in registers, NR .. TU-1 in LDS), moved
+                // onto the tile's reference by the same factor as the pass (1 for the
+                // group holding the maximum), then onto the row's
+                const int g1 = (tid >= 32 * NR) ? 1 : 0;
+                float gmx[2];
+                block_max2(g1 == 0 ? z : -INFINITY, g1 == 1 ? z : -INFINITY, gmx, L.sh);
+                const float mg = gmx[g1];
+                const bool first = gmx[0] >= gmx[1];
+                const float m_t = first ? gmx[0] : gmx[1];
+                const double fg = ((g1 == 0) == first) ? 1.0 : rescale64(mg, m_t, a.inv_temp);
+                const float mref = (mg == -INFINITY) ? 0.0f : mg;
+                double e1[1] = {vin ? (double)wexp(z - mref, itL) * fg * rescale64(m_t, M, a.inv_temp)
+                                    : 0.0};
                 double b2;
                 const int loc = block_locate<1>(e1, target - before, &b2, L.sh, 1);
                 tok_out = vt0 + loc;
@@ -548,7 +571,10 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
                     const int t = tid * PER + i;
-                    if (t < n_t) dev_store_u64(ps + t, kRunSlotEmpty);
+                    if (t < n_t) {
+                        dev_store_u64(ps + 2 * t, kRunSlotEmpty);
+                        dev_store_u64(ps + 2 * t + 1, kRunSlotEmpty);
+                    }
                 }
             }
         }

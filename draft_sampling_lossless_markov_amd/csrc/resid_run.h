@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
     const int G = gridDim.x;
     const int tw = 4 * (int)blockIdx.x + wave;
     const int v_tile = tw * 32 * TU;
-    const float itL = fold_itl(a.inv_temp);
+    const Itl itL = fold_itl(a.inv_temp);
     const int prow = unit_row_col(c32);
 
     // ================= phase 1: residual mass of every (queued request, tile) ====
@@ -191,18 +191,18 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
                 acc[u] = mfma32_bf16(av, bv, acc[u]);
             }
         }
-        // max(0, p - q) per column in fp32 (the arithmetic of the streaming
-        // residual pass), four running sums, fp64 across the lane pair
-        float d4[4] = {0.f, 0.f, 0.f, 0.f};
+        // max(0, p - q) per column with the arithmetic of the streaming residual
+        // pass (fp32 weights, fp64 products, difference and sums)
+        double d2[2] = {0.0, 0.0};
 #pragma unroll
         for (int u = 0; u < TU; ++u)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const float zd = Logit<uint16_t>::raw_at(&dw[sl % RING_D][u][j >> 3], j & 7) + acc[u][j];
                 const float xt = Logit<uint16_t>::raw_at(&xw[sl][u][j >> 3], j & 7);
-                d4[j & 3] += fmaxf(wexp(xt - Mt[sl], itL) * invZt[sl] - wexp(zd - Md[sl], itL) * invZd[sl], 0.0f);
+                d2[j & 1] += resid_w(wexp(xt - Mt[sl], itL), invZt[sl], wexp(zd - Md[sl], itL), invZd[sl]);
             }
-        const double sum = xsum<32>((double)((d4[0] + d4[1]) + (d4[2] + d4[3])));
+        const double sum = xsum<32>(d2[0] + d2[1]);
         if (h == 0 && ok && tw < n_t)
             dev_store_u64(a.slots + (int64_t)ee * n_t + tw, (uint64_t)__double_as_longlong(sum));
         if constexpr (RING_D == 1) {
@@ -315,17 +315,14 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
                     }
                 }
                 lds_barrier();
+                // the rows' statistics exactly as phase 1 used them
                 const float Md = (float)sd0;
-                const double invZd = 1.0 / sd1;
-                const double invZt = 1.0 / zt;
+                const float invZd = (float)(1.0 / sd1);
+                const float invZt = (float)(1.0 / zt);
                 double rho[1] = {0.0};
                 if (vin) {
                     const float zd = xb + L.sh.lg[tid];
-                    if (zd != -INFINITY) {
-                        const double pq = (double)wexp(xt - Mt, itL) * invZt;
-                        const double qq = (double)wexp(zd - Md, itL) * invZd;
-                        rho[0] = fmax(pq - qq, 0.0);
-                    }
+                    rho[0] = resid_w(wexp(xt - Mt, itL), invZt, wexp(zd - Md, itL), invZd);
                 }
                 double b2;
                 const int loc = block_locate<1>(rho, tgt - before, &b2, L.sh, 1);
@@ -356,9 +353,7 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
             double ls = 0.0;
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
-                w[i] = (mt[i] == -INFINITY)
-                           ? 0.0
-                           : st[i] * exp(((double)mt[i] - (double)M) * (double)a.inv_temp);
+                w[i] = st[i] * rescale64(mt[i], M, a.inv_temp);
                 ls += w[i];
             }
             const double Z = block_sum256(ls, L.sh);
@@ -367,7 +362,12 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
             const int tsel = block_locate<PER>(w, tgt, &before, L.sh, 0);
             const uint16_t* trow = a.target + (int64_t)n * a.ts.rs + (int64_t)row_j * a.ts.ps;
             const int v = tsel * kVocabTile + tid;
-            double e1[1] = {(v < V) ? (double)wexp(Logit<uint16_t>::at(trow, v) - M, itL) : 0.0};
+            // verify_rows' own weights: relative to the tile maximum, moved onto M
+            const float m_t = pp[tsel].m;
+            const float mref = (m_t == -INFINITY) ? 0.0f : m_t;
+            double e1[1] = {(v < V) ? (double)wexp(Logit<uint16_t>::at(trow, v) - mref, itL) *
+                                          rescale64(m_t, M, a.inv_temp)
+                                    : 0.0};
             double b2;
             const int loc = block_locate<1>(e1, tgt - before, &b2, L.sh, 1);
             if (tid == 0) a.y[n] = tsel * kVocabTile + loc;

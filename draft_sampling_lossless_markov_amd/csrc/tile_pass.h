@@ -27,22 +27,73 @@ namespace dsp {
 enum PassKind : int { kSample = 0, kGreedy = 1, kResidual = 2 };
 
 // ---------------------------------------------------------------------------
-// softmax weight exp(x), x <= 0 (x = -inf gives 0): the hardware exp2 of
-// x log2 e.  Accuracy budget: the sums these weights enter are accumulated in
-// fp64, which is what keeps the inverse-CDF decisions in step with an fp64
-// reference at vocabularies of 10^5; a more careful argument reduction did not
-// change a single decision in measurement and costs four times the ALU work.
+// Softmax weights exp((z - ref) / T) = 2^((z - ref) log2(e) / T), z <= ref (z =
+// -inf gives 0), by the hardware exp2 (on gfx950 correctly rounded for ~95% of
+// arguments, within 0.8 ulp for all, measured).  log2(e) / T is carried as an
+// fp32 pair hi + lo folded once per kernel, and the argument formed with one
+// rounding: fl32(log2 e / T) alone is off by up to 6e-8 relative, a systematic
+// change of temperature that shifts a whole row's CDF.  Every pass, combine and
+// rescan of a row forms its weights this same way, so partials and rescans agree.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float exp_w(float x)
+struct Itl {
+    float hi, lo;
+};
+
+// hi is taken strictly below log2(e) / T, so lo > 0: a masked logit (d = -inf)
+// then forms -inf * lo = -inf and the weight 0 (a negative lo would give
+// -inf * hi + inf = NaN)
+__host__ __device__ inline Itl fold_itl(float inv_temp)
 {
-    return __builtin_amdgcn_exp2f(x * 1.44269502162933349609375f);
+    const double t = (double)inv_temp * 1.4426950408889634074;   // log2(e) / T
+    float hi = (float)t;
+    if ((double)hi >= t) hi = nextafterf(hi, 0.0f);
+    return Itl{hi, (float)(t - (double)hi)};
 }
 
-// exp((z - ref) / T) with itL = log2(e) / T folded once per kernel; every pass,
-// combine and rescan of a row uses this same form so partials and rescans agree.
-__device__ __forceinline__ float wexp(float d, float itL) { return __builtin_amdgcn_exp2f(d * itL); }
+__device__ __forceinline__ float wexp(float d, Itl itL)
+{
+    return __builtin_amdgcn_exp2f(fmaf(d, itL.hi, d * itL.lo));
+}
 
-__host__ __device__ inline float fold_itl(float inv_temp) { return inv_temp * 1.44269502162933349609375f; }
+// exp((m0 - m1) / T) in fp64: the factor that moves a sum of weights taken
+// relative to m0 onto the reference m1 (0 for an empty sum, m0 = -inf).  Every
+// merge of partials, every combine and every rescan of a row uses it, so a
+// rescan reproduces the pass's sums up to fp64 rounding.
+__device__ __forceinline__ double rescale64(float m0, float m1, float inv_temp)
+{
+    return (m0 == -INFINITY) ? 0.0 : exp(((double)m0 - (double)m1) * (double)inv_temp);
+}
+
+// Sum of a lane's fp32 softmax weights exp((z_s - ref) / T), accumulated in fp64
+// element by element as they are produced (one chain: no weight array and no
+// second accumulator is kept live).  An fp32 tree over a tile's weights rounds at the magnitude of its
+// dominant weights, and that rounding alone moves the inverse-CDF boundaries of
+// a 1.5e5-word row by ~1.5e-9 on average -- enough to flip ~2e-4 of the draws
+// against an fp64 reference; the weights' own rounding moves them ~5x less.
+template <int N>
+__device__ __forceinline__ double sum_w64(const float (&z)[N], float ref, Itl itL)
+{
+    // in groups of eight kept apart for the scheduler, so that it does not hoist
+    // every exponential ahead of the chain and hold all their results live
+    static_assert(N % 8 == 0, "groups of eight");
+    double c = 0.0;
+#pragma unroll
+    for (int g = 0; g < N; g += 8) {
+#pragma unroll
+        for (int s = g; s < g + 8; ++s) c += (double)wexp(z[s] - ref, itL);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return c;
+}
+
+// One column's residual max(0, p - q) from its fp32 target and draft weights
+// (relative to the rows' maxima) and the rows' fp32 inverse normalisers: the
+// products and the difference in fp64, so that cancellation between p and q
+// costs no precision beyond the weights' own.
+__device__ __forceinline__ double resid_w(float wt, float invZt, float wd, float invZd)
+{
+    return fmax((double)wt * (double)invZt - (double)wd * (double)invZd, 0.0);
+}
 
 // Partial of one 256-wide vocabulary tile of one row.
 //   softmax pass: m = max logit, s = sum exp((logit - m) / T) (fp64)
@@ -149,6 +200,7 @@ union PassLds {
     struct {
         uint16_t e[2][kPassBlock][kRankMax + kERowPad];
         Part red[2][4][kPassBlock];
+        float mx[2][4][kPassBlock];   // softmax: each wave's block maxima
     } s;
 };
 
@@ -211,6 +263,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
     __shared__ PassLds L;
     auto& e_tile = L.s.e;
     auto& red = L.s.red;
+    auto& mx = L.s.mx;
     constexpr int RW = Logit<LT>::kRaw;
     constexpr bool RES = (KIND == kResidual);
 
@@ -229,7 +282,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
     const int v_lane = v_blk + 32 * h;   // first of this lane's 32 columns
     const LT* __restrict__ base = static_cast<const LT*>(a.base);
     const LT* __restrict__ target = static_cast<const LT*>(a.target);
-    const float itL = fold_itl(a.inv_temp);
+    const Itl itL = fold_itl(a.inv_temp);
 
     bf16x8 afrag[2][kKSteps];
     stage_w2_frags(a.W2, V, r, vt * kVocabTile, L, afrag);
@@ -266,8 +319,10 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
 #pragma unroll
         for (int c = 0; c < kWords; ++c) {
             const int kk = (sq * kWords + c) * 8;
-            const bool live = ok && kk < r;
-            *reinterpret_cast<uint4*>(&e_tile[b][srow][kk]) = live ? eu[c] : make_uint4(0, 0, 0, 0);
+            // a dead row or a k-step past r stores zeros (masked, branch-free)
+            const uint32_t mk = (ok && kk < r) ? 0xFFFFFFFFu : 0u;
+            const uint4 v = eu[c];
+            *reinterpret_cast<uint4*>(&e_tile[b][srow][kk]) = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
         }
     };
 
@@ -389,17 +444,14 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
 #pragma unroll
             for (int s = 1; s < 32; ++s) m = fmaxf(m, z[s]);
             m = xmax<32>(m);
-            const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked block
-            float w[32];
-#pragma unroll
-            for (int s = 0; s < 32; ++s) w[s] = wexp(z[s] - mref, itL);
-            // pairwise tree over the lane's 32 weights (relative error below
-            // 5 * 2^-24), then fp64 across the lane pair, tiles and rows
-#pragma unroll
-            for (int hw = 16; hw >= 1; hw >>= 1)
-#pragma unroll
-                for (int s = 0; s < hw; ++s) w[s] = w[s] + w[s + hw];
-            res = Part{m, 0, xsum<32>((double)w[0])};
+            // the tile maximum over the four waves' blocks: every weight of the
+            // tile then has one reference, the tile's, which the partial records
+            // and a pick's rescan uses as it is
+            if (h == 0) mx[b][wave][c32] = m;
+            lds_barrier();
+            m = fmaxf(fmaxf(mx[b][0][c32], mx[b][1][c32]), fmaxf(mx[b][2][c32], mx[b][3][c32]));
+            const float mref = (m == -INFINITY) ? 0.0f : m;   // an all-masked tile
+            res = Part{m, 0, xsum<32>(sum_w64(z, mref, itL))};
         } else {   // kResidual
             const int e = min(n0 + c32, n_end - 1);
             const int n = a.list[e];
@@ -408,16 +460,15 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
             const float invZd = (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]);
             const float Mt = a.row_m[n];
             const float invZt = (float)(1.0 / a.row_z[n]);
-            // max(0, p - q) per column in fp32 (relative error ~1e-7 of the larger
-            // of p and q), four running fp32 sums over the lane's 32 columns, then
-            // fp64 across lanes, tiles and rows
-            float d4[4] = {0.f, 0.f, 0.f, 0.f};
+            // max(0, p - q) per column: fp32 weights, then the products, the
+            // difference and the sums in fp64 (the rescan of a pick repeats it)
+            double d2[2] = {0.0, 0.0};
 #pragma unroll
             for (int s = 0; s < 32; ++s) {
                 const float xt = Logit<LT>::raw_at(rt + (s >> 3) * RW, s & 7);
-                d4[s & 3] += fmaxf(wexp(xt - Mt, itL) * invZt - wexp(z[s] - Md, itL) * invZd, 0.0f);
+                d2[s & 1] += resid_w(wexp(xt - Mt, itL), invZt, wexp(z[s] - Md, itL), invZd);
             }
-            res = Part{0.f, 0, xsum<32>((double)((d4[0] + d4[1]) + (d4[2] + d4[3])))};
+            res = Part{0.f, 0, xsum<32>(d2[0] + d2[1])};
         }
         if (h == 0) red[b][wave][c32] = res;
         lds_barrier();
@@ -435,10 +486,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
                     p.m = mm.v;
                     p.idx = mm.i;
                 } else if constexpr (KIND == kSample) {
-                    const float mm = fmaxf(p.m, q.m);
-                    if (mm != -INFINITY)
-                        p.s = p.s * (double)wexp(p.m - mm, itL) + q.s * (double)wexp(q.m - mm, itL);
-                    p.m = mm;
+                    p.s += q.s;   // one reference (the tile maximum) throughout
                 } else {
                     p.s += q.s;
                 }
@@ -459,6 +507,7 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
 // ---------------------------------------------------------------------------
 struct PickScratch {
     float wmax[4];
+    float wmax2[2][4];
     double wsum[4];
     double scan[2][4];
     int hit[2][4];
@@ -475,6 +524,22 @@ __device__ __forceinline__ float block_max256(float v, PickScratch& sh)
     if (lane == 0) sh.wmax[wave] = v;
     lds_barrier();
     return fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
+}
+
+// two block maxima at once (one LDS barrier): out[i] = max over the block of v_i
+__device__ __forceinline__ void block_max2(float v0, float v1, float (&out)[2], PickScratch& sh)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    v0 = wave_max_f(v0);
+    v1 = wave_max_f(v1);
+    if (lane == 0) {
+        sh.wmax2[0][wave] = v0;
+        sh.wmax2[1][wave] = v1;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        out[i] = fmaxf(fmaxf(sh.wmax2[i][0], sh.wmax2[i][1]), fmaxf(sh.wmax2[i][2], sh.wmax2[i][3]));
 }
 
 __device__ __forceinline__ double block_sum256(double v, PickScratch& sh)

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 {
     constexpr int RW = Logit<LT>::kRaw;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const float itL = fold_itl(inv_temp);
+    const Itl itL = fold_itl(inv_temp);
     // the error word of the call: 0, or 1 under the give-up test hook (every wait
     // of the persistent residual launch then returns at once)
     if (blockIdx.x == 0 && tid == 0) {
@@ -158,17 +158,14 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
         const float mref = (m == -INFINITY) ? 0.0f : m;
-        // a pairwise fp32 tree over the lane's 32 weights, then fp64 across lanes
-        float w[32];
+        // fp32 weights relative to the tile maximum (the reference a pick's rescan
+        // recomputes), summed in fp64 per lane and across the tile's lanes
+        float x[32];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[8 * k + e] = wexp(Logit<LT>::raw_at(raw[k], e) - mref, itL);
-#pragma unroll
-        for (int hw = 16; hw >= 1; hw >>= 1)
-#pragma unroll
-            for (int i = 0; i < hw; ++i) w[i] = w[i] + w[i + hw];
-        double s = (double)w[0];
+            for (int e = 0; e < 8; ++e) x[8 * k + e] = Logit<LT>::raw_at(raw[k], e);
+        double s = sum_w64(x, mref, itL);
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
         if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
@@ -176,7 +173,8 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
         // summed: one partial per wave
         float mw = fmaxf(m, __shfl_xor(m, 8, kWave));
         mw = xmax<32>(xmax<16>(mw));
-        // (the rescale factor in fp32, as the persistent draft merges its groups)
+        // (an fp32 factor: these partials only give each row's normaliser, to
+        // ~1e-7; the draws use the tile partials and rescans)
         double sw = (m == -INFINITY) ? 0.0 : s * (double)wexp(m - mw, itL);
         sw += __shfl_xor(sw, 8, kWave);
         sw = xsum<32>(xsum<16>(sw));
@@ -257,7 +255,7 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
             double Z = 0.0;
 #pragma unroll
             for (int i = 0; i < PER; ++i)
-                if (pt[i].m != -INFINITY) Z += pt[i].s * exp(((double)pt[i].m - (double)M) * (double)inv_temp);
+                Z += pt[i].s * rescale64(pt[i].m, M, inv_temp);
             Z = wave_sum_d(Z);
             if (lane == 0) {
                 const double p = exp(((double)zx_j - (double)M) * (double)inv_temp) / Z;
@@ -333,7 +331,7 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     const int m = min(max(n_accept[n], 0), l);
     const int slot = ws.resid_slot[n];
     const double u = uniform24(seed, round, (uint32_t)n, (uint32_t)m, 2u);
-    const float itL = fold_itl(inv_temp);
+    const Itl itL = fold_itl(inv_temp);
 
     if (slot >= 0) {   // workgroup-uniform
         const Part* rp = ws.resid_part + (int64_t)slot * n_vt;
@@ -358,10 +356,11 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
             const int v = tsel * kVocabTile + tid;
             const float xb = (v < V) ? Logit<LT>::at(drow, v) : -INFINITY;
             const float xt = (v < V) ? Logit<LT>::at(trow, v) : -INFINITY;
+            // the rows' statistics exactly as the residual pass used them
             const float Md = (float)stats[2 * ((int64_t)n * gamma + m)];
-            const double invZd = 1.0 / stats[2 * ((int64_t)n * gamma + m) + 1];
+            const float invZd = (float)(1.0 / stats[2 * ((int64_t)n * gamma + m) + 1]);
             const float Mt = ws.row_m[n];
-            const double invZt = 1.0 / ws.row_z[n];
+            const float invZt = (float)(1.0 / ws.row_z[n]);
             if (tid < kRankMax / 8) {
                 const int kk = 8 * tid;
                 uint4 ev = make_uint4(0, 0, 0, 0);
@@ -369,12 +368,7 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
                 *reinterpret_cast<uint4*>(e_row + kk) = ev;
             }
             const float zd = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, sh);
-            double rho[1] = {0.0};
-            if (v < V && zd != -INFINITY) {
-                const double pv = (double)wexp(xt - Mt, itL) * invZt;
-                const double qv = (double)wexp(zd - Md, itL) * invZd;
-                rho[0] = fmax(pv - qv, 0.0);
-            }
+            double rho[1] = {(v < V) ? resid_w(wexp(xt - Mt, itL), invZt, wexp(zd - Md, itL), invZd) : 0.0};
             double b2;
             const int loc = block_locate<1>(rho, tgt - before, &b2, sh, 1);
             if (tid == 0) y[n] = tsel * kVocabTile + loc;
@@ -400,7 +394,7 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     double ls = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        w[i] = (mt[i] == -INFINITY) ? 0.0 : st[i] * exp(((double)mt[i] - (double)M) * (double)inv_temp);
+        w[i] = st[i] * rescale64(mt[i], M, inv_temp);
         ls += w[i];
     }
     const double Z = block_sum256(ls, sh);
@@ -409,7 +403,11 @@ __global__ __launch_bounds__(256) void verify_pick_kernel(
     const int tsel = block_locate<PER>(w, tgt, &before, sh, 0);
     const LT* trow = target + (int64_t)n * ts.rs + (int64_t)row_j * ts.ps;
     const int v = tsel * kVocabTile + tid;
-    double e1[1] = {(v < V) ? (double)wexp(Logit<LT>::at(trow, v) - M, itL) : 0.0};
+    // verify_rows' own weights: relative to the tile maximum, moved onto M
+    const float m_t = pp[tsel].m;
+    const float mref = (m_t == -INFINITY) ? 0.0f : m_t;
+    double e1[1] = {(v < V) ? (double)wexp(Logit<LT>::at(trow, v) - mref, itL) * rescale64(m_t, M, inv_temp)
+                            : 0.0};
     double b2;
     const int loc = block_locate<1>(e1, tgt - before, &b2, sh, 1);
     if (tid == 0) y[n] = tsel * kVocabTile + loc;

@@ -27,9 +27,11 @@ class Round:
         self.n_accept = torch.zeros((R,), dtype=i32, device=dev)
         self.y = torch.zeros((R,), dtype=i32, device=dev)
         self.p = torch.zeros((R, gamma), dtype=f32, device=dev)
-        self.ws_draft = torch.empty(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, R, gamma, V, r)),
+        # zero-filled, so that the workspaces' error words read "no give-up" even
+        # before their first call
+        self.ws_draft = torch.zeros(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, R, gamma, V, r)),
                                     dtype=torch.uint8, device=dev)
-        self.ws_verify = torch.empty(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, R, gamma, V, r)),
+        self.ws_verify = torch.zeros(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, R, gamma, V, r)),
                                      dtype=torch.uint8, device=dev)
 
     def draft(self, inp, temperature, seed, rnd, stream=None):

@@ -50,8 +50,9 @@ def test_workspace_sizes(L):
     assert dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 0, 4, 32, 8) == 0
     a = dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 64, 7, 151936, 256)
     # partials of the larger tiling (a persistent run's at most 1024 tiles per
-    # row), rounded to 256 bytes, then 256 bytes of barrier words
-    assert a == 64 * 1024 * 16 + 256
+    # row, two positions of two 8-byte words), rounded to 256 bytes, then 256
+    # bytes holding the error word
+    assert a == 64 * 1024 * 32 + 256
     assert dsp.dsp_workspace_size(dsp.DSP_WS_DRAFT, 3, 4, 32, 8) == 256 + 256
     b = dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, 64, 7, 151936, 256)
     assert b > 64 * 8 * 19 * 8

@@ -14,7 +14,7 @@ import torch
 
 import oracle as orc
 from oracle.compare import (Tally, compare_confidence, compare_draft, compare_schedule,
-                            compare_verify)
+                            compare_verify, round_parity)
 from draft_sampling_lossless_markov_amd import dsp
 from draft_sampling_lossless_markov_amd.engine import Round
 from draft_sampling_lossless_markov_amd.workloads import (BENCH_LAYOUT, WORKLOADS, Workload,
@@ -23,6 +23,13 @@ from draft_sampling_lossless_markov_amd.workloads import (BENCH_LAYOUT, WORKLOAD
 pytestmark = pytest.mark.gpu
 
 SEED = 0
+# host threads for the oracle's share of a comparison (plain C through ctypes,
+# which releases the GIL); at most 16, a GPU's share of its host
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+# sampling decisions compared over the whole module, and the differing ones (each
+# inside the oracle's near-boundary window, else the comparison fails outright)
+AGG = Tally()
 
 
 def _say(msg):
@@ -57,31 +64,34 @@ def custom(R, gamma, V, r, d, dtype, mode=1, temperature=1.0, offset=None, B_max
                     B_max if B_max is not None else R * (gamma + 1), mode, temperature)
 
 
-def run_both(inp_cpu, temperature, rnd, mode=None):
-    inp = to_dev(inp_cpu)
+ROUND_KEYS = ("tok", "q", "stats", "c", "len", "a", "B", "accept", "n_accept", "y", "p")
+
+
+def gpu_round(inp, temperature, rnd):
+    """One whole round on the GPU (inputs on the device); host copies of its outputs.
+    Raises if a bounded wait of a persistent launch gave up."""
     R, gamma, V, r = inp["R"], inp["gamma"], inp["V"], inp["r"]
     rd = Round(R, gamma, V, r)
-    rd.run(inp, temperature, SEED, rnd, mode=mode)
-    torch.cuda.synchronize()
-    g = {k: np_(getattr(rd, k)) for k in ("tok", "q", "stats", "c", "len", "a", "B", "accept",
-                                          "n_accept", "y", "p")}
-    o = orc.run_round(inp_cpu, temperature, SEED, rnd, mode=mode)
-    return g, o
+    rd.run(inp, temperature, SEED, rnd)
+    rd.check()
+    return {k: np_(getattr(rd, k)).copy() for k in ROUND_KEYS}
 
 
-def compare_round(g, o, greedy):
-    t = Tally()
-    td, div_at = compare_draft(g["tok"], g["q"], g["stats"], o["tok"], o["q"], o["stats"],
-                               o["flag_draft"], greedy)
-    t.add(td)
-    gamma = o["tok"].shape[1]
-    valid = np.arange(gamma)[None, :] <= div_at[:, None]
-    t.add(compare_confidence(g["c"], o["c"], o["flag_conf"], valid))
-    if np.all(div_at == gamma) and not np.any((g["c"].view(np.uint32) != o["c32"].view(np.uint32))):
-        t.add(compare_schedule(g["len"], g["a"], g["B"][0], o["len"], o["a"], o["B"]))
-        t.add(compare_verify(g, o, o["len"], greedy))
+def run_both(inp_cpu, temperature, rnd, subset=None):
+    """The GPU round and its chained, teacher-forced comparison with the oracle."""
+    inp = to_dev(inp_cpu)
+    g = gpu_round(inp, temperature, rnd)
+    res = round_parity(g, inp_cpu, temperature, SEED, rnd, subset=subset, threads=THREADS)
+    return g, res
+
+
+def check_round(res, greedy):
+    t = res["total"]
+    assert t.ok(), t.summary()
+    if greedy:
+        assert t.diverged == 0, t.summary()
     else:
-        t.skipped += 1
+        AGG.add(Tally(decisions=t.decisions, flagged=t.flagged, diverged=t.diverged))
     return t
 
 
@@ -109,10 +119,9 @@ def test_round_parity_small(case):
     tot = Tally()
     for rnd in range(6):
         inp = make_inputs(wl, rnd)
-        g, o = run_both(inp, temp, rnd)
-        tot.add(compare_round(g, o, temp == 0.0))
-    assert tot.ok(), tot.summary()
-    assert tot.mismatch_rate() <= 1e-4, tot.summary()
+        _, res = run_both(inp, temp, rnd)
+        tot.add(check_round(res, temp == 0.0))
+    _say(f"  {tot.summary()}")
 
 
 LAYOUT_CASES = [
@@ -135,10 +144,8 @@ def test_round_parity_layouts(case, layout):
     tot = Tally()
     for rnd in range(3):
         inp = make_inputs(wl, rnd, layout=layout)
-        g, o = run_both(inp, temp, rnd)
-        tot.add(compare_round(g, o, temp == 0.0))
-    assert tot.ok(), tot.summary()
-    assert tot.mismatch_rate() <= 1e-4, tot.summary()
+        _, res = run_both(inp, temp, rnd)
+        tot.add(check_round(res, temp == 0.0))
 
 
 # draft paths: the persistent launch (W2 slice resident on chip, all positions in
@@ -196,11 +203,14 @@ def test_draft_paths_vs_oracle(case):
                                                 np_(inp_cpu["anchor"]), S, temp, SEED, rnd)
         for name, (tok, q, st) in (("persistent", pers), ("streaming", strm)):
             t, _ = compare_draft(tok, q, st, o_tok, o_q, o_stats, o_flag, greedy, S)
-            # every differing draw lies within 1e-6 of a boundary of the oracle's CDF
-            # (t.ok()); their count stays within 1e-3 of the draws, or two in a case
-            # this small
+            # greedy: identical; sampling: every differing draw lies within 1e-6 of
+            # a boundary of the oracle's CDF (t.ok()), and the differing draws count
+            # towards the module's rate, bounded by 1e-4 of all sampled decisions
             assert t.ok(), (name, t.summary())
-            assert t.diverged <= max(2, 1e-3 * t.decisions), (name, t.summary())
+            if greedy:
+                assert t.diverged == 0, (name, t.summary())
+            else:
+                AGG.add(Tally(decisions=t.decisions, flagged=t.flagged, diverged=t.diverged))
         if greedy:
             assert np.array_equal(pers[0], strm[0])
         del rd, inp
@@ -243,7 +253,7 @@ def test_residual_paths_vs_oracle(case):
             g_v = {k: np_(getattr(rd, k)).copy() for k in ("accept", "n_accept", "y", "p")}
             t = compare_verify(g_v, o_v, lens.numpy(), False, S)
             assert t.ok(), (flags, t.summary())
-            assert t.diverged <= max(2, 1e-3 * t.decisions), (flags, t.summary())
+            AGG.add(Tally(decisions=t.decisions, flagged=t.flagged, diverged=t.diverged))
             ys.append(g_v["y"])
         n_rej = int((ys[0] >= 0).sum())
         _say(f"  {n_rej} draws, paths differ on {int((ys[0] != ys[1]).sum())}")
@@ -275,9 +285,8 @@ def test_tiny_workload_1000_rounds():
         tot = Tally()
         for rnd in range(1000):
             inp = make_inputs(wl, rnd)
-            g, o = run_both(inp, temp, rnd)
-            tot.add(compare_round(g, o, temp == 0.0))
-        assert tot.ok(), tot.summary()
+            _, res = run_both(inp, temp, rnd)
+            tot.add(check_round(res, temp == 0.0))
         assert tot.flag_rate() <= 1e-4 and tot.mismatch_rate() <= 1e-4, tot.summary()
         _say(f"  {tot.summary()}")
 
@@ -287,9 +296,8 @@ def test_no_markov_bias_and_zero_lengths():
     wl = custom(40, 4, 700, 16, 8, torch.bfloat16, B_max=40)
     inp = make_inputs(wl, 0)
     inp["anchor"] = torch.full_like(inp["anchor"], -1)
-    g, o = run_both(inp, 1.0, 3)
-    t = compare_round(g, o, False)
-    assert t.ok(), t.summary()
+    g, res = run_both(inp, 1.0, 3)
+    check_round(res, False)
     assert np.all(g["len"] == 0) and g["B"][0] == 40
 
 
@@ -416,46 +424,245 @@ def test_full_size_stages(wid):
     torch.cuda.empty_cache()
 
 
+def _chain_subset(R, n_cu=256):
+    """Requests whose whole round the oracle recomputes at full size: the first
+    32-request block (one block of the persistent and streaming passes), a request
+    past the compute-unit count (a persistent workgroup then draws two), the middle
+    one and the last."""
+    S = set(range(min(R, 32)))
+    S |= {R // 2 + 1, R - 1}
+    if R > n_cu:
+        S |= {n_cu + 3}
+    return np.array(sorted(x for x in S if 0 <= x < R), np.int32)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_full_size_rounds_chained(wid):
+    """Whole rounds at the workloads' full sizes, chained draft -> confidence ->
+    schedule -> verify exactly as the bench runs them (position-major base logits,
+    the default implementation paths): the confidence head and the scheduler
+    compared over every request, draft and verification recomputed by the oracle
+    for a request subset, three rounds per mode, teacher-forced at flagged draws."""
+    wl = WORKLOADS[wid]
+    inp = make_inputs(wl, 0, device="cuda", layout=BENCH_LAYOUT)
+    S = _chain_subset(inp["R"])
+    for mode_name in wl.modes:
+        temp = 0.0 if mode_name == "greedy" else wl.temperature
+        tot = Tally()
+        for rnd in range(3):
+            _say(f"full-size chained round: {wl.name} {mode_name} round {rnd}, "
+                 f"{len(S)} requests recomputed")
+            g = gpu_round(inp, temp, rnd)
+            res = round_parity(g, inp, temp, SEED, rnd, subset=S, threads=THREADS)
+            t = check_round(res, temp == 0.0)
+            tot.add(t)
+            _say(f"  B={res['B']} sum(len)={res['len_sum']} {t.summary()}")
+        assert tot.skipped == 0
+    del inp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("temp", [1.0, 0.0])
+def test_persistent_give_up_is_reported(temp):
+    """A persistent launch started as if a bounded wait had given up (the test hook:
+    every wait returns at once, every kernel runs to its end) is reported by
+    dsp_workspace_status as DSP_ERR_TIMEOUT; the next normal call clears it."""
+    R, gamma, V, r = 70, 5, 1000, 24
+    wl = custom(R, gamma, V, r, 8, torch.bfloat16)
+    inp = to_dev(make_inputs(wl, 0, layout="position"))
+    rd = Round(R, gamma, V, r)
+    P = dsp.DSP_PATH_PERSISTENT
+    for flags, expect in ((P | dsp.DSP_FLAG_TEST_GIVE_UP, True), (P, False),
+                          (dsp.DSP_PATH_STREAMING | dsp.DSP_FLAG_TEST_GIVE_UP, False)):
+        _say(f"give-up report: draft flags {flags:#x} temperature {temp}")
+        dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q, rd.stats,
+                           0, temp, SEED, 1, rd.ws_draft, n_steps=gamma, flags=flags)
+        if expect:
+            with pytest.raises(dsp.DspError) as ei:
+                dsp.dsp_workspace_status(dsp.DSP_WS_DRAFT, rd.ws_draft, R, gamma, V, r)
+            assert ei.value.status == dsp.DSP_ERR_TIMEOUT
+        else:
+            dsp.dsp_workspace_status(dsp.DSP_WS_DRAFT, rd.ws_draft, R, gamma, V, r)
+    if temp > 0:
+        rd.len.fill_(gamma)
+        for flags, expect in ((P | dsp.DSP_FLAG_TEST_GIVE_UP, True), (P, False)):
+            _say(f"give-up report: verify flags {flags:#x}")
+            rd.verify(inp, temp, SEED, 1, flags=flags)
+            if expect:
+                with pytest.raises(dsp.DspError) as ei:
+                    dsp.dsp_workspace_status(dsp.DSP_WS_VERIFY, rd.ws_verify, R, gamma, V, r)
+                assert ei.value.status == dsp.DSP_ERR_TIMEOUT
+            else:
+                dsp.dsp_workspace_status(dsp.DSP_WS_VERIFY, rd.ws_verify, R, gamma, V, r)
+    # the outputs of a normal round after a reported give-up match the oracle
+    _, res = run_both(make_inputs(wl, 0), temp, 2)
+    check_round(res, temp == 0.0)
+
+
+def test_hip_path_output_law_chi2():
+    """Losslessness of the whole HIP path (page "为什么DSpark 可以加速推理？", section on
+    the mathematics of speculative decoding: the output law is the target's; page
+    "DSpark.让每一轮计算，多走几步", lossless section and its two-token example):
+    V = 8, 2048 requests that share each target row p_j but have their own draft
+    rows, Markov bias and confidences, the scheduler on (ragged l_r), 5000 rounds
+    (>= 10^7 trials at position 0).  The token emitted at every reached position j
+    (x_j if accepted, else the correction; the bonus at j = l_r) must follow p_j:
+    chi-square per position, Bonferroni over positions."""
+    from scipy import stats as sst
+    R, gamma, V, r, d = 2048, 8, 8, 8, 16
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    rows_t = (torch.randn((gamma + 1, V), generator=gen) * 1.5).to(torch.bfloat16)
+    target = rows_t[None].expand(R, gamma + 1, V).contiguous().cuda()
+    base = (torch.randn((R, gamma, V), generator=gen) * 1.5).to(torch.bfloat16).cuda()
+    E = (torch.randn((V, r), generator=gen) * 0.5).to(torch.bfloat16).cuda()
+    W2 = (torch.randn((V, r), generator=gen) * 0.5).to(torch.bfloat16).cuda()
+    h = torch.randn((R, gamma, d), generator=gen).to(torch.bfloat16).cuda()
+    w = (torch.randn(d + r, generator=gen) * 0.5).cuda()
+    T = torch.full((gamma,), 1.0).cuda()
+    anchor = torch.randint(0, V, (R,), generator=gen, dtype=torch.int32).cuda()
+    B_max = R * (gamma + 1)
+    sps = (1.0 / (12.0 + 0.1 * torch.arange(1, B_max + 1, dtype=torch.float64)
+                  + 0.0008 * torch.arange(1, B_max + 1, dtype=torch.float64) ** 2)).float().cuda()
+    inp = dict(base=base, target=target, E=E, W2=W2, h=h, w=w, T=T, offset=None, anchor=anchor,
+               sps=sps, B_max=B_max, mode=1, tau0=0.0)
+    rd = Round(R, gamma, V, r)
+    counts = torch.zeros((gamma + 1) * V, dtype=torch.int64, device="cuda")
+    pos = torch.arange(gamma + 1, device="cuda")[None, :]
+    lens = torch.zeros(gamma + 1, dtype=torch.int64, device="cuda")
+    rounds = 5000
+    for rnd in range(rounds):
+        rd.run(inp, 1.0, SEED, rnd)
+        n = rd.n_accept.long()[:, None]
+        emitted = torch.cat([rd.tok.long(), torch.zeros((R, 1), dtype=torch.long, device="cuda")], 1)
+        emitted = torch.where(pos == n, rd.y.long()[:, None], emitted)
+        reached = pos <= n
+        counts += torch.bincount((pos * V + emitted)[reached], minlength=(gamma + 1) * V)
+        lens += torch.bincount(rd.len.long(), minlength=gamma + 1)
+        if rnd % 1000 == 0:
+            _say(f"chi2 round {rnd}")
+    rd.check()
+    counts = counts.view(gamma + 1, V).cpu().numpy()
+    p = torch.softmax(rows_t.double(), dim=-1).numpy()
+    _say(f"  trials per position {counts.sum(1).tolist()}; l_r histogram {lens.cpu().tolist()}")
+    assert counts[0].sum() >= 10 ** 7
+    alpha = 1e-4 / (gamma + 1)
+    for j in range(gamma + 1):
+        nj = counts[j].sum()
+        if nj < 1000:
+            continue
+        res = sst.chisquare(counts[j], p[j] * nj)
+        _say(f"  position {j}: n={nj} p-value={res.pvalue:.3g}")
+        assert res.pvalue > alpha, (j, counts[j].tolist(), (p[j] * nj).tolist())
+    assert len([j for j in range(gamma + 1) if counts[j].sum() >= 1000]) >= 3
+
+
+_REPLAY_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+from draft_sampling_lossless_markov_amd.engine import Round
+from draft_sampling_lossless_markov_amd.workloads import make_inputs
+from tests.test_gpu_parity import custom, to_dev, ROUND_KEYS
+wl = custom(70, 5, 1000, 24, 100, torch.bfloat16)
+inp = to_dev(make_inputs(wl, 4, layout="position"))
+out = {}
+for rnd in range(int(sys.argv[2]), int(sys.argv[3])):
+    rd = Round(70, 5, 1000, 24)
+    rd.run(inp, 1.0, 0, rnd)
+    rd.check()
+    for k in ROUND_KEYS:
+        out[f"{rnd}_{k}"] = getattr(rd, k).cpu().numpy()
+np.savez(sys.argv[4], **out)
+print("child done", flush=True)
+"""
+
+
+def test_cross_process_replay(tmp_path):
+    """Rounds [0, 6) in this process equal rounds [3, 6) recomputed in a fresh
+    process: every round is a pure function of its inputs and (seed, round)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    wl = custom(70, 5, 1000, 24, 100, torch.bfloat16)
+    inp = to_dev(make_inputs(wl, 4, layout="position"))
+    here = {}
+    for rnd in range(6):
+        rd = Round(70, 5, 1000, 24)
+        rd.run(inp, 1.0, 0, rnd)
+        rd.check()
+        here[rnd] = {k: np_(getattr(rd, k)).copy() for k in ROUND_KEYS}
+    out = tmp_path / "replay.npz"
+    _say("cross-process replay: child process for rounds 3..5")
+    r = subprocess.run([sys.executable, "-c", _REPLAY_CHILD, root, "3", "6", str(out)],
+                       cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    other = np.load(out)
+    for rnd in range(3, 6):
+        for k in ROUND_KEYS:
+            assert np.array_equal(here[rnd][k], other[f"{rnd}_{k}"]), (rnd, k)
+    # different rounds do differ
+    assert not np.array_equal(here[3]["tok"], here[4]["tok"])
+
+
 def test_full_vocab_sampling_mismatch_rate():
-    """Qwen3-4B-shaped rows (V = 151936): 19200 draft draws at position 0 over 300
-    rounds.  Every draw that differs from the oracle must have u within 1e-6 of
-    a boundary of the oracle's fp64 CDF; the rate of such differing draws is
-    bounded by the fp32 arithmetic (exp rounding and bias summation order leave
-    a CDF error of a few 1e-9 against ~1.5e5 boundaries)."""
+    """Qwen3-4B-shaped rows (V = 151936): 409600 draft draws at position 0 over 6400
+    rounds.  Every draw that differs from the oracle must have u within 1e-6 of a
+    boundary of the oracle's fp64 CDF, and the differing draws must stay at or
+    below 1e-4 of all draws (a rate of 5e-5 gives ~20 of them, against 41)."""
     wl = WORKLOADS[1]
     inp = make_inputs(wl, 0, device="cuda", layout=BENCH_LAYOUT)
     R, gamma, V, r = inp["R"], inp["gamma"], inp["V"], inp["r"]
     E_h, W2_h = orc.bf16_bits(inp["E"]), orc.bf16_bits(inp["W2"])
     anchor = np_(inp["anchor"])
     base0 = orc.host_logits(inp["base"][:, 0])
-    cdfs, probs = [], []
-    for i in range(R):
+
+    def law(i):
         lg, _ = orc.markov_logits(base0[i], E_h, W2_h, int(anchor[i]))
         p, _ = orc.softmax(lg, 1.0)
-        probs.append(p)
-        cdfs.append(np.cumsum(p))
+        return p, np.cumsum(p)
+
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        laws = list(ex.map(law, range(R)))
     rd = Round(R, gamma, V, r)
-    decisions = mismatched = flagged = 0
-    worst = 0.0
-    for rnd in range(300):
+    rounds = 6400
+    toks = torch.zeros((rounds, R), dtype=torch.int32, device="cuda")
+    qs = torch.zeros((rounds, R), dtype=torch.float32, device="cuda")
+    for rnd in range(rounds):
         dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok, rd.q,
                            rd.stats, 0, 1.0, SEED, rnd, rd.ws_draft)
-        tok = np_(rd.tok[:, 0])
-        q = np_(rd.q[:, 0])
-        for i in range(R):
-            u = orc.uniform(SEED, rnd, i, 0, 0)
-            c = cdfs[i]
-            x = min(int(np.searchsorted(c, u, side="right")), V - 1)
-            lo = c[x - 1] if x > 0 else 0.0
-            dist = min(u - lo, c[x] - u)
-            decisions += 1
-            flagged += dist < 1e-6
-            if tok[i] != x:
-                assert dist < 1e-6, (rnd, i, int(tok[i]), x, dist)
-                mismatched += 1
-                worst = max(worst, dist)
-            else:
-                assert abs(q[i] - probs[i][x]) <= 1e-5 * probs[i][x]
+        toks[rnd] = rd.tok[:, 0]
+        qs[rnd] = rd.q[:, 0]
+        if rnd % 1600 == 0:
+            _say(f"  full-vocab draws: round {rnd}")
+    rd.check()
+    toks, qs = np_(toks), np_(qs)
+    decisions = mismatched = flagged = 0
+    worst = 0.0
+    for i in range(R):
+        p, c = laws[i]
+        u = np.array([orc.uniform(SEED, rnd, i, 0, 0) for rnd in range(rounds)])
+        x = np.minimum(np.searchsorted(c, u, side="right"), V - 1)
+        lo = np.where(x > 0, c[np.maximum(x - 1, 0)], 0.0)
+        dist = np.minimum(u - lo, c[x] - u)
+        decisions += rounds
+        flagged += int((dist < 1e-6).sum())
+        bad = toks[:, i] != x
+        assert np.all(dist[bad] < 1e-6), (i, np.nonzero(bad)[0][:5], dist[bad][:5])
+        mismatched += int(bad.sum())
+        if bad.any():
+            worst = max(worst, float(dist[bad].max()))
+        good = ~bad
+        assert np.all(np.abs(qs[good, i] - p[x[good]]) <= 1e-5 * p[x[good]])
     _say(f"  decisions={decisions} flagged(1e-6)={flagged} mismatched={mismatched} "
-         f"worst boundary distance of a mismatch={worst:.3g}")
-    assert mismatched <= 1e-3 * decisions
+         f"rate={mismatched / decisions:.3g} worst boundary distance of a mismatch={worst:.3g}")
+    AGG.add(Tally(decisions=decisions, flagged=flagged, diverged=mismatched))
+    assert mismatched <= 1e-4 * decisions
+
+
+def test_zz_sampling_mismatch_rate_over_the_module():
+    """Every sampled decision compared in this module (drafts, accept tests,
+    corrections and bonus draws): the differing ones, each inside the oracle's
+    near-boundary window, are at most 1e-4 of them."""
+    _say(f"module aggregate: {AGG.summary()} rate={AGG.mismatch_rate():.3g}")
+    assert AGG.decisions > 10 ** 5
+    assert AGG.diverged <= 1e-4 * AGG.decisions, AGG.summary()

@@ -82,6 +82,34 @@ bool known_path(unsigned f)
 int path_of(unsigned f) { return (int)(f & ~DSP_FLAG_TEST_GIVE_UP); }
 bool give_up_of(unsigned f) { return (f & DSP_FLAG_TEST_GIVE_UP) != 0u; }
 
+// the arguments dsp_draft_step and dsp_draft_step_noalloc share
+dsp_status check_draft(const char* fn, const void* base, dsp_dtype dtype, int64_t base_rs,
+                       int64_t base_ps, const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
+                       int32_t* tok, float* q, double* stats, int R, int gamma, int V, int r, int k,
+                       int n_steps, unsigned flags, float temperature)
+{
+    if (!base || !E || !W2 || !anchor || !tok || !q || !stats)
+        return fail(DSP_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+    if (dtype != DSP_F32 && dtype != DSP_BF16)
+        return fail(DSP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    dsp_status st = check_markov(R, gamma, V, r);
+    if (st != DSP_OK) return st;
+    if (k < 0 || k >= gamma)
+        return fail(DSP_ERR_INVALID_ARG, "%s: k = %d outside [0, gamma)", fn, k);
+    if (!known_path(flags))
+        return fail(DSP_ERR_INVALID_ARG, "%s: unknown flags %u", fn, flags);
+    if (n_steps < 1 || n_steps > gamma - k)
+        return fail(DSP_ERR_INVALID_ARG, "%s: n_steps = %d outside [1, gamma - k] (k = %d)", fn,
+                    n_steps, k);
+    st = check_strides(fn, "base", base_rs, base_ps);
+    if (st != DSP_OK) return st;
+    if (!(temperature >= 0.0f) || std::isinf(temperature))
+        return fail(DSP_ERR_INVALID_ARG, "%s: temperature must be finite and >= 0", fn);
+    if (!aligned16(base) || !aligned16(E) || !aligned16(W2))
+        return fail(DSP_ERR_INVALID_ARG, "%s: base, E and W2 must be 16-byte aligned", fn);
+    return DSP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,25 +172,9 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                           unsigned flags, float temperature, uint64_t seed, uint32_t round,
                           void* ws, size_t ws_bytes, void* stream)
 {
-    if (!base || !E || !W2 || !anchor || !tok || !q || !stats)
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: null pointer argument");
-    if (dtype != DSP_F32 && dtype != DSP_BF16)
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: unknown dtype %d", (int)dtype);
-    dsp_status st = check_markov(R, gamma, V, r);
+    dsp_status st = check_draft("dsp_draft_step", base, dtype, base_rs, base_ps, E, W2, anchor, tok,
+                                q, stats, R, gamma, V, r, k, n_steps, flags, temperature);
     if (st != DSP_OK) return st;
-    if (k < 0 || k >= gamma)
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: k = %d outside [0, gamma)", k);
-    if (!known_path(flags))
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: unknown flags %u", flags);
-    if (n_steps < 1 || n_steps > gamma - k)
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: n_steps = %d outside [1, gamma - k] (k = %d)",
-                    n_steps, k);
-    st = check_strides("dsp_draft_step", "base", base_rs, base_ps);
-    if (st != DSP_OK) return st;
-    if (!(temperature >= 0.0f) || std::isinf(temperature))
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: temperature must be finite and >= 0");
-    if (!aligned16(base) || !aligned16(E) || !aligned16(W2))
-        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step: base, E and W2 must be 16-byte aligned");
     const size_t need = dsp::draft_workspace_bytes(R, V);
     if (!ws || ws_bytes < need)
         return fail(DSP_ERR_WORKSPACE, "dsp_draft_step: workspace of %zu bytes, %zu needed",
@@ -176,6 +188,32 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                                              seed, round,
                                              ws, static_cast<hipStream_t>(stream)),
                       "dsp_draft_step launch");
+}
+
+dsp_status dsp_draft_step_noalloc(const void* base, dsp_dtype dtype, int64_t base_rs,
+                                  int64_t base_ps, const uint16_t* E, const uint16_t* W2,
+                                  const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
+                                  int gamma, int V, int r, int k, int n_steps, unsigned flags,
+                                  float temperature, uint64_t seed, uint32_t round, void* stream)
+{
+    dsp_status st = check_draft("dsp_draft_step_noalloc", base, dtype, base_rs, base_ps, E, W2,
+                                anchor, tok, q, stats, R, gamma, V, r, k, n_steps, flags, temperature);
+    if (st != DSP_OK) return st;
+    const size_t need = dsp::draft_workspace_bytes(R, V);
+    if (need > dsp::kStaticScratchBytes)
+        return fail(DSP_ERR_WORKSPACE,
+                    "dsp_draft_step_noalloc: these sizes need %zu bytes of scratch, more than the "
+                    "static %zu",
+                    need, dsp::kStaticScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = dsp::static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "dsp_draft_step_noalloc: static scratch address");
+    return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
+                                             dtype == DSP_BF16, E, W2, anchor, tok, q,
+                                             stats, R, gamma, V, r, k, n_steps, path_of(flags),
+                                             give_up_of(flags), temperature, seed, round, ws,
+                                             static_cast<hipStream_t>(stream)),
+                      "dsp_draft_step_noalloc launch");
 }
 
 dsp_status dsp_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,

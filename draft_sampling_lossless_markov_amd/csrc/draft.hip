@@ -325,6 +325,33 @@ hipError_t try_launch_run(const uint16_t* base, RowStrides bs, const uint16_t* E
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free draft entry point: one array per device,
+// holding what the workspace argument holds for dsp_draft_step.  In host code the
+// array's name is not a device address: the address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr)
+{
+    constexpr int kDevs = 64;
+    static std::atomic<void*> addr[kDevs];
+    int d = 0;
+    hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess) return e;
+    if (d < 0 || d >= kDevs) return hipErrorInvalidDevice;
+    void* p = addr[d].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[d].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 bool run_geometry(int V, RunGeometry* g)
 {
     const int ncu = device_cus();

@@ -26,6 +26,12 @@ __host__ __device__ inline bool rows_vec(RowStrides s, int V, int align)
 }
 
 size_t draft_workspace_bytes(int R, int V);
+
+// Bytes of the per-device static scratch that dsp_draft_step_noalloc uses as its
+// workspace, and its device address on the current device (looked up once per
+// device with hipGetSymbolAddress).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(void** ptr);
 size_t verify_workspace_bytes(int R, int gamma, int V);
 // the error word of a workspace: nonzero when a bounded wait of the last call
 // on it gave up

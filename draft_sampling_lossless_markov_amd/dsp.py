@@ -27,8 +27,8 @@ DSP_PATH_AUTO, DSP_PATH_STREAMING, DSP_PATH_PERSISTENT = 0, 1, 2
 DSP_FLAG_TEST_GIVE_UP = 0x100
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
-            "dsp_workspace_status", "dsp_draft_step", "dsp_confidence", "dsp_schedule",
-            "dsp_verify")
+            "dsp_workspace_status", "dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence",
+            "dsp_schedule", "dsp_verify")
 
 _lib = None
 
@@ -66,11 +66,14 @@ def lib():
     I64 = C.c_int64
     L.dsp_draft_step.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, I, U32, F, U64,
                                  U32, P, SZ, P]
+    L.dsp_draft_step_noalloc.argtypes = [P, I, I64, I64, P, P, P, P, P, P, I, I, I, I, I, I, U32,
+                                         F, U64, U32, P]
     L.dsp_confidence.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P]
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
     L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
                              I, I, U32, F, U64, U32, P, SZ, P]
-    for f in ("dsp_draft_step", "dsp_confidence", "dsp_schedule", "dsp_verify"):
+    for f in ("dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence", "dsp_schedule",
+              "dsp_verify"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -128,6 +131,18 @@ def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, rou
                                 _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V, r, int(k),
                                 int(n_steps), int(flags), float(temperature), int(seed), int(round_),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsp_draft_step_noalloc(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_,
+                           stream=None, n_steps=1, flags=DSP_PATH_AUTO):
+    """dsp_draft_step without a workspace (the library's static per-device scratch)."""
+    R, gamma, V = base.shape
+    r = E.shape[1]
+    rs, ps = _rows(base, "base")
+    _check(lib().dsp_draft_step_noalloc(_ptr(base), _dtype(base), rs, ps, _ptr(E), _ptr(W2),
+                                        _ptr(anchor), _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V,
+                                        r, int(k), int(n_steps), int(flags), float(temperature),
+                                        int(seed), int(round_), _stream(stream)))
 
 
 def dsp_confidence(h, E, anchor, tok, w, T, offset, c, stream=None):

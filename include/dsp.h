@@ -176,6 +176,25 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                           size_t ws_bytes, void* stream);
 
 /*
+ * dsp_draft_step_noalloc -- dsp_draft_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments, the same results bit for bit,
+ * without the workspace.  Its scratch is a static array of the library, 16 MiB
+ * on each device it runs on, held until the process ends; every call on a
+ * device shares it, so calls that overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller.  Sizes whose workspace
+ * (dsp_workspace_size(DSP_WS_DRAFT, ...)) exceeds 16 MiB return
+ * DSP_ERR_WORKSPACE before any HIP call.  No call allocates or frees memory.  A
+ * bounded wait that gives up is not reported (dsp_workspace_status needs a
+ * workspace); the outputs of such a call are undefined.
+ */
+dsp_status dsp_draft_step_noalloc(const void* base, dsp_dtype dtype, int64_t base_rs,
+                                  int64_t base_ps, const uint16_t* E, const uint16_t* W2,
+                                  const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
+                                  int gamma, int V, int r, int k, int n_steps, unsigned flags,
+                                  float temperature, uint64_t seed, uint32_t round, void* stream);
+
+/*
  * dsp_confidence -- confidence head with sequential temperature scaling.
  *
  * Page "DeepSeek联合北大最新文章DSpark", section 2.1: c_k is the probability that

@@ -166,3 +166,23 @@ def test_confidence_and_verify_validation(L):
     assert v == 1 and b"flags" in L.dsp_last_error()
     v = L.dsp_verify(*two, 1, *[P(FAKE)] * 11, 4, 4, 32, 8, 0, 1.0, 0, 0, P(FAKE + 8), 1 << 20, None)
     assert v == 3 and b"aligned" in L.dsp_last_error()
+
+
+def test_noalloc_draft_validation(L):
+    """The allocation-free draft entry point validates like dsp_draft_step and
+    refuses sizes whose workspace exceeds its 16 MiB static scratch, all before any
+    HIP call."""
+    P = C.c_void_p
+    f = L.dsp_draft_step_noalloc
+
+    def call(R=4, gamma=4, V=32, r=8, k=0, n_steps=1, flags=0, temperature=1.0, base=FAKE):
+        return f(P(base), 1, gamma * V, V, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                 R, gamma, V, r, k, n_steps, flags, temperature, 0, 0, None)
+
+    assert call(base=0) == 1
+    assert call(k=4) == 1
+    assert call(flags=3) == 1
+    assert call(r=12) == 2
+    assert call(temperature=-1.0) == 1
+    assert call(R=2048, V=262144, r=256) == 3
+    assert b"static" in L.dsp_last_error()

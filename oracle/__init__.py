@@ -42,6 +42,8 @@ def lib():
         _lib.orc_verify.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P,
                                     P, P, P, P, P, C.c_double, C.c_uint64, C.c_uint32,
                                     P, P, P, P, P, P, P]
+        _lib.orc_tv_accept.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P, P,
+                                       P, C.c_double, P]
     return _lib
 
 
@@ -189,6 +191,25 @@ def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, see
                             float(temperature), int(seed), int(rnd), _p(accept), _p(n_acc),
                             _p(y), _p(p), _p(fa), _p(fy), _p(force_acc)), "verify")
     return dict(accept=accept, n_accept=n_acc, y=y, p=p, flag_acc=fa, flag_y=fy)
+
+
+def tv_accept(target, base, E, W2, anchor, tok, temperature):
+    """alpha [n, gamma]: the exact acceptance probability sum_v min(q_k, p_k) of
+    every draft position (target [n, gamma+1, V], base [n, gamma, V])."""
+    target, dt = _logits(target)
+    base, dt2 = _logits(base)
+    assert dt == dt2
+    n, g1, V = target.shape
+    gamma = g1 - 1
+    E = _c(E, np.uint16)
+    W2 = _c(W2, np.uint16)
+    r = E.shape[1]
+    anchor = _c(anchor, np.int32)
+    tok = _c(tok, np.int32)
+    alpha = np.zeros((n, gamma), np.float64)
+    _check(lib().orc_tv_accept(n, gamma, V, r, _p(target), _p(base), dt, _p(E), _p(W2),
+                               _p(anchor), _p(tok), float(temperature), _p(alpha)), "tv_accept")
+    return alpha
 
 
 def bf16_bits(t):

@@ -498,3 +498,42 @@ int orc_verify(int n_req, int gamma, int V, int r,
     free(tl); free(dl); free(pt); free(pd);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Exact acceptance probability of each draft position [P5-PROOF], which is   */
+/* also the total-variation target of the confidence head [P4-2.1]:          */
+/*   alpha[i,k] = sum_v min(q_k(v), p_k(v)) = 1 - (1/2) sum_v |q_k(v) - p_k(v)| */
+/* q_k the draft law at position k (Markov head with prev = anchor for k = 0, */
+/* else x_{k-1} = tok[i,k-1]), p_k = softmax(target row k / T).  Both laws in */
+/* fp64 from the fp32 logits; sampling temperatures only (T > 0).             */
+/* ------------------------------------------------------------------------- */
+
+int orc_tv_accept(int n, int gamma, int V, int r, const void* target, const void* base, int dtype,
+                  const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
+                  const int32_t* tok, double temperature, double* alpha)
+{
+    if (n < 0 || gamma <= 0 || V <= 0 || r <= 0 || !(temperature > 0.0)) return 1;
+    float* tl = (float*)malloc(sizeof(float) * (size_t)V);
+    float* dl = (float*)malloc(sizeof(float) * (size_t)V);
+    double* pt = (double*)malloc(sizeof(double) * (size_t)V);
+    double* pd = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!tl || !dl || !pt || !pd) { free(tl); free(dl); free(pt); free(pd); return 2; }
+    for (int i = 0; i < n; ++i) {
+        for (int k = 0; k < gamma; ++k) {
+            const size_t trow = ((size_t)i * (gamma + 1) + k) * (size_t)V;
+            for (int v = 0; v < V; ++v) tl[v] = logit_at(target, dtype, trow + v);
+            orc_softmax(V, tl, temperature, pt, NULL);
+            const int prev = (k == 0) ? anchor[i] : tok[(size_t)i * gamma + k - 1];
+            const size_t drow = ((size_t)i * gamma + k) * (size_t)V;
+            const void* brow = (dtype == DT_F32) ? (const void*)((const float*)base + drow)
+                                                 : (const void*)((const uint16_t*)base + drow);
+            orc_markov_logits(V, r, brow, dtype, E, W2, prev, dl, NULL);
+            orc_softmax(V, dl, temperature, pd, NULL);
+            double a = 0.0;
+            for (int v = 0; v < V; ++v) a += (pd[v] < pt[v]) ? pd[v] : pt[v];
+            alpha[(size_t)i * gamma + k] = a;
+        }
+    }
+    free(tl); free(dl); free(pt); free(pd);
+    return 0;
+}

@@ -783,3 +783,76 @@ def test_oracle_is_deterministic(orc):
         np.testing.assert_array_equal(a[k], b[k])
     c = orc.run_round(inp, 1.0, 0, 6)
     assert not np.array_equal(a["tok"], c["tok"]) or not np.array_equal(a["y"], c["y"])
+
+
+# ---------------------------------------------------------------------------
+# Exact acceptance probability (total-variation target)
+# ---------------------------------------------------------------------------
+
+def test_tv_accept_identities(orc):
+    """alpha = sum_v min(q, p) (page "为什么DSpark 可以加速推理？", section on the
+    mathematics of speculative decoding: the total acceptance probability) equals
+    1 - TV(q, p) (page "DeepSeek联合北大最新文章DSpark", section 2.1: the confidence
+    head's target is one minus the total-variation distance).  Without a Markov
+    bias the draft law is scipy's softmax of the base row, so the identity is
+    checked against laws the oracle did not compute; p = q gives 1; disjoint
+    supports (masked logits) give 0; the pages' two-token example (target 60/40)
+    gives min(qa, 0.6) + min(1 - qa, 0.4)."""
+    rng = np.random.default_rng(30)
+    n, g, V, r = 5, 3, 40, 8
+    base = rng.normal(0, 2, (n, g, V)).astype(np.float32)
+    target = rng.normal(0, 2, (n, g + 1, V)).astype(np.float32)
+    E = bf16(rng.normal(0, 0.3, (V, r)))
+    W0 = bf16(np.zeros((V, r)))
+    anchor = rng.integers(0, V, n).astype(np.int32)
+    tok = rng.integers(0, V, (n, g)).astype(np.int32)
+    for T in (1.0, 0.7):
+        a = orc.tv_accept(target, base, E, W0, anchor, tok, T)
+        q = sp_softmax(base.astype(np.float64) / T, axis=-1)
+        p = sp_softmax(target[:, :g].astype(np.float64) / T, axis=-1)
+        np.testing.assert_allclose(a, 1 - 0.5 * np.abs(q - p).sum(-1), rtol=0, atol=1e-14)
+    # p = q
+    same = np.concatenate([base, base[:, :1]], axis=1)
+    np.testing.assert_allclose(orc.tv_accept(same, base, E, W0, anchor, tok, 1.0), 1.0, atol=1e-14)
+    # disjoint supports
+    b2 = np.full((1, 1, 4), -np.inf, np.float32)
+    b2[0, 0, :2] = 0.0
+    t2 = np.full((1, 2, 4), -np.inf, np.float32)
+    t2[0, :, 2:] = 0.0
+    assert orc.tv_accept(t2, b2, bf16(np.zeros((4, 8))), bf16(np.zeros((4, 8))),
+                         np.array([-1], np.int32), np.zeros((1, 1), np.int32), 1.0)[0, 0] == 0.0
+    # the two-token example
+    tgt = np.array([float(x) for x in _golden("two_token_example.txt")["target"][0]])
+    tl = np.log(tgt).astype(np.float32)
+    p2 = sp_softmax(tl.astype(np.float64))
+    for qa in (0.95, 0.05, 0.6, 0.3):
+        ql = np.log(np.array([qa, 1 - qa])).astype(np.float32)
+        q2 = sp_softmax(ql.astype(np.float64))
+        a = orc.tv_accept(np.stack([tl, tl])[None], ql[None, None], bf16(np.zeros((2, 1))),
+                          bf16(np.zeros((2, 1))), np.array([-1], np.int32), np.zeros((1, 1), np.int32),
+                          1.0)
+        assert abs(a[0, 0] - np.minimum(q2, p2).sum()) < 1e-15
+
+
+def test_tv_accept_is_the_verification_accept_rate(orc):
+    """With the Markov bias on, alpha of a position equals the rate at which the
+    oracle's own lossless verification accepts draws at it: 4e5 draws of one
+    request's first position (distinct Philox request ids), accept rate within
+    5 sigma of alpha."""
+    rng = np.random.default_rng(31)
+    V, r, N = 6, 4, 400_000
+    row = rng.normal(0, 1.2, V).astype(np.float32)
+    trow = (row + rng.normal(0, 1.0, V)).astype(np.float32)
+    E = bf16(rng.normal(0, 0.5, (V, r)))
+    W2 = bf16(rng.normal(0, 0.5, (V, r)))
+    prev = 3
+    base = np.broadcast_to(row, (N, 1, V)).copy()
+    target = np.broadcast_to(np.stack([trow, trow]), (N, 2, V)).copy()
+    anc = np.full(N, prev, np.int32)
+    req = np.arange(N, dtype=np.int32)
+    tok, q, _, _ = orc.draft(base, E, W2, anc, req, 1.0, 8, 2)
+    res = orc.verify(target, base, E, W2, anc, tok, q, np.ones(N, np.int32), req, 1.0, 8, 2)
+    rate = float((res["accept"][:, 0] == 1).mean())
+    a = orc.tv_accept(target[:1], base[:1], E, W2, anc[:1], tok[:1], 1.0)[0, 0]
+    assert 0.05 < a < 0.95
+    assert abs(rate - a) < 5 * math.sqrt(a * (1 - a) / N), (rate, a)

@@ -136,6 +136,7 @@ size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
     if (R <= 0 || gamma <= 0 || V <= 0 || r <= 0) return 0;
     if (which == DSP_WS_DRAFT) return dsp::draft_workspace_bytes(R, V);
     if (which == DSP_WS_VERIFY) return dsp::verify_workspace_bytes(R, gamma, V);
+    if (which == DSP_WS_TV) return dsp::tv_workspace_bytes(R, gamma, V);
     return 0;
 }
 
@@ -299,3 +300,39 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
 }
 
 }  // extern "C"
+
+extern "C" dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64_t target_ps,
+                                    const void* base, int64_t base_rs, int64_t base_ps,
+                                    dsp_dtype dtype, const uint16_t* E, const uint16_t* W2,
+                                    const int32_t* anchor, const int32_t* tok, const double* stats,
+                                    double* alpha, int R, int gamma, int V, int r, float temperature,
+                                    void* ws, size_t ws_bytes, void* stream)
+{
+    if (!target || !base || !E || !W2 || !anchor || !tok || !stats || !alpha)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept: null pointer argument");
+    if (dtype != DSP_F32 && dtype != DSP_BF16)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept: unknown dtype %d", (int)dtype);
+    dsp_status st = check_markov(R, gamma, V, r);
+    if (st != DSP_OK) return st;
+    if ((int64_t)R * gamma > (int64_t)INT32_MAX / 4)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_tv_accept: R * gamma too large");
+    if (!(temperature > 0.0f) || std::isinf(temperature))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept: temperature must be finite and > 0");
+    st = check_strides("dsp_tv_accept", "target", target_rs, target_ps);
+    if (st != DSP_OK) return st;
+    st = check_strides("dsp_tv_accept", "base", base_rs, base_ps);
+    if (st != DSP_OK) return st;
+    if (!aligned16(target) || !aligned16(base) || !aligned16(E) || !aligned16(W2))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept: target, base, E and W2 must be 16-byte aligned");
+    const size_t need = dsp::tv_workspace_bytes(R, gamma, V);
+    if (!ws || ws_bytes < need)
+        return fail(DSP_ERR_WORKSPACE, "dsp_tv_accept: workspace of %zu bytes, %zu needed", ws_bytes,
+                    need);
+    if (!aligned16(ws))
+        return fail(DSP_ERR_WORKSPACE, "dsp_tv_accept: the workspace must be 16-byte aligned");
+    return hip_status(dsp::launch_tv_accept(target, dsp::RowStrides{target_rs, target_ps}, base,
+                                            dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16, E, W2,
+                                            anchor, tok, stats, alpha, R, gamma, V, r, temperature,
+                                            ws, static_cast<hipStream_t>(stream)),
+                      "dsp_tv_accept launch");
+}

@@ -68,6 +68,12 @@ hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t
 hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t S0, int mode,
                            int32_t* len, float* a, int32_t* B, int R, int gamma, hipStream_t s);
 
+size_t tv_workspace_bytes(int R, int gamma, int V);
+hipError_t launch_tv_accept(const void* target, RowStrides ts, const void* base, RowStrides bs,
+                            bool bf16, const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
+                            const int32_t* tok, const double* stats, double* alpha, int R, int gamma,
+                            int V, int r, float temperature, void* ws, hipStream_t s);
+
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
                          bool bf16, int path, bool give_up, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,

@@ -129,6 +129,7 @@ struct PassArgs {
     Part* part;              // [R, n_vt] (kResidual: [queue slot, n_vt])
     unsigned* ctl;           // error word of the call's workspace, set to 0 by the
                              // first pass of a call (nullptr: left alone)
+    int row_by_entry;        // kResidual: row_m / row_z indexed by queue slot (else by request)
 };
 
 // ---------------------------------------------------------------------------
@@ -456,10 +457,11 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
             const int e = min(n0 + c32, n_end - 1);
             const int n = a.list[e];
             const int m = a.list_m[e];
+            const int rs = a.row_by_entry ? e : n;
             const float Md = (float)a.stats[2 * ((int64_t)n * gamma + m)];
             const float invZd = (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]);
-            const float Mt = a.row_m[n];
-            const float invZt = (float)(1.0 / a.row_z[n]);
+            const float Mt = a.row_m[rs];
+            const float invZt = (float)(1.0 / a.row_z[rs]);
             // max(0, p - q) per column: fp32 weights, then the products, the
             // difference and the sums in fp64 (the rescan of a pick repeats it)
             double d2[2] = {0.0, 0.0};

@@ -567,6 +567,195 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Exact acceptance probability of every draft position:
+//   alpha[n, k] = sum_v min(q_k(v), p_k(v)) = 1 - sum_v max(0, p_k(v) - q_k(v))
+// (page "为什么DSpark 可以加速推理？", section on the mathematics of speculative
+// decoding: the total acceptance probability; page "DeepSeek联合北大最新文章DSpark",
+// section 2.1: one minus the total-variation distance is the confidence head's
+// target).  The target rows' normalisers come first (verify_rows and a per-row
+// combine); then the residual pass runs over every (request, position) entry --
+// the draft row rebuilt with the draft step's MFMA bias, max(0, p - q) per column
+// in fp64 -- and a combine sums each entry's tiles.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct TvWs {
+    VerifyWs v;          // verify_rows' outputs (rowpart, spanpart, zx) and scratch words
+    int* lens;           // [R] gamma - 1: verify_rows streams target rows 0 .. gamma-1
+    int* count;          // [1] R gamma
+    int* list;           // [R gamma] request of each entry
+    int* list_m;         // [R gamma] its position
+    int* list_prev;      // [R gamma] the token before it (-1: no bias)
+    float* row_m;        // [R gamma] target row maximum
+    double* row_z;       // [R gamma] target row normaliser
+    Part* part;          // [R gamma, n_vt] residual mass per tile
+};
+
+inline TvWs carve_tv(void* ws, int R, int gamma, int V, size_t* total)
+{
+    const size_t n_vt = (size_t)((V + kVocabTile - 1) / kVocabTile);
+    const size_t spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
+    const size_t N = (size_t)R * gamma;
+    char* p = static_cast<char*>(ws);
+    size_t off = 0;
+    TvWs w{};
+    w.v.rowpart = reinterpret_cast<Part*>(p + off);  off += align256((size_t)R * (gamma + 1) * n_vt * sizeof(Part));
+    w.v.spanpart = reinterpret_cast<Part*>(p + off); off += align256((size_t)R * (gamma + 1) * 4 * spans * sizeof(Part));
+    w.v.zx = reinterpret_cast<float*>(p + off);      off += align256(N * sizeof(float));
+    w.v.resid_cnt = reinterpret_cast<int*>(p + off); off += 256;
+    w.v.run_ctl = reinterpret_cast<unsigned*>(p + off); off += 256;
+    w.lens = reinterpret_cast<int*>(p + off);        off += align256((size_t)R * sizeof(int));
+    w.count = reinterpret_cast<int*>(p + off);       off += 256;
+    w.list = reinterpret_cast<int*>(p + off);        off += align256(N * sizeof(int));
+    w.list_m = reinterpret_cast<int*>(p + off);      off += align256(N * sizeof(int));
+    w.list_prev = reinterpret_cast<int*>(p + off);   off += align256(N * sizeof(int));
+    w.row_m = reinterpret_cast<float*>(p + off);     off += align256(N * sizeof(float));
+    w.row_z = reinterpret_cast<double*>(p + off);    off += align256(N * sizeof(double));
+    w.part = reinterpret_cast<Part*>(p + off);       off += align256(N * n_vt * sizeof(Part));
+    if (total) *total = off;
+    return w;
+}
+
+}  // namespace
+
+// one thread per (request, position) entry: the residual pass's queue and the
+// row limit that makes verify_rows stream target rows 0 .. gamma - 1
+__global__ void tv_prep_kernel(const int32_t* __restrict__ anchor, const int32_t* __restrict__ tok,
+                               int R, int gamma, int V, TvWs ws)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t N = (int64_t)R * gamma;
+    if (e < R) ws.lens[e] = gamma - 1;
+    if (e == 0) *ws.count = (int)N;
+    if (e >= N) return;
+    const int n = (int)(e / gamma), k = (int)(e % gamma);
+    const int p = (k == 0) ? anchor[n] : tok[e - 1];
+    ws.list[e] = n;
+    ws.list_m[e] = k;
+    ws.list_prev[e] = (p >= 0 && p < V) ? p : -1;
+}
+
+// one wave per entry: the target row's (M, Z) from verify_rows' 8-tile partials
+template <int PER>
+__global__ __launch_bounds__(256) void tv_rowstats_kernel(int R, int gamma, int n_vt, float inv_temp,
+                                                          TvWs ws)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t e = (int64_t)blockIdx.x * 4 + wave;
+    if (e >= (int64_t)R * gamma) return;
+    const int n = (int)(e / gamma), k = (int)(e % gamma);
+    const int np = 4 * ((n_vt + kSpanTiles - 1) / kSpanTiles);
+    const Part* pp = ws.v.spanpart + ((int64_t)n * (gamma + 1) + k) * np;
+    Part pt[PER];
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int t = lane * PER + i;
+        pt[i] = (t < np) ? pp[t] : Part{-INFINITY, 0, 0.0};
+        M = fmaxf(M, pt[i].m);
+    }
+    M = wave_max_f(M);
+    double Z = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) Z += pt[i].s * rescale64(pt[i].m, M, inv_temp);
+    Z = wave_sum_d(Z);
+    if (lane == 0) {
+        ws.row_m[e] = M;
+        ws.row_z[e] = Z;
+    }
+}
+
+// one wave per entry: alpha = 1 - (sum of the tiles' residual mass)
+template <int PER>
+__global__ __launch_bounds__(256) void tv_combine_kernel(int R, int gamma, int n_vt, TvWs ws,
+                                                         double* __restrict__ alpha)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t e = (int64_t)blockIdx.x * 4 + wave;
+    if (e >= (int64_t)R * gamma) return;
+    const Part* pp = ws.part + e * n_vt;
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int t = lane * PER + i;
+        if (t < n_vt) s += pp[t].s;
+    }
+    s = wave_sum_d(s);
+    if (lane == 0) alpha[e] = fmin(fmax(1.0 - s, 0.0), 1.0);
+}
+
+size_t tv_workspace_bytes(int R, int gamma, int V)
+{
+    size_t total = 0;
+    carve_tv(nullptr, R, gamma, V, &total);
+    return total;
+}
+
+template <typename LT>
+static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
+                              const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
+                              const int32_t* tok, const double* stats, double* alpha, int R,
+                              int gamma, int V, int r, float temperature, void* ws_raw, hipStream_t s)
+{
+    const TvWs ws = carve_tv(ws_raw, R, gamma, V, nullptr);
+    const int n_vt = (V + kVocabTile - 1) / kVocabTile;
+    const float it = 1.0f / temperature;
+    const int64_t N = (int64_t)R * gamma;
+    hipLaunchKernelGGL(tv_prep_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, anchor, tok,
+                       R, gamma, V, ws);
+    const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
+    const int64_t items = (int64_t)R * (gamma + 1) * spans;
+    hipLaunchKernelGGL((verify_rows_kernel<LT, false>), dim3((unsigned)items), dim3(256), 0, s, target,
+                       ts, tok, ws.lens, R, gamma, V, it, n_vt, ws.v, 0u);
+    const int np = 4 * spans;
+    const int per = (np + kWave - 1) / kWave;
+    const dim3 gw((unsigned)((N + 3) / 4));
+#define DSP_TVROW(P) hipLaunchKernelGGL((tv_rowstats_kernel<P>), gw, dim3(256), 0, s, R, gamma, n_vt, it, ws)
+    if (per <= 1) DSP_TVROW(1);
+    else if (per <= 2) DSP_TVROW(2);
+    else if (per <= 4) DSP_TVROW(4);
+    else if (per <= 8) DSP_TVROW(8);
+    else if (per <= 16) DSP_TVROW(16);
+    else DSP_TVROW(32);
+#undef DSP_TVROW
+    PassArgs a{};
+    a.base = base; a.target = target; a.bs = bs; a.ts = ts;
+    a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.list = ws.list; a.list_m = ws.list_m; a.list_prev = ws.list_prev; a.count = ws.count;
+    a.stats = stats; a.row_m = ws.row_m; a.row_z = ws.row_z; a.row_by_entry = 1;
+    a.R = R; a.gamma = gamma; a.V = V; a.r = r; a.k = 0; a.inv_temp = it;
+    a.n_vt = n_vt;
+    a.req_per_wg = pass_req_per_wg((int)N, n_vt);
+    a.part = ws.part;
+    const dim3 g3(n_vt, (unsigned)((N + a.req_per_wg - 1) / a.req_per_wg));
+    if (rows_vec(bs, V, 8) && rows_vec(ts, V, 8))
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, true>), g3, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, false>), g3, dim3(256), 0, s, a);
+    const int pc = (n_vt + kWave - 1) / kWave;
+#define DSP_TVC(P) hipLaunchKernelGGL((tv_combine_kernel<P>), gw, dim3(256), 0, s, R, gamma, n_vt, ws, alpha)
+    if (pc <= 1) DSP_TVC(1);
+    else if (pc <= 2) DSP_TVC(2);
+    else if (pc <= 4) DSP_TVC(4);
+    else if (pc <= 8) DSP_TVC(8);
+    else DSP_TVC(16);
+#undef DSP_TVC
+    return hipGetLastError();
+}
+
+hipError_t launch_tv_accept(const void* target, RowStrides ts, const void* base, RowStrides bs,
+                            bool bf16, const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
+                            const int32_t* tok, const double* stats, double* alpha, int R, int gamma,
+                            int V, int r, float temperature, void* ws, hipStream_t s)
+{
+    if (bf16)
+        return launch_tv_t(static_cast<const uint16_t*>(target), ts, static_cast<const uint16_t*>(base),
+                           bs, E, W2, anchor, tok, stats, alpha, R, gamma, V, r, temperature, ws, s);
+    return launch_tv_t(static_cast<const float*>(target), ts, static_cast<const float*>(base), bs, E,
+                       W2, anchor, tok, stats, alpha, R, gamma, V, r, temperature, ws, s);
+}
+
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
                          bool bf16, int path, bool give_up, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,

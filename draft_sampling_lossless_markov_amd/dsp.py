@@ -22,13 +22,13 @@ LIB_PATH = os.path.join(_PKG, "libdsp.so")
 _STATUS_NAMES = ("DSP_OK", "DSP_ERR_INVALID_ARG", "DSP_ERR_UNSUPPORTED", "DSP_ERR_WORKSPACE",
                  "DSP_ERR_HIP", "DSP_ERR_TIMEOUT")
 DSP_F32, DSP_BF16 = 0, 1
-DSP_WS_DRAFT, DSP_WS_VERIFY = 0, 1
+DSP_WS_DRAFT, DSP_WS_VERIFY, DSP_WS_TV = 0, 1, 2
 DSP_PATH_AUTO, DSP_PATH_STREAMING, DSP_PATH_PERSISTENT = 0, 1, 2
 DSP_FLAG_TEST_GIVE_UP = 0x100
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
             "dsp_workspace_status", "dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence",
-            "dsp_schedule", "dsp_verify")
+            "dsp_schedule", "dsp_verify", "dsp_tv_accept")
 
 _lib = None
 
@@ -72,8 +72,9 @@ def lib():
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
     L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
                              I, I, U32, F, U64, U32, P, SZ, P]
+    L.dsp_tv_accept.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, I, I, I, I, F, P, SZ, P]
     for f in ("dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence", "dsp_schedule",
-              "dsp_verify"):
+              "dsp_verify", "dsp_tv_accept"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -172,3 +173,17 @@ def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_acc
                             _ptr(accept), _ptr(n_accept), _ptr(y), _ptr(p), R, g1 - 1, V, r,
                             int(flags), float(temperature), int(seed), int(round_), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsp_tv_accept(target, base, E, W2, anchor, tok, stats, alpha, temperature, ws, stream=None):
+    """alpha [R, gamma] (f64): sum_v min(q_k, p_k) of every draft position."""
+    R, g1, V = target.shape
+    r = E.shape[1]
+    trs, tps = _rows(target, "target")
+    brs, bps = _rows(base, "base")
+    if base.dtype != target.dtype:
+        raise TypeError("base and target logits must share a dtype")
+    _check(lib().dsp_tv_accept(_ptr(target), trs, tps, _ptr(base), brs, bps, _dtype(target),
+                               _ptr(E), _ptr(W2), _ptr(anchor), _ptr(tok), _ptr(stats), _ptr(alpha),
+                               R, g1 - 1, V, r, float(temperature), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))

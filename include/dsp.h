@@ -80,7 +80,7 @@ typedef enum {
 
 typedef enum { DSP_F32 = 0, DSP_BF16 = 1 } dsp_dtype;
 
-typedef enum { DSP_WS_DRAFT = 0, DSP_WS_VERIFY = 1 } dsp_ws_kind;
+typedef enum { DSP_WS_DRAFT = 0, DSP_WS_VERIFY = 1, DSP_WS_TV = 2 } dsp_ws_kind;
 
 /* Static text for a status code. */
 const char* dsp_status_string(dsp_status s);
@@ -91,8 +91,8 @@ const char* dsp_last_error(void);
 /* Library ABI version (major * 100 + minor). */
 int dsp_version(void);
 
-/* Bytes of workspace dsp_draft_step (DSP_WS_DRAFT) or dsp_verify (DSP_WS_VERIFY)
- * needs for these sizes; 0 for invalid sizes. */
+/* Bytes of workspace dsp_draft_step (DSP_WS_DRAFT), dsp_verify (DSP_WS_VERIFY) or
+ * dsp_tv_accept (DSP_WS_TV) needs for these sizes; 0 for invalid sizes. */
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
 
 /*
@@ -289,6 +289,32 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
                       unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
                       size_t ws_bytes, void* stream);
+
+/*
+ * dsp_tv_accept -- the exact acceptance probability of every draft position.
+ *
+ * Page "为什么DSpark 可以加速推理？", section on the mathematics of speculative
+ * decoding: a draft token x ~ q is accepted with probability min(1, p(x)/q(x)),
+ * so the total acceptance probability of a position is sum_v min(q(v), p(v));
+ * page "DeepSeek联合北大最新文章DSpark", section 2.1: the confidence head is trained
+ * towards one minus the total-variation distance between the draft and target
+ * laws, the same quantity.  For each request n and position k < gamma:
+ *   q_k  = the draft law of dsp_draft_step at k (prev = anchor for k = 0, else
+ *          tok[n, k-1]; base row k plus the Markov bias, / temperature)
+ *   p_k  = softmax(target[n, k, :] / temperature)
+ *   alpha[n, k] = sum_v min(q_k(v), p_k(v)) = 1 - sum_v max(0, p_k(v) - q_k(v))
+ * computed as the latter (fp32 weights, fp64 differences and sums), clamped to
+ * [0, 1].  The arguments are those of dsp_verify: stats [R, gamma, 2] (f64) as
+ * written by dsp_draft_step give q_k's (M, Z); tok [R, gamma] its tokens; alpha
+ * [R, gamma] f64 (device memory).  temperature > 0 (DSP_ERR_INVALID_ARG
+ * otherwise).  ws >= dsp_workspace_size(DSP_WS_TV, R, gamma, V, r) bytes.
+ * Streams each target row twice (its normaliser first) and each base row once.
+ */
+dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                         int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                         const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
+                         const double* stats, double* alpha, int R, int gamma, int V, int r,
+                         float temperature, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -186,3 +186,24 @@ def test_noalloc_draft_validation(L):
     assert call(temperature=-1.0) == 1
     assert call(R=2048, V=262144, r=256) == 3
     assert b"static" in L.dsp_last_error()
+
+
+def test_tv_accept_validation(L):
+    P = C.c_void_p
+    f = L.dsp_tv_accept
+    f.argtypes = [P, C.c_int64, C.c_int64, P, C.c_int64, C.c_int64, C.c_int, P, P, P, P, P, P,
+                  C.c_int, C.c_int, C.c_int, C.c_int, C.c_float, P, C.c_size_t, P]
+    two = [P(FAKE), 5 * 32, 32, P(FAKE), 4 * 32, 32, 1]
+
+    def call(R=4, gamma=4, V=32, r=8, temperature=1.0, ws_bytes=1 << 20, ws=FAKE, target=FAKE):
+        args = list(two)
+        args[0] = P(target)
+        return f(*args, *[P(FAKE)] * 6, R, gamma, V, r, temperature, P(ws), ws_bytes, None)
+
+    assert call(target=0) == 1
+    assert call(temperature=0.0) == 1 and b"temperature" in L.dsp_last_error()
+    assert call(r=12) == 2
+    assert call(ws_bytes=16) == 3
+    assert call(ws=FAKE + 8) == 3
+    from draft_sampling_lossless_markov_amd import dsp
+    assert dsp.dsp_workspace_size(dsp.DSP_WS_TV, 4, 4, 32, 8) > 0

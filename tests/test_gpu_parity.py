@@ -659,6 +659,85 @@ def test_full_vocab_sampling_mismatch_rate():
     assert mismatched <= 1e-4 * decisions
 
 
+TV_CASES = [
+    # (R, gamma, V, r, dtype, temperature, layout)
+    (4, 4, 32, 8, torch.float32, 1.0, "request"),
+    (70, 5, 1000, 24, torch.bfloat16, 0.7, "position"),
+    (33, 3, 1003, 8, torch.float32, 1.3, "padded"),
+    (130, 6, 4100, 256, torch.bfloat16, 1.0, "request"),
+    (9, 4, 40000, 256, torch.bfloat16, 0.9, "position"),
+]
+
+
+def _tv_check(g, o):
+    err = np.abs(g - o)
+    bad = err > 1e-5 * np.abs(o) + 1e-7
+    assert not bad.any(), (np.argwhere(bad)[:5].tolist(), g[bad][:5], o[bad][:5])
+    assert np.all((g >= 0) & (g <= 1))
+    return float(err.max())
+
+
+@pytest.mark.parametrize("case", TV_CASES, ids=lambda c: f"R{c[0]}g{c[1]}V{c[2]}r{c[3]}"
+                         f"{'bf16' if c[4] == torch.bfloat16 else 'f32'}T{c[5]}{c[6]}")
+def test_tv_accept_vs_oracle(case):
+    """dsp_tv_accept (alpha = sum_v min(q_k, p_k) of every draft position) against the
+    oracle's orc_tv_accept on the GPU's own draft tokens: within 1e-5 relative."""
+    R, gamma, V, r, dt, temp, layout = case
+    wl = custom(R, gamma, V, r, 8, dt)
+    for rnd in range(2):
+        _say(f"tv accept {case} round {rnd}")
+        inp_cpu = make_inputs(wl, rnd, layout=layout)
+        inp = to_dev(inp_cpu)
+        rd = Round(R, gamma, V, r)
+        rd.draft(inp, temp, SEED, rnd)
+        alpha = torch.zeros((R, gamma), dtype=torch.float64, device="cuda")
+        ws = torch.zeros(dsp.dsp_workspace_size(dsp.DSP_WS_TV, R, gamma, V, r), dtype=torch.uint8,
+                         device="cuda")
+        dsp.dsp_tv_accept(inp["target"], inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok,
+                          rd.stats, alpha, temp, ws)
+        g = np_(alpha)
+        o = orc.tv_accept(orc.host_logits(inp_cpu["target"]), orc.host_logits(inp_cpu["base"]),
+                          orc.bf16_bits(inp_cpu["E"]), orc.bf16_bits(inp_cpu["W2"]),
+                          np_(inp_cpu["anchor"]), np_(rd.tok), temp)
+        _say(f"  max |alpha - oracle| = {_tv_check(g, o):.3g}, mean alpha {g.mean():.4f}")
+
+
+@pytest.mark.parametrize("wid", [1, 4])
+def test_tv_accept_full_size(wid):
+    """The workloads' full shapes (Qwen3-4B-shaped and the large one): every
+    entry computed on the GPU, the oracle on the first 8 requests' positions."""
+    wl = WORKLOADS[wid]
+    inp = make_inputs(wl, 0, device="cuda", layout=BENCH_LAYOUT)
+    R, gamma, V, r = inp["R"], inp["gamma"], inp["V"], inp["r"]
+    rd = Round(R, gamma, V, r)
+    rd.draft(inp, 1.0, SEED, 0)
+    alpha = torch.zeros((R, gamma), dtype=torch.float64, device="cuda")
+    ws = torch.zeros(dsp.dsp_workspace_size(dsp.DSP_WS_TV, R, gamma, V, r), dtype=torch.uint8,
+                     device="cuda")
+    dsp.dsp_tv_accept(inp["target"], inp["base"], inp["E"], inp["W2"], inp["anchor"], rd.tok,
+                      rd.stats, alpha, 1.0, ws)
+    g = np_(alpha)
+    S = np.arange(8)
+    Sl = torch.as_tensor(S).cuda()
+    E_h, W2_h = orc.bf16_bits(inp["E"]), orc.bf16_bits(inp["W2"])
+    tgt_S = orc.host_logits(inp["target"][Sl])
+    base_S = orc.host_logits(inp["base"][Sl])
+    anc_S, tok_S = np_(inp["anchor"])[S], np_(rd.tok)[S]
+    import concurrent.futures as cf
+
+    def one(i):
+        return orc.tv_accept(tgt_S[i:i + 1], base_S[i:i + 1], E_h, W2_h, anc_S[i:i + 1],
+                             tok_S[i:i + 1], 1.0)[0]
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        o = np.stack(list(ex.map(one, range(len(S)))))
+    _say(f"  {wl.name}: max |alpha - oracle| = {_tv_check(g[S], o):.3g}, "
+         f"mean alpha {g.mean():.4f} over {R * gamma} positions")
+    assert np.all((g >= 0) & (g <= 1))
+    del inp, rd, ws
+    torch.cuda.empty_cache()
+
+
 def test_zz_sampling_mismatch_rate_over_the_module():
     """Every sampled decision compared in this module (drafts, accept tests,
     corrections and bonus draws): the differing ones, each inside the oracle's

@@ -42,6 +42,8 @@ def lib():
         _lib.orc_verify.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P,
                                     P, P, P, P, P, C.c_double, C.c_uint64, C.c_uint32,
                                     P, P, P, P, P, P, P]
+        _lib.orc_schedule_async.argtypes = [C.c_int, C.c_int, P, P, P, C.c_int, C.c_double, P, P,
+                                            P, P]
         _lib.orc_tv_accept.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P, P,
                                        P, C.c_double, P]
     return _lib
@@ -160,6 +162,23 @@ def schedule(c32, sps, B_max, tau0, mode):
     _check(lib().orc_schedule(R, gamma, _p(c32), _p(sps), int(B_max), float(tau0), int(mode),
                               _p(length), _p(a), _p(B), _p(ev)), "schedule")
     return length, a, int(B[0]), int(ev[0])
+
+
+def schedule_async(c32, c_hist32, sps, B_max, tau0):
+    """Capacity K from the earlier round's confidences (global maximum of Theta, no
+    early stop), the first K of the current candidates admitted.  Returns len [R],
+    a [R, gamma] (current survival), B, K."""
+    c32 = _c(c32, np.float32)
+    ch = _c(c_hist32, np.float32)
+    R, gamma = c32.shape
+    sps = _c(sps, np.float32)
+    length = np.zeros(R, np.int32)
+    a = np.zeros((R, gamma), np.float32)
+    B = np.zeros(1, np.int32)
+    K = np.zeros(1, np.int32)
+    _check(lib().orc_schedule_async(R, gamma, _p(c32), _p(ch), _p(sps), int(B_max), float(tau0),
+                                    _p(length), _p(a), _p(B), _p(K)), "schedule_async")
+    return length, a, int(B[0]), int(K[0])
 
 
 def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, seed, rnd,

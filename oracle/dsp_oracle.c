@@ -537,3 +537,66 @@ int orc_tv_accept(int n, int gamma, int V, int r, const void* target, const void
     free(tl); free(dl); free(pt); free(pd);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Asynchronous scheduler with a capacity barrier ("DeepSeek联合北大最新文章  */
+/* DSpark", 挑战2 异步调度与 ZOS 兼容; "DSpark.让每一轮计算，多走几步", the     */
+/* causality paragraph of 两个严谨补丁).                                     */
+/*   capacity: from the confidences of an earlier round (c_hist), the same   */
+/*     survival products, order and Q48 sums as orc_schedule, then the       */
+/*     global maximum of Theta_n = tau_n SPS(R + n) over every n with        */
+/*     R + n <= B_max and n <= R gamma -- no early stop; the smallest such n */
+/*     on ties:  K = argmax_n Theta_n.                                       */
+/*   admission: the current survival products (from c) in the same order;    */
+/*     the first K candidates are admitted; l_r = admitted candidates of r;  */
+/*     B = R + K.                                                            */
+/* ------------------------------------------------------------------------- */
+
+static void survival_and_order(int R, int gamma, const float* c, float* a, cand_t* cs)
+{
+    for (int r = 0; r < R; ++r) {
+        float prod = 1.0f;
+        for (int j = 0; j < gamma; ++j) {
+            prod = prod * c[(size_t)r * gamma + j];
+            a[(size_t)r * gamma + j] = prod;
+        }
+    }
+    for (int r = 0; r < R; ++r)
+        for (int j = 0; j < gamma; ++j) {
+            cand_t* t = &cs[(size_t)r * gamma + j];
+            t->a = a[(size_t)r * gamma + j]; t->r = r; t->j = j;
+        }
+    qsort(cs, (size_t)R * gamma, sizeof(cand_t), cand_cmp);
+}
+
+int orc_schedule_async(int R, int gamma, const float* c, const float* c_hist, const float* sps,
+                       int B_max, double tau0, int32_t* len, float* a, int32_t* B_out,
+                       int32_t* K_out)
+{
+    if (R <= 0 || gamma <= 0 || B_max < R || !(tau0 >= 0.0) || !(tau0 < 16384.0)) return 1;
+    if ((int64_t)R * gamma > 16384) return 1;
+    const size_t N = (size_t)R * gamma;
+    cand_t* cs = (cand_t*)malloc(sizeof(cand_t) * N);
+    float* ah = (float*)malloc(sizeof(float) * N);
+    if (!cs || !ah) { free(cs); free(ah); return 2; }
+    /* capacity from the earlier round's confidences */
+    survival_and_order(R, gamma, c_hist, ah, cs);
+    const double scale = ldexp(1.0, 48);
+    uint64_t S = (uint64_t)floor(tau0 * scale);
+    double best = (double)S / scale * (double)sps[R - 1];
+    size_t K = 0;
+    const size_t n_max = (N < (size_t)(B_max - R)) ? N : (size_t)(B_max - R);
+    for (size_t n = 1; n <= n_max; ++n) {
+        S += (uint64_t)floor((double)cs[n - 1].a * scale);
+        const double theta = ((double)S / scale) * (double)sps[R + n - 1];
+        if (theta > best) { best = theta; K = n; }
+    }
+    /* admission by the current confidences */
+    survival_and_order(R, gamma, c, a, cs);
+    for (int r = 0; r < R; ++r) len[r] = 0;
+    for (size_t n = 0; n < K; ++n) len[cs[n].r] += 1;
+    *B_out = R + (int32_t)K;
+    *K_out = (int32_t)K;
+    free(cs); free(ah);
+    return 0;
+}

@@ -856,3 +856,109 @@ def test_tv_accept_is_the_verification_accept_rate(orc):
     a = orc.tv_accept(target[:1], base[:1], E, W2, anc[:1], tok[:1], 1.0)[0, 0]
     assert 0.05 < a < 0.95
     assert abs(rate - a) < 5 * math.sqrt(a * (1 - a) / N), (rate, a)
+
+
+# ---------------------------------------------------------------------------
+# Asynchronous scheduler with a capacity barrier
+# ---------------------------------------------------------------------------
+
+def _survival_order(c):
+    """Survival products (fp32, left to right) and the order a desc, r asc, j asc."""
+    a = np.cumprod(c.astype(np.float32), axis=1, dtype=np.float32)
+    R, g = a.shape
+    rr, jj = np.meshgrid(np.arange(R), np.arange(g), indexing="ij")
+    order = np.lexsort((jj.ravel(), rr.ravel(), -a.ravel().astype(np.float64)))
+    return a, order, rr.ravel(), jj.ravel()
+
+
+def test_async_schedule_capacity_is_the_global_optimum(orc):
+    """Page "DeepSeek联合北大最新文章DSpark", 挑战2: the capacity comes from an earlier
+    round's confidences by a global search without early stop.  Against brute force
+    over every length vector of that round (tiny R, gamma, jagged and smooth SPS):
+    Theta at the capacity is the exhaustive optimum and the capacity is the smallest
+    such n; the admitted set is the first K candidates of the current round's order
+    (numpy's cumprod and lexsort)."""
+    rng = np.random.default_rng(40)
+    for trial in range(300):
+        R = int(rng.integers(1, 4))
+        gamma = int(rng.integers(1, 5))
+        ch = rng.uniform(0.05, 1.0, (R, gamma)).astype(np.float32)
+        c = rng.uniform(0.05, 1.0, (R, gamma)).astype(np.float32)
+        B_max = int(rng.integers(R, R * (gamma + 1) + 1))
+        if trial % 2 == 0:
+            sps = rng.uniform(0.2, 1.0, B_max).astype(np.float32)
+        else:
+            Bs = np.arange(1, B_max + 1, dtype=np.float64)
+            sps = (1.0 / (1.0 + rng.uniform(0.01, 3) * Bs + rng.uniform(0, .5) * Bs ** 2)).astype(np.float32)
+        tau0 = float(rng.choice([0.0, 0.5]))
+        length, a, B, K = orc.schedule_async(c, ch, sps, B_max, tau0)
+        ah, _, _, _ = _survival_order(ch)
+        spsd = sps.astype(np.float64)
+        thetas = {}
+        for lv in itertools.product(range(gamma + 1), repeat=R):
+            Bv = R + sum(lv)
+            if Bv > B_max:
+                continue
+            tau = tau0 + sum(float(ah[r_, :lv[r_]].astype(np.float64).sum()) for r_ in range(R))
+            thetas[Bv - R] = max(thetas.get(Bv - R, -1.0), tau * spsd[Bv - 1])
+        best = max(thetas.values())
+        assert abs(thetas[K] - best) <= 1e-12 * max(best, 1e-300), (trial, K, thetas)
+        assert all(thetas[n] < best * (1 - 1e-12) for n in thetas if n < K), (trial, K, thetas)
+        assert B == R + K
+        an, order, rr, jj = _survival_order(c)
+        np.testing.assert_array_equal(a, an)
+        np.testing.assert_array_equal(length, np.bincount(rr[order[:K]], minlength=R))
+
+
+def test_async_schedule_matches_early_stop_on_unimodal_curves_and_beats_it_on_sawtooth(orc):
+    """With the earlier round's confidences equal to the current ones and a smooth
+    cost curve, the global search and the synchronous early stop agree.  On a
+    sawtooth SPS table (the pages: real hardware curves are jagged and the naive
+    early stop gets stuck in a local optimum) the capacity goes past the early stop
+    and reaches a strictly higher Theta."""
+    rng = np.random.default_rng(41)
+    R, gamma = 64, 7
+    c = rng.uniform(0.6, 0.98, (R, gamma)).astype(np.float32)
+    B_max = R * (gamma + 1)
+    Bs = np.arange(1, B_max + 1, dtype=np.float64)
+    smooth = (1.0 / (12 + 0.1 * Bs + 0.0008 * Bs * Bs)).astype(np.float32)
+    l_s, a_s, B_s, _ = orc.schedule(c, smooth, B_max, 0.0, 1)
+    l_a, a_a, B_a, K = orc.schedule_async(c, c, smooth, B_max, 0.0)
+    np.testing.assert_array_equal(l_s, l_a)
+    assert B_s == B_a == R + K
+    # sawtooth: throughput drops right after every multiple of 64 (a kernel-tile edge)
+    saw = (1.0 / (12 + 0.02 * Bs) * np.where((Bs % 64) < 8, 0.9, 1.0)).astype(np.float32)
+    l_e, _, B_e, _ = orc.schedule(c, saw, B_max, 0.0, 1)
+    l_g, _, B_g, K = orc.schedule_async(c, c, saw, B_max, 0.0)
+    a, order, _, _ = _survival_order(c)
+    cum = np.concatenate([[0.0], np.cumsum(a.ravel()[order].astype(np.float64))])
+    theta = lambda B: cum[B - R] * float(saw[B - 1])
+    assert B_g > B_e and theta(B_g) > theta(B_e) * 1.01, (B_e, B_g)
+
+
+def test_async_schedule_causality_and_why_the_barrier_matters(orc):
+    """With the capacity fixed from the earlier round, whether position j of
+    request r is verified does not depend on x_{r,j} or later tokens (c_{r,j+1..}).
+    A global search over the current round's own confidences (the earlier round
+    replaced by the current one) does depend on them in some instances -- the
+    anticipation the capacity barrier removes (page "DSpark.让每一轮计算，多走几步",
+    causality paragraph)."""
+    rng = np.random.default_rng(42)
+    violations = 0
+    for _ in range(2000):
+        R, gamma = int(rng.integers(1, 6)), int(rng.integers(2, 7))
+        c = rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
+        ch = rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
+        B_max = R * (gamma + 1)
+        sps = rng.uniform(0.2, 1.0, B_max).astype(np.float32)
+        r = int(rng.integers(0, R))
+        j = int(rng.integers(0, gamma - 1))
+        c2 = c.copy()
+        c2[r, j + 1:] = rng.uniform(0.0, 1.0, gamma - j - 1).astype(np.float32)
+        l0, _, _, _ = orc.schedule_async(c, ch, sps, B_max, 0.0)
+        l1, _, _, _ = orc.schedule_async(c2, ch, sps, B_max, 0.0)
+        assert min(l0[r], j + 1) == min(l1[r], j + 1)
+        g0, _, _, _ = orc.schedule_async(c, c, sps, B_max, 0.0)
+        g1, _, _, _ = orc.schedule_async(c2, c2, sps, B_max, 0.0)
+        violations += min(g0[r], j + 1) != min(g1[r], j + 1)
+    assert violations > 0

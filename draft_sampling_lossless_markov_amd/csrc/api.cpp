@@ -336,3 +336,24 @@ extern "C" dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64
                                             ws, static_cast<hipStream_t>(stream)),
                       "dsp_tv_accept launch");
 }
+
+extern "C" dsp_status dsp_schedule_async(const float* c, const float* c_hist, const float* sps,
+                                         int B_max, double tau0, int32_t* len, float* a, int32_t* B,
+                                         int32_t* K, int R, int gamma, void* stream)
+{
+    if (!c || !c_hist || !sps || !len || !a || !B || !K)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule_async: null pointer argument");
+    if (R <= 0 || gamma <= 0)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule_async: bad sizes R=%d gamma=%d", R, gamma);
+    if (B_max < R)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule_async: B_max = %d < R = %d", B_max, R);
+    if (!(tau0 >= 0.0) || !(tau0 < 16384.0))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_schedule_async: tau0 must be in [0, 2^14)");
+    if ((int64_t)R * gamma > dsp::kSchedMaxCand)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_schedule_async: R * gamma = %lld exceeds %d",
+                    (long long)R * gamma, dsp::kSchedMaxCand);
+    const uint64_t S0 = (uint64_t)std::floor(tau0 * 281474976710656.0);
+    return hip_status(dsp::launch_schedule_async(c, c_hist, sps, B_max, S0, len, a, B, K, R, gamma,
+                                                 static_cast<hipStream_t>(stream)),
+                      "dsp_schedule_async launch");
+}

@@ -74,6 +74,10 @@ hipError_t launch_tv_accept(const void* target, RowStrides ts, const void* base,
                             const int32_t* tok, const double* stats, double* alpha, int R, int gamma,
                             int V, int r, float temperature, void* ws, hipStream_t s);
 
+hipError_t launch_schedule_async(const float* c, const float* c_hist, const float* sps, int B_max,
+                                 uint64_t S0, int32_t* len, float* a, int32_t* B, int32_t* K, int R,
+                                 int gamma, hipStream_t s);
+
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
                          bool bf16, int path, bool give_up, const uint16_t* E,
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,

@@ -28,7 +28,7 @@ DSP_FLAG_TEST_GIVE_UP = 0x100
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
             "dsp_workspace_status", "dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence",
-            "dsp_schedule", "dsp_verify", "dsp_tv_accept")
+            "dsp_schedule", "dsp_schedule_async", "dsp_verify", "dsp_tv_accept")
 
 _lib = None
 
@@ -72,9 +72,10 @@ def lib():
     L.dsp_schedule.argtypes = [P, P, I, D, I, P, P, P, I, I, P]
     L.dsp_verify.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, I, I,
                              I, I, U32, F, U64, U32, P, SZ, P]
+    L.dsp_schedule_async.argtypes = [P, P, P, I, D, P, P, P, P, I, I, P]
     L.dsp_tv_accept.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, I, I, I, I, F, P, SZ, P]
     for f in ("dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence", "dsp_schedule",
-              "dsp_verify", "dsp_tv_accept"):
+              "dsp_schedule_async", "dsp_verify", "dsp_tv_accept"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -157,6 +158,13 @@ def dsp_schedule(c, sps, B_max, tau0, mode, length, a, B, stream=None):
     R, gamma = c.shape
     _check(lib().dsp_schedule(_ptr(c), _ptr(sps), int(B_max), float(tau0), int(mode),
                               _ptr(length), _ptr(a), _ptr(B), R, gamma, _stream(stream)))
+
+
+def dsp_schedule_async(c, c_hist, sps, B_max, tau0, length, a, B, K, stream=None):
+    R, gamma = c.shape
+    _check(lib().dsp_schedule_async(_ptr(c), _ptr(c_hist), _ptr(sps), int(B_max), float(tau0),
+                                    _ptr(length), _ptr(a), _ptr(B), _ptr(K), R, gamma,
+                                    _stream(stream)))
 
 
 def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_accept, y, p,

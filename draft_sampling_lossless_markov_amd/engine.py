@@ -23,6 +23,7 @@ class Round:
         self.len = torch.zeros((R,), dtype=i32, device=dev)
         self.a = torch.zeros((R, gamma), dtype=f32, device=dev)
         self.B = torch.zeros((1,), dtype=i32, device=dev)
+        self.K = torch.zeros((1,), dtype=i32, device=dev)
         self.accept = torch.zeros((R, gamma), dtype=torch.int8, device=dev)
         self.n_accept = torch.zeros((R,), dtype=i32, device=dev)
         self.y = torch.zeros((R,), dtype=i32, device=dev)
@@ -48,6 +49,13 @@ class Round:
         tau0 = inp["tau0"] if tau0 is None else tau0
         dsp.dsp_schedule(self.c, inp["sps"], inp["B_max"], tau0, mode, self.len, self.a, self.B,
                          stream)
+
+    def schedule_async(self, inp, c_hist, tau0=None, stream=None):
+        """The capacity-barrier scheduler: capacity from c_hist (an earlier round's
+        confidences of the same requests), admission by this round's self.c."""
+        tau0 = inp["tau0"] if tau0 is None else tau0
+        dsp.dsp_schedule_async(self.c, c_hist, inp["sps"], inp["B_max"], tau0, self.len, self.a,
+                               self.B, self.K, stream)
 
     def verify(self, inp, temperature, seed, rnd, stream=None, flags=dsp.DSP_PATH_AUTO):
         dsp.dsp_verify(inp["target"], inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok,

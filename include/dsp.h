@@ -244,6 +244,33 @@ dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0
                         int32_t* len, float* a, int32_t* B, int R, int gamma, void* stream);
 
 /*
+ * dsp_schedule_async -- the scheduler with a capacity barrier, for engines that
+ * must fix a step's batch size before the previous step ends.
+ *
+ * Page "DeepSeek联合北大最新文章DSpark", 挑战2 (asynchronous scheduling and
+ * zero-overhead scheduling): real SPS curves are jagged, so the early stop of
+ * dsp_schedule can stop at a local optimum; the verification capacity is instead
+ * taken from the confidences of two steps back, the candidates are still ranked
+ * by the newest ones, and the capacity barrier lets the search over the old
+ * confidences drop the early stop without breaking losslessness (page "DSpark.
+ * 让每一轮计算，多走几步", causality paragraph of 两个严谨补丁).
+ *
+ *   capacity: survival products, order and Q48 sums of dsp_schedule over c_hist;
+ *             K = the smallest n in [0, min(R gamma, B_max - R)] with the maximum
+ *             Theta_n = (tau0 + sum of the n best) * SPS(R + n) -- no early stop
+ *   admission: a = survival products of c (written out), the same order; the
+ *             first K candidates admitted; len[r] = admitted candidates of r;
+ *             *B = R + K; *K = K
+ * c, c_hist [R, gamma] f32 in [0, 1] (c_hist: the same requests' confidences of
+ * an earlier round, e.g. two steps back); sps, B_max, tau0 as for dsp_schedule;
+ * len [R], a [R, gamma], B [1], K [1] (device memory).  One workgroup;
+ * R * gamma <= 16384.
+ */
+dsp_status dsp_schedule_async(const float* c, const float* c_hist, const float* sps, int B_max,
+                              double tau0, int32_t* len, float* a, int32_t* B, int32_t* K, int R,
+                              int gamma, void* stream);
+
+/*
  * dsp_verify -- lossless verification of the scheduled prefixes.
  *
  * Accept rule, residual and bonus token: page "DSpark.让每一轮计算，多走几步",

@@ -207,3 +207,15 @@ def test_tv_accept_validation(L):
     assert call(ws=FAKE + 8) == 3
     from draft_sampling_lossless_markov_amd import dsp
     assert dsp.dsp_workspace_size(dsp.DSP_WS_TV, 4, 4, 32, 8) > 0
+
+
+def test_schedule_async_validation(L):
+    P = C.c_void_p
+    f = L.dsp_schedule_async
+    f.argtypes = [P, P, P, C.c_int, C.c_double, P, P, P, P, C.c_int, C.c_int, P]
+    ok = [P(FAKE)] * 3
+    assert f(P(0), P(FAKE), P(FAKE), 20, 0.0, *ok, P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(0), P(FAKE), 20, 0.0, *ok, P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), P(FAKE), 3, 0.0, *ok, P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), P(FAKE), 20, 16384.0, *ok, P(FAKE), 4, 4, None) == 1
+    assert f(P(FAKE), P(FAKE), P(FAKE), 10 ** 6, 0.0, *ok, P(FAKE), 4097, 4, None) == 2

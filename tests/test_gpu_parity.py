@@ -499,7 +499,8 @@ def test_persistent_give_up_is_reported(temp):
     check_round(res, temp == 0.0)
 
 
-def test_hip_path_output_law_chi2():
+@pytest.mark.parametrize("scheduler", ["early-stop", "async"])
+def test_hip_path_output_law_chi2(scheduler):
     """Losslessness of the whole HIP path (page "为什么DSpark 可以加速推理？", section on
     the mathematics of speculative decoding: the output law is the target's; page
     "DSpark.让每一轮计算，多走几步", lossless section and its two-token example):
@@ -507,7 +508,10 @@ def test_hip_path_output_law_chi2():
     rows, Markov bias and confidences, the scheduler on (ragged l_r), 5000 rounds
     (>= 10^7 trials at position 0).  The token emitted at every reached position j
     (x_j if accepted, else the correction; the bonus at j = l_r) must follow p_j:
-    chi-square per position, Bonferroni over positions."""
+    chi-square per position, Bonferroni over positions.  Run with the early-stop
+    scheduler and with the capacity-barrier scheduler, whose capacity comes from
+    the confidences of two rounds earlier (page "DeepSeek联合北大最新文章DSpark",
+    挑战2: the barrier is what keeps its global search lossless)."""
     from scipy import stats as sst
     R, gamma, V, r, d = 2048, 8, 8, 8, 16
     gen = torch.Generator(device="cpu").manual_seed(77)
@@ -530,8 +534,16 @@ def test_hip_path_output_law_chi2():
     pos = torch.arange(gamma + 1, device="cuda")[None, :]
     lens = torch.zeros(gamma + 1, dtype=torch.int64, device="cuda")
     rounds = 5000
+    hist = [torch.full((R, gamma), 0.9, device="cuda") for _ in range(2)]
     for rnd in range(rounds):
-        rd.run(inp, 1.0, SEED, rnd)
+        if scheduler == "early-stop":
+            rd.run(inp, 1.0, SEED, rnd)
+        else:
+            rd.draft(inp, 1.0, SEED, rnd)
+            rd.confidence(inp)
+            rd.schedule_async(inp, hist[rnd % 2])     # the confidences of round rnd - 2
+            rd.verify(inp, 1.0, SEED, rnd)
+            hist[rnd % 2].copy_(rd.c)
         n = rd.n_accept.long()[:, None]
         emitted = torch.cat([rd.tok.long(), torch.zeros((R, 1), dtype=torch.long, device="cuda")], 1)
         emitted = torch.where(pos == n, rd.y.long()[:, None], emitted)
@@ -736,6 +748,58 @@ def test_tv_accept_full_size(wid):
     assert np.all((g >= 0) & (g <= 1))
     del inp, rd, ws
     torch.cuda.empty_cache()
+
+
+def test_schedule_async_vs_oracle():
+    """dsp_schedule_async against orc_schedule_async, bit for bit (len, a, B, K): random
+    small instances with jagged and smooth SPS tables and tau0 in {0, 0.5}, then the
+    workloads' full scheduled shapes with the confidence head's own outputs (c_hist
+    from the confidences of an earlier input set)."""
+    rng = np.random.default_rng(50)
+    for trial in range(60):
+        R = int(rng.integers(1, 300))
+        gamma = int(rng.integers(1, 17))
+        if R * gamma > 16384:
+            continue
+        c = rng.uniform(0.02, 1.0, (R, gamma)).astype(np.float32)
+        ch = rng.uniform(0.02, 1.0, (R, gamma)).astype(np.float32)
+        c[rng.random((R, gamma)) < 0.05] = 1.0
+        B_max = int(rng.integers(R, R * (gamma + 1) + 1))
+        Bs = np.arange(1, B_max + 1, dtype=np.float64)
+        if trial % 2:
+            sps = (1.0 / (12 + 0.02 * Bs) * np.where((Bs % 64) < 8, 0.9, 1.0)).astype(np.float32)
+        else:
+            sps = (1.0 / (12 + 0.1 * Bs + 0.0008 * Bs * Bs)).astype(np.float32)
+        tau0 = float(rng.choice([0.0, 0.5]))
+        o_len, o_a, o_B, o_K = orc.schedule_async(c, ch, sps, B_max, tau0)
+        rd = Round(R, gamma, 8, 8)
+        rd.c.copy_(torch.from_numpy(c))
+        inp = dict(sps=torch.from_numpy(sps).cuda(), B_max=B_max, tau0=tau0)
+        rd.schedule_async(inp, torch.from_numpy(ch).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(rd.len), o_len), trial
+        assert np.array_equal(np_(rd.a).view(np.uint32), o_a.view(np.uint32)), trial
+        assert int(np_(rd.B)[0]) == o_B and int(np_(rd.K)[0]) == o_K, (trial, o_B, o_K)
+    for wid in (2, 3, 4):
+        wl = WORKLOADS[wid]
+        _say(f"async schedule at full size: {wl.name}")
+        inps = [make_inputs(wl, s_, device="cuda", layout=BENCH_LAYOUT) for s_ in (0, 1)]
+        R, gamma, V, r = inps[0]["R"], inps[0]["gamma"], inps[0]["V"], inps[0]["r"]
+        rds = [Round(R, gamma, V, r) for _ in inps]
+        for inp_, rd_ in zip(inps, rds):
+            rd_.draft(inp_, 1.0, SEED, 3)
+            rd_.confidence(inp_)
+        rd = rds[0]
+        rd.schedule_async(inps[0], rds[1].c)
+        torch.cuda.synchronize()
+        o_len, o_a, o_B, o_K = orc.schedule_async(np_(rd.c), np_(rds[1].c), np_(inps[0]["sps"]),
+                                                  inps[0]["B_max"], inps[0]["tau0"])
+        assert np.array_equal(np_(rd.len), o_len)
+        assert np.array_equal(np_(rd.a).view(np.uint32), o_a.view(np.uint32))
+        assert int(np_(rd.B)[0]) == o_B and int(np_(rd.K)[0]) == o_K
+        _say(f"  K={o_K} B={o_B}")
+        del inps, rds, rd
+        torch.cuda.empty_cache()
 
 
 def test_zz_sampling_mismatch_rate_over_the_module():

@@ -34,7 +34,7 @@ namespace dsp {
 // overlap.
 // ---------------------------------------------------------------------------
 template <typename LT, bool GREEDY, int PER>
-__global__ __launch_bounds__(256) void draft_pick_kernel(
+__global__ __launch_bounds__(256, 4) void draft_pick_kernel(
     const LT* __restrict__ base, RowStrides bs, const uint16_t* __restrict__ E,
     const uint16_t* __restrict__ W2,
     const int32_t* __restrict__ anchor, int32_t* __restrict__ tok, float* __restrict__ q,

@@ -635,15 +635,23 @@ __device__ __forceinline__ float tile_logit(const uint16_t* __restrict__ W2, int
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int h = lane >> 5, c32 = lane & 31;
-    uint4 af[2][kKSteps];
+    // the fragments in two halves of the k-steps (64 registers each, not 128):
+    // the pick kernels then fit four waves per SIMD instead of two
+    constexpr int kHalf = kKSteps / 2;
+    const uint16_t* wrow[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int v = v0 + 64 * wave + a_row_voff(t, c32);
-        const uint16_t* wrow = W2 + (int64_t)min(v, V - 1) * r;
+    for (int t = 0; t < 2; ++t)
+        wrow[t] = W2 + (int64_t)min(v0 + 64 * wave + a_row_voff(t, c32), V - 1) * r;
+    uint4 af[2][kHalf];
+    auto fetch = [&](int half) {
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks)
-            af[t][ks] = *reinterpret_cast<const uint4*>(wrow + min(ks * kKStep + 8 * h, r - 8));
-    }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < kHalf; ++i)
+                af[t][i] = *reinterpret_cast<const uint4*>(
+                    wrow[t] + min((half * kHalf + i) * kKStep + 8 * h, r - 8));
+    };
+    fetch(0);
     lds_barrier();   // e_row is written
     floatx16 acc[2];
 #pragma unroll
@@ -651,12 +659,20 @@ __device__ __forceinline__ float tile_logit(const uint16_t* __restrict__ W2, int
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (c32 == 0) u = *reinterpret_cast<const uint4*>(e_row + ks * kKStep + 8 * h);
-        const bf16x8 bv = as_bf16x8(u);
+    for (int half = 0; half < 2; ++half) {
+        if (half == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(1);
+        }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma32_bf16(as_bf16x8(af[t][ks]), bv, acc[t]);
+        for (int i = 0; i < kHalf; ++i) {
+            const int ks = half * kHalf + i;
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (c32 == 0) u = *reinterpret_cast<const uint4*>(e_row + ks * kKStep + 8 * h);
+            const bf16x8 bv = as_bf16x8(u);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[t] = mfma32_bf16(as_bf16x8(af[t][i]), bv, acc[t]);
+        }
     }
     if (c32 == 0) {
 #pragma unroll

@@ -86,10 +86,12 @@ __device__ __forceinline__ int clamp_len(const int32_t* len, int n, int gamma)
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// verify_rows: one workgroup per (request, row, 32-tile span) item; rows past
-// l_r return at once.  Wave w covers tiles [32 sp + 8 w, +8): lanes 8i .. 8i+7
-// own tile i of the wave, 32 values each (load k reads columns k*64 + 8*(l%8)
-// .. +7 of the tile, so each load instruction moves eight whole 128-byte runs).
+// verify_rows: one workgroup per (request, 32-tile span), looping over the
+// request's verified rows j = 0 .. l_r (so no workgroup is launched for a row
+// that is not verified); the next row's words are requested before the current
+// row is reduced.  Wave w covers tiles [32 sp + 8 w, +8): lanes 8i .. 8i+7 own
+// tile i of the wave, 32 values each (load k reads columns k*64 + 8*(l%8) .. +7
+// of the tile, so each load instruction moves eight whole 128-byte runs).
 // ---------------------------------------------------------------------------
 template <typename LT, bool GREEDY>
 __global__ __launch_bounds__(256) void verify_rows_kernel(
@@ -107,85 +109,94 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
         ws.run_ctl[0] = ctl0;
     }
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
-    const int per_req = (gamma + 1) * spans;
     const bool vec_ok = rows_vec(ts, V, Logit<LT>::kVecAlign);
-    const int item = blockIdx.x;
-    const int n = item / per_req;
-    const int rem = item - n * per_req;
-    const int j = rem / spans, sp = rem - (rem / spans) * spans;
+    const int n = blockIdx.x / spans;
+    const int sp = blockIdx.x - n * spans;
     const int l = clamp_len(len, n, gamma);
-    if (j > l) return;
-    const LT* row = target + (int64_t)n * ts.rs + (int64_t)j * ts.ps;
     const int t = sp * kSpanTiles + wave * 8 + (lane >> 3);
     const int sub = lane & 7;
-    uint4 raw[4][RW];
+
+    auto load_row = [&](int j, uint4 (&raw)[4][RW]) {
+        const LT* row = target + (int64_t)n * ts.rs + (int64_t)j * ts.ps;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int v0 = t * kVocabTile + k * 64 + sub * 8;
-        Logit<LT>::load8_raw(row, min(v0, V), V, vec_ok && v0 + 8 <= V, raw[k]);
-    }
-    Part* out = ws.rowpart + ((int64_t)n * (gamma + 1) + j) * n_vt;
-    if constexpr (GREEDY) {
-        ArgMax am{-INFINITY, 0x7fffffff};
+        for (int k = 0; k < 4; ++k) {
+            const int v0 = t * kVocabTile + k * 64 + sub * 8;
+            Logit<LT>::load8_raw(row, min(v0, V), V, vec_ok && v0 + 8 <= V, raw[k]);
+        }
+    };
+    auto reduce_row = [&](int j, const uint4 (&raw)[4][RW]) {
+        Part* out = ws.rowpart + ((int64_t)n * (gamma + 1) + j) * n_vt;
+        if constexpr (GREEDY) {
+            ArgMax am{-INFINITY, 0x7fffffff};
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int v = t * kVocabTile + k * 64 + sub * 8 + e;
-                if (v < V) am = argmax_merge(am, ArgMax{Logit<LT>::raw_at(raw[k], e), v});
+                for (int e = 0; e < 8; ++e) {
+                    const int v = t * kVocabTile + k * 64 + sub * 8 + e;
+                    if (v < V) am = argmax_merge(am, ArgMax{Logit<LT>::raw_at(raw[k], e), v});
+                }
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) {
+                ArgMax b;
+                b.v = __shfl_xor(am.v, o, kWave);
+                b.i = __shfl_xor(am.i, o, kWave);
+                am = argmax_merge(am, b);
             }
+            if (sub == 0 && t < n_vt) out[t] = Part{am.v, am.i, 0.0};
+            // the wave's 8 tiles (lane groups) combined: one partial per wave
+            ArgMax b8;
+            b8.v = __shfl_xor(am.v, 8, kWave);
+            b8.i = __shfl_xor(am.i, 8, kWave);
+            am = xargmax<32>(xargmax<16>(argmax_merge(am, b8)));
+            if (lane == 0)
+                ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{am.v, am.i, 0.0};
+        } else {
+            float m = -INFINITY;
 #pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            ArgMax b;
-            b.v = __shfl_xor(am.v, o, kWave);
-            b.i = __shfl_xor(am.i, o, kWave);
-            am = argmax_merge(am, b);
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, Logit<LT>::raw_at(raw[k], e));
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+            const float mref = (m == -INFINITY) ? 0.0f : m;
+            // fp32 weights relative to the tile maximum (the reference a pick's
+            // rescan recomputes), summed in fp64 per lane and across the tile's lanes
+            float x[32];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[8 * k + e] = Logit<LT>::raw_at(raw[k], e);
+            double s = sum_w64(x, mref, itL);
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
+            if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
+            // the wave's 8 tiles (lane groups) rescaled to their max and summed:
+            // one partial per wave (an fp32 factor: these partials only give each
+            // row's normaliser, to ~1e-7; the draws use the tile partials and rescans)
+            float mw = fmaxf(m, __shfl_xor(m, 8, kWave));
+            mw = xmax<32>(xmax<16>(mw));
+            double sw = (m == -INFINITY) ? 0.0 : s * (double)wexp(m - mw, itL);
+            sw += __shfl_xor(sw, 8, kWave);
+            sw = xsum<32>(xsum<16>(sw));
+            if (lane == 0)
+                ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{mw, 0, sw};
+            if (tid == 0 && j < l) {
+                const int xj = tok[(int64_t)n * gamma + j];
+                const int lo = sp * kSpanTiles * kVocabTile;
+                if (xj >= lo && xj < min(V, lo + kSpanTiles * kVocabTile))
+                    ws.zx[(int64_t)n * gamma + j] =
+                        Logit<LT>::at(target + (int64_t)n * ts.rs + (int64_t)j * ts.ps, xj);
+            }
         }
-        if (sub == 0 && t < n_vt) out[t] = Part{am.v, am.i, 0.0};
-        // the wave's 8 tiles (lane groups) combined: one partial per wave
-        ArgMax b8;
-        b8.v = __shfl_xor(am.v, 8, kWave);
-        b8.i = __shfl_xor(am.i, 8, kWave);
-        am = xargmax<32>(xargmax<16>(argmax_merge(am, b8)));
-        if (lane == 0)
-            ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{am.v, am.i, 0.0};
-    } else {
-        float m = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, Logit<LT>::raw_at(raw[k], e));
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        const float mref = (m == -INFINITY) ? 0.0f : m;
-        // fp32 weights relative to the tile maximum (the reference a pick's rescan
-        // recomputes), summed in fp64 per lane and across the tile's lanes
-        float x[32];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[8 * k + e] = Logit<LT>::raw_at(raw[k], e);
-        double s = sum_w64(x, mref, itL);
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
-        if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
-        // the wave's 8 tiles (lane groups) rescaled to their max in fp64 and
-        // summed: one partial per wave
-        float mw = fmaxf(m, __shfl_xor(m, 8, kWave));
-        mw = xmax<32>(xmax<16>(mw));
-        // (an fp32 factor: these partials only give each row's normaliser, to
-        // ~1e-7; the draws use the tile partials and rescans)
-        double sw = (m == -INFINITY) ? 0.0 : s * (double)wexp(m - mw, itL);
-        sw += __shfl_xor(sw, 8, kWave);
-        sw = xsum<32>(xsum<16>(sw));
-        if (lane == 0)
-            ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{mw, 0, sw};
-        if (tid == 0 && j < l) {
-            const int xj = tok[(int64_t)n * gamma + j];
-            const int lo = sp * kSpanTiles * kVocabTile;
-            if (xj >= lo && xj < min(V, lo + kSpanTiles * kVocabTile))
-                ws.zx[(int64_t)n * gamma + j] = Logit<LT>::at(row, xj);
-        }
+    };
+    uint4 ra[4][RW], rb[4][RW];
+    load_row(0, ra);
+    for (int j = 0; j <= l; j += 2) {
+        if (j + 1 <= l) load_row(j + 1, rb);
+        reduce_row(j, ra);
+        if (j + 1 > l) break;
+        if (j + 2 <= l) load_row(j + 2, ra);
+        reduce_row(j + 1, rb);
     }
 }
 
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
 // verify_pick: one workgroup per request (sampling)
 // ---------------------------------------------------------------------------
 template <typename LT, int PER>
-__global__ __launch_bounds__(256) void verify_pick_kernel(
+__global__ __launch_bounds__(256, 4) void verify_pick_kernel(
     const LT* __restrict__ target, RowStrides ts, const LT* __restrict__ base, RowStrides bs,
     const uint16_t* __restrict__ E, const uint16_t* __restrict__ W2,
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ tok,
@@ -497,7 +508,7 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     const bool greedy = (temperature == 0.0f);
     const float it = greedy ? 1.0f : 1.0f / temperature;
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
-    const int64_t items = (int64_t)R * (gamma + 1) * spans;
+    const int64_t items = (int64_t)R * spans;   // verify_rows: (request, span) items
     const dim3 g1((unsigned)items);
     if (path == kPathPersistent && !std::is_same<LT, uint16_t>::value) return hipErrorNotSupported;
     if (greedy) {
@@ -705,7 +716,7 @@ static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, R
     hipLaunchKernelGGL(tv_prep_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, anchor, tok,
                        R, gamma, V, ws);
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
-    const int64_t items = (int64_t)R * (gamma + 1) * spans;
+    const int64_t items = (int64_t)R * spans;
     hipLaunchKernelGGL((verify_rows_kernel<LT, false>), dim3((unsigned)items), dim3(256), 0, s, target,
                        ts, tok, ws.lens, R, gamma, V, it, n_vt, ws.v, 0u);
     const int np = 4 * spans;

@@ -18,6 +18,7 @@
 #include <atomic>
 
 #include "bias_tile.h"
+#include "draft_pass.h"
 #include "draft_run.h"
 #include "dsp_device.h"
 #include "dsp_launch.h"
@@ -181,7 +182,10 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     a.ctl = ctl;
     const dim3 g1(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
     const bool vec = rows_vec(bs, V, 8);
-    if (greedy && vec)
+    if (sizeof(LT) == 2 && vec) {   // bf16 rows of 16-byte words: the software-pipelined pass
+        if (greedy) hipLaunchKernelGGL((draft_pass_kernel<true>), g1, dim3(kDpThreads), 0, s, a);
+        else hipLaunchKernelGGL((draft_pass_kernel<false>), g1, dim3(kDpThreads), 0, s, a);
+    } else if (greedy && vec)
         hipLaunchKernelGGL((bias_pass_kernel<LT, kGreedy, true>), g1, dim3(256), 0, s, a);
     else if (greedy)
         hipLaunchKernelGGL((bias_pass_kernel<LT, kGreedy, false>), g1, dim3(256), 0, s, a);

@@ -177,3 +177,26 @@ def make_inputs(wl: Workload, set_idx: int = 0, device="cpu", *, seed_base: int 
     return dict(base=base, target=target, E=E, W2=W2, h=h, w=w, T=T, offset=offset,
                 anchor=anchor, sps=sps, R=R, gamma=gamma, V=V, r=r, d=d, B_max=B_max,
                 mode=wl.mode, tau0=wl.tau0, temperature=wl.temperature, layout=layout)
+
+
+def calibration_set(N: int, gamma: int, seed: int, t_true=None, mu: float = 1.5,
+                    sd: float = 1.5, device="cpu"):
+    """Held-out calibration data for sequential temperature scaling.
+
+    z [N, gamma] fp32 raw confidence logits ~ N(mu, sd^2); acc [N] int32 the
+    number of leading draft positions accepted, drawn position by position:
+    given positions 0 .. k-1 accepted, position k is accepted with probability
+    1 / (1 + exp(-z[n, k] / t_true[k])).  t_true > 1 makes the raw logits
+    overconfident, as the pages describe the uncalibrated head.  This is the
+    data law of the synthetic labels, not a step of the method.
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    if t_true is None:
+        t_true = torch.linspace(1.3, 2.2, gamma, dtype=torch.float64)
+    t_true = torch.as_tensor(t_true, dtype=torch.float64)
+    z = (mu + sd * torch.randn(N, gamma, generator=g, dtype=torch.float64)).to(torch.float32)
+    u = torch.rand(N, gamma, generator=g, dtype=torch.float64)
+    p = torch.sigmoid(z.double() / t_true)
+    ok = (u < p).to(torch.int32)
+    acc = torch.cumprod(ok, dim=1).sum(dim=1).to(torch.int32)
+    return z.to(device), acc.to(device)

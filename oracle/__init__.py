@@ -46,6 +46,11 @@ def lib():
                                             P, P]
         _lib.orc_tv_accept.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P, P,
                                        P, C.c_double, P]
+        _lib.orc_confidence_logit.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P,
+                                              P, P, P, P, P]
+        _lib.orc_sts_fit.argtypes = [C.c_int, C.c_int, P, P, C.c_double, C.c_double, C.c_int, P,
+                                     P, P]
+        _lib.orc_ece.argtypes = [C.c_int, C.c_int, P, P, P, C.c_int, P, P]
     return _lib
 
 
@@ -148,6 +153,55 @@ def confidence(h, E, anchor, tok, w, T, offset=None):
     _check(lib().orc_confidence(n, gamma, d, V, r, _p(h), _p(E), _p(anchor), _p(tok), _p(w),
                                 _p(T), _p(offset), _p(c), _p(flag)), "confidence")
     return c, flag
+
+
+def confidence_logit(h, E, anchor, tok, w, offset=None):
+    """y [n, gamma] fp64: the confidence head's sigmoid argument before temperature."""
+    h = _c(h, np.uint16)
+    n, gamma, d = h.shape
+    E = _c(E, np.uint16)
+    V, r = E.shape
+    y = np.zeros((n, gamma), np.float64)
+    _check(lib().orc_confidence_logit(n, gamma, d, V, r, _p(h), _p(E), _p(_c(anchor, np.int32)),
+                                      _p(_c(tok, np.int32)), _p(_c(w, np.float32)),
+                                      _p(None if offset is None else _c(offset, np.float32)),
+                                      _p(y)), "confidence_logit")
+    return y
+
+
+STS_GRID = 256
+
+
+def sts_fit(z, acc, t_lo=1.0 / 16, t_hi=16.0, G=STS_GRID):
+    """Sequential temperature scaling on held-out (z [N, gamma] f32, acc [N]).
+
+    t_lo and t_hi bound the temperature grid; a comparison with a caller that
+    receives them as fp32 passes the fp32-rounded values.  Returns beta [gamma]
+    (fp64 grid points), T = fp32(1 / beta), the final objective nll [gamma] and
+    the relative objective gaps [gamma, 2] between the best and second-best
+    point of each grid stage."""
+    z = _c(z, np.float32)
+    N, gamma = z.shape
+    acc = _c(acc, np.int32)
+    beta = np.zeros(gamma, np.float64)
+    nll = np.zeros(gamma, np.float64)
+    gap = np.zeros((gamma, 2), np.float64)
+    _check(lib().orc_sts_fit(N, gamma, _p(z), _p(acc), float(t_lo), float(t_hi), int(G), _p(beta),
+                             _p(nll), _p(gap)), "sts_fit")
+    T = (1.0 / beta).astype(np.float32)
+    return beta, T, nll, gap
+
+
+def ece(z, acc, T=None, M=15):
+    """Expected calibration error of the cumulative survival; returns (ece, n_edge)."""
+    z = _c(z, np.float32)
+    N, gamma = z.shape
+    out = np.zeros(1, np.float64)
+    edge = np.zeros(1, np.int32)
+    _check(lib().orc_ece(N, gamma, _p(z), _p(_c(acc, np.int32)),
+                         _p(None if T is None else _c(T, np.float32)), int(M), _p(out), _p(edge)),
+           "ece")
+    return float(out[0]), int(edge[0])
 
 
 def schedule(c32, sps, B_max, tau0, mode):

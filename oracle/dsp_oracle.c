@@ -600,3 +600,171 @@ int orc_schedule_async(int R, int gamma, const float* c, const float* c_hist, co
     free(cs); free(ah);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Confidence logit [P4-2.1]: the argument of the sigmoid before the         */
+/* per-position temperature, y = w . [h_k; E[x_{k-1}]] + offset (fp64).       */
+/* ------------------------------------------------------------------------- */
+
+int orc_confidence_logit(int n, int gamma, int d, int V, int r,
+                         const uint16_t* h, const uint16_t* E,
+                         const int32_t* anchor, const int32_t* tok,
+                         const float* w, const float* offset, double* y_out)
+{
+    if (n < 0 || gamma <= 0 || d < 0 || r <= 0 || V <= 0) return 1;
+    for (int i = 0; i < n; ++i) {
+        for (int k = 0; k < gamma; ++k) {
+            const size_t ik = (size_t)i * gamma + k;
+            const int prev = (k == 0) ? anchor[i] : tok[ik - 1];
+            double y = 0.0;
+            for (int t = 0; t < d; ++t)
+                y += (double)w[t] * (double)bf16_to_float(h[ik * (size_t)d + t]);
+            if (prev >= 0)
+                for (int t = 0; t < r; ++t)
+                    y += (double)w[d + t] * (double)bf16_to_float(E[(size_t)prev * r + t]);
+            if (offset) y += (double)offset[i];
+            y_out[ik] = y;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Sequential temperature scaling [P4-2.1], [P2-SCH] (calibration of the      */
+/* cumulative prefix survival on held-out data, position by position from     */
+/* left to right).  Reading: sample n of the held-out set carries the raw     */
+/* confidence logits z[n, k] and the number of its draft tokens accepted,     */
+/* acc[n] (every position verified); s[n, k] = 1 when acc[n] > k, i.e. the    */
+/* prefix through position k survived.  With beta_j = 1 / T_j,                */
+/*   a[n, k] = prod_{j <= k} sigma(beta_j z[n, j])   (a[n, -1] = 1)           */
+/* and T_k, with T_0 .. T_{k-1} already fixed, minimises the binary cross-   */
+/* entropy of a[n, k] against s[n, k] over all n:                            */
+/*   F_k(beta) = - sum_n [ s ln(a_{k-1} sigma(beta z))                        */
+/*                       + (1 - s) ln(1 - a_{k-1} sigma(beta z)) ]            */
+/* The minimiser is searched on two grids of G values of beta, each point     */
+/* fma(g, step, lo) in fp64: first [1 / t_hi, 1 / t_lo], then the span of the */
+/* first grid's best point and its two neighbours; the lowest index wins a    */
+/* tie and a NaN objective counts as +inf.  ln a and b = 1 - a are carried    */
+/* separately, so that neither is formed by cancellation:                     */
+/*   s = 1: -ln(a sigma(x))     = -(ln a + ln sigma(x))                       */
+/*   s = 0: -ln(1 - a sigma(x)) = -ln(b + a sigma(-x))                        */
+/*   ln sigma(x) = -(max(-x, 0) + log1p(exp(-|x|)))                          */
+/* ------------------------------------------------------------------------- */
+
+static double log_sigmoid(double x) { return -(fmax(-x, 0.0) + log1p(exp(-fabs(x)))); }
+
+static double survival_bce(double x, int s, double la, double b)
+{
+    if (s) return -(la + log_sigmoid(x));
+    return -log(b + exp(la + log_sigmoid(-x)));
+}
+
+static double sts_objective(int N, int gamma, int k, const float* z, const int32_t* acc,
+                            const double* la, const double* b, double beta)
+{
+    double f = 0.0;
+    for (int n = 0; n < N; ++n)
+        f += survival_bce(beta * (double)z[(size_t)n * gamma + k], acc[n] > k, la[n], b[n]);
+    return f;
+}
+
+/* best of G grid points lo + g step; gap = (second best - best) / |best| */
+static int sts_grid_argmin(int N, int gamma, int k, const float* z, const int32_t* acc,
+                           const double* la, const double* b, int G, double lo, double step,
+                           double* f_best, double* gap)
+{
+    int best = 0;
+    double fb = INFINITY, f2 = INFINITY;
+    for (int g = 0; g < G; ++g) {
+        double f = sts_objective(N, gamma, k, z, acc, la, b, fma((double)g, step, lo));
+        if (isnan(f)) f = INFINITY;
+        if (f < fb) {
+            f2 = fb;
+            fb = f;
+            best = g;
+        } else if (f < f2) {
+            f2 = f;
+        }
+    }
+    *f_best = fb;
+    *gap = (f2 - fb) / fabs(fb);
+    return best;
+}
+
+int orc_sts_fit(int N, int gamma, const float* z, const int32_t* acc, double t_lo, double t_hi,
+                int G, double* beta_out, double* nll_out, double* gap_out)
+{
+    if (N <= 0 || gamma <= 0 || G < 2 || !(t_lo > 0.0) || !(t_hi > t_lo)) return 1;
+    double* la = (double*)calloc((size_t)N, sizeof(double));
+    double* b = (double*)calloc((size_t)N, sizeof(double));
+    if (!la || !b) { free(la); free(b); return 2; }
+    const double lo1 = 1.0 / t_hi, hi1 = 1.0 / t_lo;
+    const double step1 = (hi1 - lo1) / (double)(G - 1);
+    for (int k = 0; k < gamma; ++k) {
+        double f1, g1gap, f2, g2gap;
+        const int g1 = sts_grid_argmin(N, gamma, k, z, acc, la, b, G, lo1, step1, &f1, &g1gap);
+        const double lo2 = fma((double)(g1 > 0 ? g1 - 1 : 0), step1, lo1);
+        const double hi2 = fma((double)(g1 < G - 1 ? g1 + 1 : G - 1), step1, lo1);
+        const double step2 = (hi2 - lo2) / (double)(G - 1);
+        const int g2 = sts_grid_argmin(N, gamma, k, z, acc, la, b, G, lo2, step2, &f2, &g2gap);
+        const double beta = fma((double)g2, step2, lo2);
+        beta_out[k] = beta;
+        nll_out[k] = f2;
+        gap_out[2 * k] = g1gap;
+        gap_out[2 * k + 1] = g2gap;
+        /* carry the survival through position k with the fitted temperature */
+        for (int n = 0; n < N; ++n) {
+            const double x = beta * (double)z[(size_t)n * gamma + k];
+            const double la_new = la[n] + log_sigmoid(x);
+            b[n] = b[n] + exp(la[n] + log_sigmoid(-x));
+            la[n] = la_new;
+        }
+    }
+    free(la);
+    free(b);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Expected calibration error of the cumulative survival [P4-2.1] (the page  */
+/* reports ECE before and after temperature scaling).  Reading: every pair   */
+/* (n, k) is one prediction a[n, k] = prod_{j <= k} sigma(z[n, j] / T_j)      */
+/* (T = NULL: T_j = 1) of the outcome s[n, k] = (acc[n] > k); predictions     */
+/* fall in M equal-width bins, bin = min(floor(a M), M - 1), and             */
+/*   ECE = sum_bins |sum_{bin} (s - a)| / (N gamma)                           */
+/* i.e. the bin-size-weighted gap between the bin's accept rate and its mean  */
+/* prediction.  sigma(x) = exp(ln sigma(x)).  n_edge counts the predictions   */
+/* within 1e-9 of a bin edge (where another rounding may pick the next bin).  */
+/* ------------------------------------------------------------------------- */
+
+int orc_ece(int N, int gamma, const float* z, const int32_t* acc, const float* T, int M,
+            double* ece, int* n_edge)
+{
+    if (N <= 0 || gamma <= 0 || M <= 0) return 1;
+    double* sa = (double*)calloc((size_t)M, sizeof(double));
+    double* ss = (double*)calloc((size_t)M, sizeof(double));
+    if (!sa || !ss) { free(sa); free(ss); return 2; }
+    int edge = 0;
+    for (int n = 0; n < N; ++n) {
+        double a = 1.0;
+        for (int k = 0; k < gamma; ++k) {
+            double x = (double)z[(size_t)n * gamma + k];
+            if (T) x = x / (double)T[k];
+            a = a * exp(log_sigmoid(x));
+            const double aM = a * (double)M;
+            int bin = (int)floor(aM);
+            if (bin > M - 1) bin = M - 1;
+            if (bin < 0) bin = 0;
+            if (fabs(aM - nearbyint(aM)) < 1e-9 && aM > 0.5 && aM < M - 0.5) ++edge;
+            sa[bin] += a;
+            ss[bin] += (acc[n] > k) ? 1.0 : 0.0;
+        }
+    }
+    double e = 0.0;
+    for (int m = 0; m < M; ++m) e += fabs(ss[m] - sa[m]);
+    *ece = e / ((double)N * (double)gamma);
+    *n_edge = edge;
+    free(sa);
+    free(ss);
+    return 0;
+}

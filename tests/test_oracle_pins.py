@@ -962,3 +962,133 @@ def test_async_schedule_causality_and_why_the_barrier_matters(orc):
         g1, _, _, _ = orc.schedule_async(c2, c2, sps, B_max, 0.0)
         violations += min(g0[r], j + 1) != min(g1[r], j + 1)
     assert violations > 0
+
+
+# ---------------------------------------------------------------------------
+# Sequential temperature scaling and ECE (page "DeepSeek联合北大最新文章DSpark",
+# section 2.1: temperatures calibrated position by position, left to right,
+# and the calibration error they reduce).
+# ---------------------------------------------------------------------------
+def _calib(N, gamma, seed, t_true=None):
+    from draft_sampling_lossless_markov_amd.workloads import calibration_set
+    z, acc = calibration_set(N, gamma, seed, t_true)
+    return z.numpy(), acc.numpy()
+
+
+def test_ece_hand_example_bins_and_cumulative_survival():
+    import oracle
+    l19 = math.log(19.0)
+    # one position: predictions 0.05 (bin 0 of 10) accepted, 0.95 (bin 9) rejected
+    z = np.array([[-l19], [l19]], np.float32)
+    e, edge = oracle.ece(z, np.array([1, 0], np.int32), M=10)
+    assert edge == 0
+    assert e == pytest.approx((abs(1 - 0.05) + abs(0 - 0.95)) / 2, abs=1e-6)
+    # two positions, cumulative survival 0.95 then 0.9025, accepted length 1:
+    # both in bin 9, outcomes 1 then 0
+    z = np.array([[l19, l19]], np.float32)
+    e, _ = oracle.ece(z, np.array([1], np.int32), M=10)
+    assert e == pytest.approx(abs((1 - 0.95) + (0 - 0.9025)) / 2, abs=1e-6)
+    # temperatures divide the logits: T = 2 at the first position of sigma(2 ln 19)
+    z = np.array([[2 * l19]], np.float32)
+    e, _ = oracle.ece(z, np.array([1], np.int32), T=np.array([2.0], np.float32), M=10)
+    assert e == pytest.approx(0.05, abs=1e-6)
+
+
+def test_ece_one_bin_is_the_mean_gap():
+    # with a single bin ECE reduces to |mean accept - mean prediction| over all
+    # (sample, position) pairs; the predictions by scipy's logistic function
+    import oracle
+    from scipy.special import expit
+    z, acc = _calib(3000, 4, seed=11)
+    T = np.array([1.2, 1.7, 0.9, 2.5], np.float32)
+    a = np.cumprod(expit(z.astype(np.float64) / T.astype(np.float64)), axis=1)
+    s = (acc[:, None] > np.arange(4)[None, :]).astype(np.float64)
+    e, _ = oracle.ece(z, acc, T=T, M=1)
+    assert e == pytest.approx(abs(s.mean() - a.mean()), rel=1e-12, abs=1e-15)
+
+
+def test_ece_separates_calibrated_from_overconfident():
+    import oracle
+    t_true = np.array([1.0, 1.0, 1.0])
+    z, acc = _calib(40000, 3, seed=5, t_true=t_true)
+    e_cal, _ = oracle.ece(z, acc, M=15)
+    assert e_cal < 0.01
+    z2, acc2 = _calib(40000, 3, seed=5, t_true=np.array([2.5, 2.5, 2.5]))
+    e_over, _ = oracle.ece(z2, acc2, M=15)
+    assert e_over > 0.05
+
+
+def test_sts_first_position_is_a_logistic_fit_without_intercept():
+    # at the first position the survival is sigma(beta z) itself: the objective
+    # is the logistic log loss, minimised here by scipy's bounded search
+    import oracle
+    from scipy.optimize import minimize_scalar
+    from scipy.special import log_expit
+    z, acc = _calib(5000, 2, seed=3)
+    beta, T, nll, gap = oracle.sts_fit(z, acc)
+    x = z[:, 0].astype(np.float64)
+    s = (acc > 0).astype(np.float64)
+
+    def loss(b):
+        return -np.sum(s * log_expit(b * x) + (1 - s) * log_expit(-b * x))
+
+    lo, hi = 1.0 / 16, 16.0
+    res = minimize_scalar(loss, bounds=(lo, hi), method="bounded", options={"xatol": 1e-10})
+    step1 = (hi - lo) / 255
+    step2 = 2 * step1 / 255
+    assert abs(beta[0] - res.x) <= step2
+    assert nll[0] == pytest.approx(loss(beta[0]), rel=1e-12)
+    assert nll[0] >= res.fun - 1e-9
+
+
+def test_sts_recovers_generating_temperatures():
+    import oracle
+    t_true = np.array([1.5, 2.0, 1.2, 1.8])
+    z, acc = _calib(20000, 4, seed=7, t_true=t_true)
+    beta, T, nll, gap = oracle.sts_fit(z, acc)
+    assert np.all(np.abs(T / t_true - 1) < 0.08), (T, t_true)
+    e_before, _ = oracle.ece(z, acc)
+    e_after, _ = oracle.ece(z, acc, T=T)
+    assert e_after < 0.5 * e_before
+
+
+def test_sts_fit_is_sequential_and_on_grid():
+    import oracle
+    z, acc = _calib(2000, 3, seed=9)
+    beta, T, nll, gap = oracle.sts_fit(z, acc)
+    z2 = z.copy()
+    z2[:, 2] = -z2[:, 2] + 0.5
+    beta2, _, _, _ = oracle.sts_fit(z2, acc)
+    # a later position's logits cannot move an earlier temperature
+    assert beta2[0] == beta[0] and beta2[1] == beta[1]
+    assert beta2[2] != beta[2]
+    # every fitted beta is a point of its second grid, inside [1/16, 16]
+    assert np.all((beta >= 1.0 / 16) & (beta <= 16.0))
+    assert np.all(gap >= 0)
+
+
+def test_sts_degenerate_all_zero_logits_take_the_first_grid_point():
+    import oracle
+    z = np.zeros((100, 2), np.float32)
+    acc = np.full(100, 1, np.int32)
+    beta, T, nll, gap = oracle.sts_fit(z, acc, t_lo=0.25, t_hi=4.0)
+    # sigma(beta 0) = 1/2 for every beta: a tie everywhere, the lowest index wins
+    assert np.all(beta == 0.25) and np.all(T == 4.0)
+    assert nll[0] == pytest.approx(100 * math.log(2.0), rel=1e-15)
+
+
+def test_confidence_logit_is_the_sigmoid_argument():
+    import oracle
+    rng = np.random.default_rng(2)
+    n, gamma, d, V, r = 3, 4, 16, 32, 8
+    h = bf16(rng.normal(0, 1, (n, gamma, d)))
+    E = bf16(rng.normal(0, 0.1, (V, r)))
+    anchor = rng.integers(0, V, n).astype(np.int32)
+    tok = rng.integers(0, V, (n, gamma)).astype(np.int32)
+    w = rng.normal(0, 0.1, d + r).astype(np.float32)
+    T = np.array([1.0, 1.3, 0.7, 2.0], np.float32)
+    off = rng.normal(0, 1, n).astype(np.float32)
+    y = oracle.confidence_logit(h, E, anchor, tok, w, off)
+    c, _ = oracle.confidence(h, E, anchor, tok, w, T, off)
+    from scipy.special import expit
+    np.testing.assert_allclose(c, expit(y / T[None, :].astype(np.float64)), rtol=1e-14)

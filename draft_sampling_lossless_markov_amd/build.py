@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsp.so")
-SOURCES = ["draft.hip", "confidence.hip", "schedule.hip", "verify.hip", "api.cpp"]
+SOURCES = ["draft.hip", "confidence.hip", "schedule.hip", "verify.hip", "sts.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -129,10 +129,12 @@ const char* dsp_status_string(dsp_status s)
 
 const char* dsp_last_error(void) { return g_err; }
 
-int dsp_version(void) { return 400; }
+int dsp_version(void) { return 410; }
 
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r)
 {
+    if (which == DSP_WS_STS) return (R > 0 && gamma > 0) ? dsp::sts_workspace_bytes(R) : 0;
+    if (which == DSP_WS_ECE) return dsp::ece_workspace_bytes();
     if (R <= 0 || gamma <= 0 || V <= 0 || r <= 0) return 0;
     if (which == DSP_WS_DRAFT) return dsp::draft_workspace_bytes(R, V);
     if (which == DSP_WS_VERIFY) return dsp::verify_workspace_bytes(R, gamma, V);
@@ -234,6 +236,66 @@ dsp_status dsp_confidence(const uint16_t* h, const uint16_t* E, const int32_t* a
     return hip_status(dsp::launch_confidence(h, E, anchor, tok, w, T, offset, c, R, gamma, d, V,
                                              r, static_cast<hipStream_t>(stream)),
                       "dsp_confidence launch");
+}
+
+dsp_status dsp_confidence_logit(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
+                                const int32_t* tok, const float* w, const float* offset, float* y,
+                                int R, int gamma, int d, int V, int r, void* stream)
+{
+    if (!E || !anchor || !tok || !w || !y || (!h && d > 0))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_confidence_logit: null pointer argument");
+    if (R <= 0 || gamma <= 0 || V <= 0 || r <= 0 || d < 0)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_confidence_logit: bad sizes R=%d gamma=%d d=%d V=%d r=%d",
+                    R, gamma, d, V, r);
+    if ((int64_t)R * gamma > (int64_t)INT32_MAX / 2)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_confidence_logit: R * gamma too large");
+    if ((h && !aligned16(h)) || !aligned16(w))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_confidence_logit: h and w must be 16-byte aligned");
+    return hip_status(dsp::launch_confidence(h, E, anchor, tok, w, nullptr, offset, y, R, gamma, d,
+                                             V, r, static_cast<hipStream_t>(stream)),
+                      "dsp_confidence_logit launch");
+}
+
+dsp_status dsp_sts_fit(const float* z, const int32_t* n_acc, int N, int gamma, float t_lo,
+                       float t_hi, float* T, double* nll, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!z || !n_acc || !T || !ws)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_sts_fit: null pointer argument");
+    if (N <= 0 || gamma <= 0)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_sts_fit: bad sizes N=%d gamma=%d", N, gamma);
+    if ((int64_t)N * gamma > (int64_t)INT32_MAX / 2)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_sts_fit: N * gamma too large");
+    if (!(t_lo > 0.0f) || !(t_hi > t_lo) || !std::isfinite(t_hi))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_sts_fit: need 0 < t_lo < t_hi < inf (got %g, %g)",
+                    (double)t_lo, (double)t_hi);
+    const size_t need = dsp::sts_workspace_bytes(N);
+    if (ws_bytes < need || !aligned16(ws))
+        return fail(DSP_ERR_WORKSPACE, "dsp_sts_fit: workspace of %zu bytes (16-byte aligned), %zu needed",
+                    ws_bytes, need);
+    return hip_status(dsp::launch_sts_fit(z, n_acc, N, gamma, (double)t_lo, (double)t_hi, T, nll, ws,
+                                          static_cast<hipStream_t>(stream)),
+                      "dsp_sts_fit launch");
+}
+
+dsp_status dsp_ece(const float* z, const int32_t* n_acc, const float* T, int N, int gamma,
+                   int n_bins, double* ece, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!z || !n_acc || !ece || !ws)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_ece: null pointer argument");
+    if (N <= 0 || gamma <= 0 || n_bins <= 0)
+        return fail(DSP_ERR_INVALID_ARG, "dsp_ece: bad sizes N=%d gamma=%d n_bins=%d", N, gamma, n_bins);
+    if (n_bins > dsp::kEceMaxBins)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_ece: n_bins = %d exceeds %d", n_bins, dsp::kEceMaxBins);
+    if ((int64_t)N * gamma > dsp::kEceMaxPredictions)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_ece: N * gamma = %lld exceeds 2^23",
+                    (long long)N * gamma);
+    const size_t need = dsp::ece_workspace_bytes();
+    if (ws_bytes < need || !aligned16(ws))
+        return fail(DSP_ERR_WORKSPACE, "dsp_ece: workspace of %zu bytes (16-byte aligned), %zu needed",
+                    ws_bytes, need);
+    return hip_status(dsp::launch_ece(z, n_acc, T, N, gamma, n_bins, ece, ws,
+                                      static_cast<hipStream_t>(stream)),
+                      "dsp_ece launch");
 }
 
 dsp_status dsp_schedule(const float* c, const float* sps, int B_max, double tau0, int mode,

@@ -7,7 +7,9 @@
 //
 // One wave per (request, position) row: a d + r long dot product accumulated in
 // fp64 (bf16 x fp32 products are exact in fp64), then the sigmoid in fp64 and one
-// rounding to fp32.  Bound by streaming h once.
+// rounding to fp32.  Bound by streaming h once.  Without temperatures (T null)
+// the kernel writes the sigmoid's argument instead: the raw logit that the
+// temperatures are fitted on.
 #include "dsp_device.h"
 #include "dsp_launch.h"
 
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void confidence_kernel(
     acc = wave_sum(acc);
     if (lane == 0) {
         const double y = acc + (offset ? (double)offset[n] : 0.0);
-        c[row] = (float)(1.0 / (1.0 + exp(-y / (double)T[k])));
+        c[row] = T ? (float)(1.0 / (1.0 + exp(-y / (double)T[k]))) : (float)y;
     }
 }
 

@@ -65,6 +65,19 @@ hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t
                              const float* offset, float* c, int R, int gamma, int d, int V, int r,
                              hipStream_t s);
 
+// Sequential temperature scaling: candidates per grid stage, most sample chunks of
+// one objective launch; calibration-error bins.
+constexpr int kStsGrid = 256;
+constexpr int kStsMaxChunks = 1024;
+constexpr int kEceMaxBins = 64;
+constexpr int64_t kEceMaxPredictions = (int64_t)1 << 23;   // exact 2^-40 bin sums fit 64 bits
+size_t sts_workspace_bytes(int N);
+size_t ece_workspace_bytes();
+hipError_t launch_sts_fit(const float* z, const int32_t* acc, int N, int gamma, double t_lo,
+                          double t_hi, float* T, double* nll, void* ws, hipStream_t s);
+hipError_t launch_ece(const float* z, const int32_t* nacc, const float* T, int N, int gamma, int M,
+                      double* ece, void* ws, hipStream_t s);
+
 hipError_t launch_schedule(const float* c, const float* sps, int B_max, uint64_t S0, int mode,
                            int32_t* len, float* a, int32_t* B, int R, int gamma, hipStream_t s);
 

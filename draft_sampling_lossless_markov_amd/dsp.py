@@ -22,13 +22,14 @@ LIB_PATH = os.path.join(_PKG, "libdsp.so")
 _STATUS_NAMES = ("DSP_OK", "DSP_ERR_INVALID_ARG", "DSP_ERR_UNSUPPORTED", "DSP_ERR_WORKSPACE",
                  "DSP_ERR_HIP", "DSP_ERR_TIMEOUT")
 DSP_F32, DSP_BF16 = 0, 1
-DSP_WS_DRAFT, DSP_WS_VERIFY, DSP_WS_TV = 0, 1, 2
+DSP_WS_DRAFT, DSP_WS_VERIFY, DSP_WS_TV, DSP_WS_STS, DSP_WS_ECE = 0, 1, 2, 3, 4
 DSP_PATH_AUTO, DSP_PATH_STREAMING, DSP_PATH_PERSISTENT = 0, 1, 2
 DSP_FLAG_TEST_GIVE_UP = 0x100
 
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
             "dsp_workspace_status", "dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence",
-            "dsp_schedule", "dsp_schedule_async", "dsp_verify", "dsp_tv_accept")
+            "dsp_schedule", "dsp_schedule_async", "dsp_verify", "dsp_tv_accept",
+            "dsp_confidence_logit", "dsp_sts_fit", "dsp_ece")
 
 _lib = None
 
@@ -74,8 +75,12 @@ def lib():
                              I, I, U32, F, U64, U32, P, SZ, P]
     L.dsp_schedule_async.argtypes = [P, P, P, I, D, P, P, P, P, I, I, P]
     L.dsp_tv_accept.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, I, I, I, I, F, P, SZ, P]
+    L.dsp_confidence_logit.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    L.dsp_sts_fit.argtypes = [P, P, I, I, F, F, P, P, P, SZ, P]
+    L.dsp_ece.argtypes = [P, P, P, I, I, I, P, P, SZ, P]
     for f in ("dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence", "dsp_schedule",
-              "dsp_schedule_async", "dsp_verify", "dsp_tv_accept"):
+              "dsp_schedule_async", "dsp_verify", "dsp_tv_accept", "dsp_confidence_logit",
+              "dsp_sts_fit", "dsp_ece"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -152,6 +157,27 @@ def dsp_confidence(h, E, anchor, tok, w, T, offset, c, stream=None):
     V, r = E.shape
     _check(lib().dsp_confidence(_ptr(h), _ptr(E), _ptr(anchor), _ptr(tok), _ptr(w), _ptr(T),
                                 _ptr(offset), _ptr(c), R, gamma, d, V, r, _stream(stream)))
+
+
+def dsp_confidence_logit(h, E, anchor, tok, w, offset, y, stream=None):
+    R, gamma, d = h.shape
+    V, r = E.shape
+    _check(lib().dsp_confidence_logit(_ptr(h), _ptr(E), _ptr(anchor), _ptr(tok), _ptr(w),
+                                      _ptr(offset), _ptr(y), R, gamma, d, V, r, _stream(stream)))
+
+
+def dsp_sts_fit(z, n_acc, t_lo, t_hi, T, nll, ws, stream=None):
+    """z [N, gamma] f32, n_acc [N] int32 -> T [gamma] f32, nll [gamma] f64 (or None)."""
+    N, gamma = z.shape
+    _check(lib().dsp_sts_fit(_ptr(z), _ptr(n_acc), N, gamma, float(t_lo), float(t_hi), _ptr(T),
+                             _ptr(nll), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsp_ece(z, n_acc, T, n_bins, ece, ws, stream=None):
+    """Calibration error of the cumulative survival into ece [1] f64 (T None: all 1)."""
+    N, gamma = z.shape
+    _check(lib().dsp_ece(_ptr(z), _ptr(n_acc), _ptr(T), N, gamma, int(n_bins), _ptr(ece),
+                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dsp_schedule(c, sps, B_max, tau0, mode, length, a, B, stream=None):

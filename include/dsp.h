@@ -80,7 +80,13 @@ typedef enum {
 
 typedef enum { DSP_F32 = 0, DSP_BF16 = 1 } dsp_dtype;
 
-typedef enum { DSP_WS_DRAFT = 0, DSP_WS_VERIFY = 1, DSP_WS_TV = 2 } dsp_ws_kind;
+typedef enum {
+    DSP_WS_DRAFT = 0,
+    DSP_WS_VERIFY = 1,
+    DSP_WS_TV = 2,
+    DSP_WS_STS = 3,
+    DSP_WS_ECE = 4
+} dsp_ws_kind;
 
 /* Static text for a status code. */
 const char* dsp_status_string(dsp_status s);
@@ -91,8 +97,10 @@ const char* dsp_last_error(void);
 /* Library ABI version (major * 100 + minor). */
 int dsp_version(void);
 
-/* Bytes of workspace dsp_draft_step (DSP_WS_DRAFT), dsp_verify (DSP_WS_VERIFY) or
- * dsp_tv_accept (DSP_WS_TV) needs for these sizes; 0 for invalid sizes. */
+/* Bytes of workspace dsp_draft_step (DSP_WS_DRAFT), dsp_verify (DSP_WS_VERIFY),
+ * dsp_tv_accept (DSP_WS_TV), dsp_sts_fit (DSP_WS_STS: R = the number of
+ * held-out samples N; V and r are ignored) or dsp_ece (DSP_WS_ECE: a fixed size,
+ * every size argument ignored) needs; 0 for invalid sizes. */
 size_t dsp_workspace_size(dsp_ws_kind which, int R, int gamma, int V, int r);
 
 /*
@@ -214,6 +222,58 @@ dsp_status dsp_confidence(const uint16_t* h, const uint16_t* E, const int32_t* a
                           const int32_t* tok, const float* w, const float* T,
                           const float* offset, float* c, int R, int gamma, int d, int V, int r,
                           void* stream);
+
+/*
+ * dsp_confidence_logit -- the confidence head's sigmoid argument before the
+ * temperatures: y[n,k] = fp32(sum_{i<d} w[i] h[n,k,i] + sum_{i<r} w[d+i] E[prev,i]
+ * + offset[n]) with the fp64 sum of dsp_confidence (same arguments without T).
+ * These raw logits are what sequential temperature scaling is fitted on.
+ */
+dsp_status dsp_confidence_logit(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
+                                const int32_t* tok, const float* w, const float* offset, float* y,
+                                int R, int gamma, int d, int V, int r, void* stream);
+
+/*
+ * dsp_sts_fit -- sequential temperature scaling fitted on held-out data.
+ *
+ * Page "DeepSeek联合北大最新文章DSpark", section 2.1: the raw confidences are
+ * overconfident and overestimate the cumulative survival; temperatures are
+ * calibrated position by position from left to right on a held-out set.  The
+ * page gives no objective.  This library's reading: sample n carries raw logits
+ * z[n,k] (dsp_confidence_logit) and n_acc[n], its number of accepted draft tokens
+ * in a round that verified every position (0..gamma); s[n,k] = (n_acc[n] > k).
+ * With beta_j = 1 / T_j and a[n,k] = prod_{j<=k} sigma(beta_j z[n,j]), T_k (the
+ * earlier ones fixed) minimises the binary cross-entropy
+ *     F_k(beta) = -sum_n [ s ln a[n,k] + (1 - s) ln(1 - a[n,k]) ]
+ * over two grids of 256 betas, each point fma(g, step, lo) in fp64: first
+ * [1/t_hi, 1/t_lo], then the span of the first grid's best point and its two
+ * neighbours.  The lowest index wins a tie; a NaN objective counts as +inf.
+ * fp64 throughout.
+ *
+ * z [N, gamma] f32; n_acc [N] int32; T [gamma] f32 out (= fp32(1/beta_k));
+ * nll [gamma] f64 out (F_k at the fitted beta) or NULL; 0 < t_lo < t_hi finite;
+ * ws >= dsp_workspace_size(DSP_WS_STS, N, gamma, 1, 1) bytes, 16-byte aligned
+ * (DSP_ERR_WORKSPACE otherwise).  Asynchronous on stream; device memory only.
+ */
+dsp_status dsp_sts_fit(const float* z, const int32_t* n_acc, int N, int gamma, float t_lo,
+                       float t_hi, float* T, double* nll, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsp_ece -- expected calibration error of the cumulative survival (the page
+ * above reports ECE before and after the temperatures).  Every pair (n, k) is
+ * a prediction a[n,k] = prod_{j<=k} sigma(z[n,j] / T_j) (T NULL: T_j = 1) of
+ * s[n,k] = (n_acc[n] > k), binned by min(floor(a n_bins), n_bins - 1):
+ *     ece = sum_bins |sum_bin (s - a)| / (N gamma)
+ * Bin sums are exact integers (a in units of 2^-40), so the result does not
+ * depend on the order of the GPU's additions and lies within 2^-40 of the
+ * real-number value of these predictions.
+ *
+ * z [N, gamma] f32; n_acc [N] int32; T [gamma] f32 or NULL; 1 <= n_bins <= 64;
+ * N gamma <= 2^23 (DSP_ERR_UNSUPPORTED beyond); ece [1] f64 out (device);
+ * ws >= dsp_workspace_size(DSP_WS_ECE, 0, 0, 0, 0) bytes, 16-byte aligned.
+ */
+dsp_status dsp_ece(const float* z, const int32_t* n_acc, const float* T, int N, int gamma,
+                   int n_bins, double* ece, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dsp_schedule -- hardware-aware prefix scheduler.

@@ -42,7 +42,7 @@ def test_status_strings_and_version(L):
     assert L.dsp_status_string(0) == b"DSP_OK"
     assert L.dsp_status_string(3) == b"DSP_ERR_WORKSPACE"
     assert L.dsp_status_string(5) == b"DSP_ERR_TIMEOUT"
-    assert L.dsp_version() == 400
+    assert L.dsp_version() == 410
 
 
 def test_workspace_sizes(L):
@@ -219,3 +219,44 @@ def test_schedule_async_validation(L):
     assert f(P(FAKE), P(FAKE), P(FAKE), 3, 0.0, *ok, P(FAKE), 4, 4, None) == 1
     assert f(P(FAKE), P(FAKE), P(FAKE), 20, 16384.0, *ok, P(FAKE), 4, 4, None) == 1
     assert f(P(FAKE), P(FAKE), P(FAKE), 10 ** 6, 0.0, *ok, P(FAKE), 4097, 4, None) == 2
+
+
+def test_sts_and_ece_validation(L):
+    from draft_sampling_lossless_markov_amd import dsp
+    P = C.c_void_p
+    ws_sts = dsp.dsp_workspace_size(dsp.DSP_WS_STS, 1000, 4, 1, 1)
+    # ln a and 1 - a per sample, one 256-candidate row per chunk of samples, the
+    # control block: each rounded to 256 bytes
+    assert ws_sts == 2 * 8192 + 4 * 256 * 8 + 256
+    assert dsp.dsp_workspace_size(dsp.DSP_WS_STS, 0, 4, 1, 1) == 0
+    ws_ece = dsp.dsp_workspace_size(dsp.DSP_WS_ECE, 0, 0, 0, 0)
+    assert ws_ece == 1024
+
+    def fit(z=FAKE, acc=FAKE, N=1000, gamma=4, t_lo=0.0625, t_hi=16.0, T=FAKE, ws=FAKE,
+            ws_bytes=ws_sts):
+        return L.dsp_sts_fit(P(z), P(acc), N, gamma, t_lo, t_hi, P(T), P(FAKE), P(ws), ws_bytes,
+                             None)
+
+    assert fit(z=0) == 1
+    assert fit(T=0) == 1
+    assert fit(N=0) == 1
+    assert fit(t_lo=0.0) == 1 and b"t_lo" in L.dsp_last_error()
+    assert fit(t_lo=2.0, t_hi=1.0) == 1
+    assert fit(t_hi=float("inf")) == 1
+    assert fit(ws_bytes=ws_sts - 1) == 3
+    assert fit(ws=FAKE + 8) == 3
+
+    def ece(z=FAKE, N=1000, gamma=4, bins=15, out=FAKE, ws_bytes=ws_ece):
+        return L.dsp_ece(P(z), P(FAKE), P(FAKE), N, gamma, bins, P(out), P(FAKE), ws_bytes, None)
+
+    assert ece(z=0) == 1
+    assert ece(out=0) == 1
+    assert ece(bins=0) == 1
+    assert ece(bins=65) == 2
+    assert ece(N=1 << 21, gamma=5) == 2
+    assert ece(ws_bytes=16) == 3
+
+    f = L.dsp_confidence_logit
+    assert f(P(FAKE), P(0), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), 4, 4, 16, 32, 8, None) == 1
+    assert f(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE + 8), None, P(FAKE), 4, 4, 16, 32, 8,
+             None) == 1

@@ -34,18 +34,19 @@ def lib():
         _lib.orc_softmax.argtypes = [C.c_int, P, C.c_double, P, P]
         _lib.orc_inverse_cdf.argtypes = [C.c_int, P, C.c_double, C.c_double, P]
         _lib.orc_draft.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P, P, P,
-                                   C.c_double, C.c_uint64, C.c_uint32, P, P, P, P, P]
+                                   C.c_double, C.c_uint64, C.c_uint32, P, P, P, P, P, P, P, P]
         _lib.orc_confidence.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P,
                                         P, P, P, P, P]
         _lib.orc_schedule.argtypes = [C.c_int, C.c_int, P, P, C.c_int, C.c_double, C.c_int,
                                       P, P, P, P]
         _lib.orc_verify.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P,
                                     P, P, P, P, P, C.c_double, C.c_uint64, C.c_uint32,
-                                    P, P, P, P, P, P, P]
+                                    P, P, P, P, P, P, P, P]
         _lib.orc_schedule_async.argtypes = [C.c_int, C.c_int, P, P, P, C.c_int, C.c_double, P, P,
                                             P, P]
         _lib.orc_tv_accept.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P, P, P,
-                                       P, C.c_double, P]
+                                       P, C.c_double, P, P]
+        _lib.orc_rnn_state.argtypes = [C.c_int, C.c_int, P, P, C.c_int, P, P, P]
         _lib.orc_confidence_logit.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P,
                                               P, P, P, P, P]
         _lib.orc_sts_fit.argtypes = [C.c_int, C.c_int, P, P, C.c_double, C.c_double, C.c_int, P,
@@ -116,10 +117,13 @@ def inverse_cdf(w, u, window=1e-6):
     return x, bool(near.value)
 
 
-def draft(base, E, W2, anchor, req_id, temperature, seed, rnd, force=None):
+def draft(base, E, W2, anchor, req_id, temperature, seed, rnd, force=None, A=None):
     """base [n, gamma, V] (float32 or bf16 bits).  Returns tok, q, stats, flag.
     force [n, gamma] int32 (optional): tokens >= 0 taken instead of the oracle's
-    own draw at those positions (teacher forcing at a flagged decision)."""
+    own draw at those positions (teacher forcing at a flagged decision).
+    A [r, r] bf16 bits (optional): the recurrent head with that matrix; the
+    result then also holds the states S [n, gamma, r] (bf16 bits) and sflag
+    [n, gamma] (a state element near a bf16 rounding midpoint)."""
     base, dt = _logits(base)
     n, gamma, V = base.shape
     E = _c(E, np.uint16)
@@ -132,10 +136,31 @@ def draft(base, E, W2, anchor, req_id, temperature, seed, rnd, force=None):
     stats = np.zeros((n, gamma, 2), np.float64)
     flag = np.zeros((n, gamma), np.int8)
     force = None if force is None else _c(force, np.int32)
+    S = sflag = None
+    if A is not None:
+        A = _c(A, np.uint16)
+        assert A.shape == (r, r)
+        S = np.zeros((n, gamma, r), np.uint16)
+        sflag = np.zeros((n, gamma), np.int8)
     _check(lib().orc_draft(n, gamma, V, r, _p(base), dt, _p(E), _p(W2), _p(anchor), _p(req_id),
                            float(temperature), int(seed), int(rnd), _p(tok), _p(q), _p(stats),
-                           _p(flag), _p(force)), "draft")
+                           _p(flag), _p(force), _p(A), _p(S), _p(sflag)), "draft")
+    if A is not None:
+        return tok, q, stats, flag, S, sflag
     return tok, q, stats, flag
+
+
+def rnn_state(A, E, prev, s_prev=None):
+    """One step of the recurrent head: bf16(tanh(A s_prev + E[prev])); (state, flag)."""
+    A = _c(A, np.uint16)
+    E = _c(E, np.uint16)
+    V, r = E.shape
+    out = np.zeros(r, np.uint16)
+    fl = np.zeros(1, np.int8)
+    _check(lib().orc_rnn_state(V, r, _p(A), _p(E), int(prev),
+                               _p(None if s_prev is None else _c(s_prev, np.uint16)), _p(out),
+                               _p(fl)), "rnn_state")
+    return out, bool(fl[0])
 
 
 def confidence(h, E, anchor, tok, w, T, offset=None):
@@ -236,9 +261,11 @@ def schedule_async(c32, c_hist32, sps, B_max, tau0):
 
 
 def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, seed, rnd,
-           force_acc=None):
+           force_acc=None, S=None):
     """force_acc [n, gamma] int8 (optional): 0/1 adopted as the accept decision at
-    those positions, -1 elsewhere (teacher forcing at a flagged accept test)."""
+    those positions, -1 elsewhere (teacher forcing at a flagged accept test).
+    S [n, gamma, r] bf16 bits (optional): the recurrent head's states, whose row
+    gives the draft law at a rejection instead of E[prev]."""
     target, dt = _logits(target)
     base, dt2 = _logits(base)
     assert dt == dt2
@@ -262,11 +289,12 @@ def verify(target, base, E, W2, anchor, tok, q, length, req_id, temperature, see
     _check(lib().orc_verify(n, gamma, V, r, _p(target), _p(base), dt, _p(E), _p(W2),
                             _p(anchor), _p(tok), _p(q), _p(length), _p(req_id),
                             float(temperature), int(seed), int(rnd), _p(accept), _p(n_acc),
-                            _p(y), _p(p), _p(fa), _p(fy), _p(force_acc)), "verify")
+                            _p(y), _p(p), _p(fa), _p(fy), _p(force_acc),
+                            _p(None if S is None else _c(S, np.uint16))), "verify")
     return dict(accept=accept, n_accept=n_acc, y=y, p=p, flag_acc=fa, flag_y=fy)
 
 
-def tv_accept(target, base, E, W2, anchor, tok, temperature):
+def tv_accept(target, base, E, W2, anchor, tok, temperature, S=None):
     """alpha [n, gamma]: the exact acceptance probability sum_v min(q_k, p_k) of
     every draft position (target [n, gamma+1, V], base [n, gamma, V])."""
     target, dt = _logits(target)
@@ -281,7 +309,8 @@ def tv_accept(target, base, E, W2, anchor, tok, temperature):
     tok = _c(tok, np.int32)
     alpha = np.zeros((n, gamma), np.float64)
     _check(lib().orc_tv_accept(n, gamma, V, r, _p(target), _p(base), dt, _p(E), _p(W2),
-                               _p(anchor), _p(tok), float(temperature), _p(alpha)), "tv_accept")
+                               _p(anchor), _p(tok), float(temperature), _p(alpha),
+                               _p(None if S is None else _c(S, np.uint16))), "tv_accept")
     return alpha
 
 

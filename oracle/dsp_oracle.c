@@ -142,6 +142,79 @@ int orc_markov_logits(int V, int r, const void* base_row, int dtype,
     return 0;
 }
 
+/* The same logits from an explicit bias row (r bf16 values; NULL: no bias):
+ * the Markov head passes E[prev], the recurrent head its state row. */
+static void head_logits(int V, int r, const void* base_row, int dtype, const uint16_t* row,
+                        const uint16_t* W2, float* logit, double* absdot)
+{
+    for (int v = 0; v < V; ++v) {
+        double s = 0.0, sa = 0.0;
+        if (row) {
+            for (int i = 0; i < r; ++i) {
+                const double t = (double)bf16_to_float(row[i]) *
+                                 (double)bf16_to_float(W2[(size_t)v * r + i]);
+                s += t;
+                sa += fabs(t);
+            }
+        }
+        const float bias = (float)s;
+        logit[v] = logit_at(base_row, dtype, (size_t)v) + bias;
+        if (absdot) absdot[v] = sa;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Recurrent sequential head [P4-SEQ] (the pages name an RNN head that keeps */
+/* a recurrent state to capture longer dependencies, without its form).      */
+/* This library's reading, an Elman recurrence on the Markov head's rank-r   */
+/* space:                                                                    */
+/*   s_{-1} = 0;  u_k = A s_{k-1} + E[x_{k-1}]  (fp64; no E term when x is   */
+/*   outside [0, V));  s_k = bf16(tanh(u_k))  (round to nearest even)        */
+/* and the bias of position k is s_k . W2 like the Markov head's E[x_{k-1}]. */
+/* A is [r, r] bf16, element (i, j) at A[i r + j] (row i gives output i).    */
+/* With A = 0 the head is the Markov head on bf16(tanh(E)).                  */
+/* *flag = 1 when some tanh(u_i) lies within 1e-12 (relative) of a bf16      */
+/* rounding midpoint (where a differently rounded tanh may round the other   */
+/* way).                                                                     */
+/* ------------------------------------------------------------------------- */
+
+static uint16_t bf16_rne(double x, int8_t* near)
+{
+    const float f = (float)x;   /* exact for the tanh values tested: see flag */
+    uint32_t u;
+    memcpy(&u, &f, sizeof(u));
+    /* candidates: truncation and the next bf16 value up in magnitude */
+    const uint32_t lo = u & 0xFFFF0000u, hi = lo + 0x10000u;
+    float flo, fhi;
+    memcpy(&flo, &lo, sizeof(flo));
+    memcpy(&fhi, &hi, sizeof(fhi));
+    const double dlo = fabs(x - (double)flo), dhi = fabs((double)fhi - x);
+    uint32_t pick;
+    if (dlo < dhi) pick = lo;
+    else if (dhi < dlo) pick = hi;
+    else pick = ((lo >> 16) & 1u) ? hi : lo;   /* tie: even mantissa */
+    const double mid = 0.5 * ((double)flo + (double)fhi);
+    if (near && fabs(x - mid) <= 1e-12 * fabs(x)) *near = 1;
+    return (uint16_t)(pick >> 16);
+}
+
+int orc_rnn_state(int V, int r, const uint16_t* A, const uint16_t* E, int prev,
+                  const uint16_t* s_prev, uint16_t* s_out, int8_t* flag)
+{
+    if (V <= 0 || r <= 0) return 1;
+    int8_t fl = 0;
+    for (int i = 0; i < r; ++i) {
+        double u = 0.0;
+        if (s_prev)
+            for (int j = 0; j < r; ++j)
+                u += (double)bf16_to_float(A[(size_t)i * r + j]) * (double)bf16_to_float(s_prev[j]);
+        if (prev >= 0 && prev < V) u += (double)bf16_to_float(E[(size_t)prev * r + i]);
+        s_out[i] = bf16_rne(tanh(u), &fl);
+    }
+    if (flag) *flag = fl;
+    return 0;
+}
+
 /* Tempered softmax in fp64: M = max logit, prob_v = exp((logit_v - M) / T) / Z
  * with Z = sum_v exp((logit_v - M) / T).  stats = (M, Z). */
 int orc_softmax(int V, const float* logit, double temperature, double* prob, double* stats)
@@ -220,12 +293,15 @@ static int argmax_f32(int V, const float* x)
 /* positions of the chain stay comparable; flag is computed as usual.        */
 /* ------------------------------------------------------------------------- */
 
+/* A (optional): the recurrent head with recurrent matrix A; its states go to */
+/* S [n, gamma, r] bf16 and sflag [n, gamma] marks a state with a            */
+/* near-midpoint element (orc_rnn_state).                                    */
 int orc_draft(int n, int gamma, int V, int r,
               const void* base, int dtype, const uint16_t* E, const uint16_t* W2,
               const int32_t* anchor, const int32_t* req_id,
               double temperature, uint64_t seed, uint32_t round,
               int32_t* tok, double* q, double* stats, int8_t* flag,
-              const int32_t* force)
+              const int32_t* force, const uint16_t* A, uint16_t* S, int8_t* sflag)
 {
     if (n < 0 || gamma <= 0 || V <= 0 || r <= 0 || temperature < 0.0) return 1;
     float* logit = (float*)malloc(sizeof(float) * (size_t)V);
@@ -240,7 +316,13 @@ int orc_draft(int n, int gamma, int V, int r,
             const size_t ik = (size_t)i * gamma + k;
             const void* brow = (dtype == DT_F32) ? (const void*)((const float*)base + row)
                                                  : (const void*)((const uint16_t*)base + row);
-            orc_markov_logits(V, r, brow, dtype, E, W2, prev, logit, absdot);
+            if (A) {
+                uint16_t* srow = S + ik * (size_t)r;
+                orc_rnn_state(V, r, A, E, prev, k > 0 ? srow - r : NULL, srow, &sflag[ik]);
+                head_logits(V, r, brow, dtype, srow, W2, logit, absdot);
+            } else {
+                orc_markov_logits(V, r, brow, dtype, E, W2, prev, logit, absdot);
+            }
             int x;
             int8_t fl = 0;
             if (greedy) {
@@ -426,7 +508,7 @@ int orc_verify(int n_req, int gamma, int V, int r,
                const int32_t* len, const int32_t* req_id,
                double temperature, uint64_t seed, uint32_t round,
                int8_t* accept, int32_t* n_accept, int32_t* y, double* p_out,
-               int8_t* flag_acc, int8_t* flag_y, const int8_t* force_acc)
+               int8_t* flag_acc, int8_t* flag_y, const int8_t* force_acc, const uint16_t* S)
 {
     if (n_req < 0 || gamma <= 0 || V <= 0 || r <= 0 || temperature < 0.0) return 1;
     float* tl = (float*)malloc(sizeof(float) * (size_t)V);
@@ -479,7 +561,11 @@ int orc_verify(int n_req, int gamma, int V, int r,
                 const size_t drow = ((size_t)i * gamma + n) * (size_t)V;
                 const void* brow = (dtype == DT_F32) ? (const void*)((const float*)base + drow)
                                                      : (const void*)((const uint16_t*)base + drow);
-                orc_markov_logits(V, r, brow, dtype, E, W2, prev, dl, NULL);
+                /* the draft law of position n: Markov row E[prev], or the
+                   recurrent head's state row S[i, n] */
+                if (S) head_logits(V, r, brow, dtype, S + ((size_t)i * gamma + n) * (size_t)r, W2,
+                                   dl, NULL);
+                else orc_markov_logits(V, r, brow, dtype, E, W2, prev, dl, NULL);
                 orc_softmax(V, dl, temperature, pd, NULL);
                 double mass = 0.0;
                 for (int v = 0; v < V; ++v) {
@@ -510,7 +596,7 @@ int orc_verify(int n_req, int gamma, int V, int r,
 
 int orc_tv_accept(int n, int gamma, int V, int r, const void* target, const void* base, int dtype,
                   const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
-                  const int32_t* tok, double temperature, double* alpha)
+                  const int32_t* tok, double temperature, double* alpha, const uint16_t* S)
 {
     if (n < 0 || gamma <= 0 || V <= 0 || r <= 0 || !(temperature > 0.0)) return 1;
     float* tl = (float*)malloc(sizeof(float) * (size_t)V);
@@ -527,7 +613,9 @@ int orc_tv_accept(int n, int gamma, int V, int r, const void* target, const void
             const size_t drow = ((size_t)i * gamma + k) * (size_t)V;
             const void* brow = (dtype == DT_F32) ? (const void*)((const float*)base + drow)
                                                  : (const void*)((const uint16_t*)base + drow);
-            orc_markov_logits(V, r, brow, dtype, E, W2, prev, dl, NULL);
+            if (S) head_logits(V, r, brow, dtype, S + ((size_t)i * gamma + k) * (size_t)r, W2, dl,
+                               NULL);
+            else orc_markov_logits(V, r, brow, dtype, E, W2, prev, dl, NULL);
             orc_softmax(V, dl, temperature, pd, NULL);
             double a = 0.0;
             for (int v = 0; v < V; ++v) a += (pd[v] < pt[v]) ? pd[v] : pt[v];

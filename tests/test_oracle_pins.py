@@ -1092,3 +1092,111 @@ def test_confidence_logit_is_the_sigmoid_argument():
     c, _ = oracle.confidence(h, E, anchor, tok, w, T, off)
     from scipy.special import expit
     np.testing.assert_allclose(c, expit(y / T[None, :].astype(np.float64)), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Recurrent sequential head (page "DeepSeek联合北大最新文章DSpark", 第二阶段轻量
+# 顺序头: an RNN head that keeps a recurrent state; its form is this library's
+# reading, an Elman recurrence s_k = bf16(tanh(A s_{k-1} + E[x_{k-1}]))).
+# ---------------------------------------------------------------------------
+def _rnn_setup(V, r, seed, a_scale=0.3):
+    rng = np.random.default_rng(seed)
+    E = bf16(rng.normal(0, 0.8, (V, r)))
+    W2 = bf16(rng.normal(0, 0.5, (V, r)))
+    A = bf16(rng.normal(0, a_scale / math.sqrt(r), (r, r)))
+    return E, W2, A
+
+
+def test_rnn_state_is_an_elman_cell():
+    # torch's RNN cell with identity input weights, no biases and tanh is the
+    # recurrence; the oracle rounds every state to bf16 (nearest even) and
+    # feeds the rounded state forward, so each step is compared from the
+    # oracle's previous state
+    import oracle
+    V, r = 40, 24
+    E, W2, A = _rnn_setup(V, r, 1)
+    cell = torch.nn.RNNCell(r, r, bias=False, nonlinearity="tanh").double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.eye(r, dtype=torch.float64))
+        cell.weight_hh.copy_(torch.as_tensor(bf16_val(A), dtype=torch.float64))
+    s = None
+    exact = total = 0
+    for x in [3, 17, 0, 39, 17, 5, -1, 8]:
+        out, fl = oracle.rnn_state(A, E, x, s)
+        assert not fl
+        h = torch.zeros(1, r, dtype=torch.float64) if s is None else \
+            torch.as_tensor(bf16_val(s), dtype=torch.float64)[None]
+        e = torch.zeros(1, r, dtype=torch.float64) if x < 0 else \
+            torch.as_tensor(bf16_val(E[x]), dtype=torch.float64)[None]
+        with torch.no_grad():
+            ref = cell(e, h)[0].numpy()
+        got = bf16_val(out).astype(np.float64)
+        ulp = np.spacing(np.abs(ref).astype(np.float32)) * 65536.0   # one bf16 ulp
+        assert np.all(np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-9))
+        exact += int(np.sum(got == torch.as_tensor(ref).to(torch.bfloat16).double().numpy()))
+        total += r
+        s = out
+    assert exact >= total - 2
+
+
+def test_rnn_with_zero_recurrence_is_the_markov_head_on_its_state_table():
+    import oracle
+    V, r, gamma, n = 64, 16, 5, 6
+    E, W2, _ = _rnn_setup(V, r, 2)
+    A0 = np.zeros((r, r), np.uint16)
+    Et = np.stack([oracle.rnn_state(A0, E, v)[0] for v in range(V)])
+    rng = np.random.default_rng(3)
+    base = rng.normal(0, 2, (n, gamma, V)).astype(np.float32)
+    anchor = rng.integers(0, V, n).astype(np.int32)
+    req = np.arange(n, dtype=np.int32)
+    for temp in (1.0, 0.0):
+        t1, q1, s1, f1, S, sf = oracle.draft(base, E, W2, anchor, req, temp, 7, 1, A=A0)
+        t2, q2, s2, f2 = oracle.draft(base, Et, W2, anchor, req, temp, 7, 1)
+        assert np.array_equal(t1, t2) and np.array_equal(q1, q2) and np.array_equal(s1, s2)
+        prev = np.concatenate([anchor[:, None], t1[:, :-1]], axis=1)
+        assert np.array_equal(S, Et[prev])
+
+
+def test_rnn_state_remembers_beyond_one_token():
+    # with the previous token forced equal, the state of position 1 still sees
+    # the anchor through A; without recurrence it does not
+    import oracle
+    V, r, gamma = 32, 16, 3
+    E, W2, A = _rnn_setup(V, r, 4, a_scale=1.0)
+    base = np.zeros((2, gamma, V), np.float32)
+    anchor = np.array([1, 2], np.int32)
+    req = np.array([0, 0], np.int32)
+    force = np.full((2, gamma), -1, np.int32)
+    force[:, 0] = 5
+    _, _, _, _, S, _ = oracle.draft(base, E, W2, anchor, req, 1.0, 0, 0, force=force, A=A)
+    assert not np.array_equal(S[0, 1], S[1, 1])
+    _, _, _, _, S0, _ = oracle.draft(base, E, W2, anchor, req, 1.0, 0, 0, force=force,
+                                     A=np.zeros_like(A))
+    assert np.array_equal(S0[0, 1], S0[1, 1])
+
+
+def test_rnn_draft_verification_is_lossless():
+    # the first emitted token (accepted draft token or the correction / bonus
+    # draw) follows the target law p_0 whatever the draft law: chi-square over a
+    # 6-token vocabulary with a recurrent draft
+    import oracle
+    V, r, gamma, n = 6, 8, 2, 60000
+    E, W2, A = _rnn_setup(V, r, 5, a_scale=1.0)
+    rng = np.random.default_rng(6)
+    base1 = rng.normal(0, 1.5, (gamma, V)).astype(np.float32)
+    tgt1 = rng.normal(0, 1.5, (gamma + 1, V)).astype(np.float32)
+    base = np.broadcast_to(base1, (n, gamma, V)).copy()
+    target = np.broadcast_to(tgt1, (n, gamma + 1, V)).copy()
+    anchor = np.full(n, 2, np.int32)
+    req = np.arange(n, dtype=np.int32)
+    tok, q, st, fl, S, sf = oracle.draft(base, E, W2, anchor, req, 1.0, 11, 3, A=A)
+    v = oracle.verify(target, base, E, W2, anchor, tok, q, np.full(n, gamma, np.int32), req, 1.0,
+                      11, 3, S=S)
+    first = np.where(v["n_accept"] > 0, tok[:, 0], v["y"])
+    p0 = sp_softmax(tgt1[0].astype(np.float64))
+    counts = np.bincount(first, minlength=V)
+    stat, pval = sst.chisquare(counts, n * p0)
+    assert pval > 1e-4, (counts, n * p0)
+    # and the draft law itself differs from p_0 (the test is not vacuous)
+    counts_d = np.bincount(tok[:, 0], minlength=V)
+    assert sst.chisquare(counts_d, n * p0)[1] < 1e-6

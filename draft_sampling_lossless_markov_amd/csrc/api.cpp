@@ -112,6 +112,16 @@ dsp_status check_draft(const char* fn, const void* base, dsp_dtype dtype, int64_
 
 }  // namespace
 
+namespace {
+dsp_status verify_impl(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                       int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
+                       const float* q, const double* stats, const int32_t* len, int8_t* accept,
+                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
+                       unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
+                       size_t ws_bytes, void* stream, const uint16_t* S);
+}  // namespace
+
 extern "C" {
 
 const char* dsp_status_string(dsp_status s)
@@ -191,6 +201,37 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                                              seed, round,
                                              ws, static_cast<hipStream_t>(stream)),
                       "dsp_draft_step launch");
+}
+
+dsp_status dsp_draft_step_rnn(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
+                              const uint16_t* E, const uint16_t* W2, const uint16_t* A,
+                              const int32_t* anchor, int32_t* tok, float* q, double* stats,
+                              uint16_t* S, int R, int gamma, int V, int r, int k, int n_steps,
+                              unsigned flags, float temperature, uint64_t seed, uint32_t round,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    dsp_status st = check_draft("dsp_draft_step_rnn", base, dtype, base_rs, base_ps, E, W2, anchor,
+                                tok, q, stats, R, gamma, V, r, k, n_steps, flags, temperature);
+    if (st != DSP_OK) return st;
+    if (!A || !S) return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step_rnn: null A or S");
+    if (!aligned16(A) || !aligned16(S))
+        return fail(DSP_ERR_INVALID_ARG, "dsp_draft_step_rnn: A and S must be 16-byte aligned");
+    if ((int64_t)R * gamma * r > dsp::kRnnMaxStateElems)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_draft_step_rnn: R * gamma * r exceeds 2^31 - 1");
+    if (path_of(flags) == DSP_PATH_PERSISTENT)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_draft_step_rnn: the recurrent head runs the streaming path only");
+    const size_t need = dsp::draft_workspace_bytes(R, V);
+    if (!ws || ws_bytes < need)
+        return fail(DSP_ERR_WORKSPACE, "dsp_draft_step_rnn: workspace of %zu bytes, %zu needed",
+                    ws_bytes, need);
+    if (!aligned16(ws))
+        return fail(DSP_ERR_WORKSPACE, "dsp_draft_step_rnn: the workspace must be 16-byte aligned");
+    return hip_status(dsp::launch_draft_step(base, dsp::RowStrides{base_rs, base_ps},
+                                             dtype == DSP_BF16, E, W2, anchor, tok, q, stats, R, gamma,
+                                             V, r, k, n_steps, path_of(flags), give_up_of(flags),
+                                             temperature, seed, round, ws,
+                                             static_cast<hipStream_t>(stream), A, S),
+                      "dsp_draft_step_rnn launch");
 }
 
 dsp_status dsp_draft_step_noalloc(const void* base, dsp_dtype dtype, int64_t base_rs,
@@ -329,6 +370,42 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
                       unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
                       size_t ws_bytes, void* stream)
 {
+    return verify_impl(target, target_rs, target_ps, base, base_rs, base_ps, dtype, E, W2, anchor, tok,
+                       q, stats, len, accept, n_accept, y, p, R, gamma, V, r, flags, temperature, seed,
+                       round, ws, ws_bytes, stream, nullptr);
+}
+
+dsp_status dsp_verify_rnn(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                          int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                          const uint16_t* W2, const uint16_t* S, const int32_t* anchor,
+                          const int32_t* tok, const float* q, const double* stats, const int32_t* len,
+                          int8_t* accept, int32_t* n_accept, int32_t* y, float* p, int R, int gamma,
+                          int V, int r, unsigned flags, float temperature, uint64_t seed,
+                          uint32_t round, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!S) return fail(DSP_ERR_INVALID_ARG, "dsp_verify_rnn: null S");
+    if (!aligned16(S)) return fail(DSP_ERR_INVALID_ARG, "dsp_verify_rnn: S must be 16-byte aligned");
+    if ((int64_t)R * gamma * r > dsp::kRnnMaxStateElems)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_verify_rnn: R * gamma * r exceeds 2^31 - 1");
+    if (path_of(flags) == DSP_PATH_PERSISTENT)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_verify_rnn: the recurrent head runs the streaming path only");
+    return verify_impl(target, target_rs, target_ps, base, base_rs, base_ps, dtype, E, W2, anchor, tok,
+                       q, stats, len, accept, n_accept, y, p, R, gamma, V, r, flags, temperature, seed,
+                       round, ws, ws_bytes, stream, S);
+}
+
+}  // extern "C"
+
+namespace {
+
+dsp_status verify_impl(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                       int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                       const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
+                       const float* q, const double* stats, const int32_t* len, int8_t* accept,
+                       int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
+                       unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
+                       size_t ws_bytes, void* stream, const uint16_t* S)
+{
     if (!target || !base || !E || !W2 || !anchor || !tok || !q || !stats || !len || !accept ||
         !n_accept || !y || !p)
         return fail(DSP_ERR_INVALID_ARG, "dsp_verify: null pointer argument");
@@ -357,11 +434,21 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
                                          W2, anchor, tok, q,
                                          stats, len, accept, n_accept, y, p, R, gamma, V, r,
                                          temperature, seed, round, ws,
-                                         static_cast<hipStream_t>(stream)),
+                                         static_cast<hipStream_t>(stream), S),
                       "dsp_verify launch");
 }
 
-}  // extern "C"
+}  // namespace
+
+namespace {
+
+dsp_status tv_impl(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                   int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                   const uint16_t* W2, const int32_t* anchor, const int32_t* tok, const double* stats,
+                   double* alpha, int R, int gamma, int V, int r, float temperature, void* ws,
+                   size_t ws_bytes, void* stream, const uint16_t* S);
+
+}  // namespace
 
 extern "C" dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64_t target_ps,
                                     const void* base, int64_t base_rs, int64_t base_ps,
@@ -369,6 +456,34 @@ extern "C" dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64
                                     const int32_t* anchor, const int32_t* tok, const double* stats,
                                     double* alpha, int R, int gamma, int V, int r, float temperature,
                                     void* ws, size_t ws_bytes, void* stream)
+{
+    return tv_impl(target, target_rs, target_ps, base, base_rs, base_ps, dtype, E, W2, anchor, tok,
+                   stats, alpha, R, gamma, V, r, temperature, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" dsp_status dsp_tv_accept_rnn(const void* target, int64_t target_rs, int64_t target_ps,
+                                        const void* base, int64_t base_rs, int64_t base_ps,
+                                        dsp_dtype dtype, const uint16_t* E, const uint16_t* W2,
+                                        const uint16_t* S, const int32_t* anchor, const int32_t* tok,
+                                        const double* stats, double* alpha, int R, int gamma, int V,
+                                        int r, float temperature, void* ws, size_t ws_bytes,
+                                        void* stream)
+{
+    if (!S) return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept_rnn: null S");
+    if (!aligned16(S)) return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept_rnn: S must be 16-byte aligned");
+    if ((int64_t)R * gamma * r > dsp::kRnnMaxStateElems)
+        return fail(DSP_ERR_UNSUPPORTED, "dsp_tv_accept_rnn: R * gamma * r exceeds 2^31 - 1");
+    return tv_impl(target, target_rs, target_ps, base, base_rs, base_ps, dtype, E, W2, anchor, tok,
+                   stats, alpha, R, gamma, V, r, temperature, ws, ws_bytes, stream, S);
+}
+
+namespace {
+
+dsp_status tv_impl(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                   int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                   const uint16_t* W2, const int32_t* anchor, const int32_t* tok, const double* stats,
+                   double* alpha, int R, int gamma, int V, int r, float temperature, void* ws,
+                   size_t ws_bytes, void* stream, const uint16_t* S)
 {
     if (!target || !base || !E || !W2 || !anchor || !tok || !stats || !alpha)
         return fail(DSP_ERR_INVALID_ARG, "dsp_tv_accept: null pointer argument");
@@ -395,9 +510,11 @@ extern "C" dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64
     return hip_status(dsp::launch_tv_accept(target, dsp::RowStrides{target_rs, target_ps}, base,
                                             dsp::RowStrides{base_rs, base_ps}, dtype == DSP_BF16, E, W2,
                                             anchor, tok, stats, alpha, R, gamma, V, r, temperature,
-                                            ws, static_cast<hipStream_t>(stream)),
+                                            ws, static_cast<hipStream_t>(stream), S),
                       "dsp_tv_accept launch");
 }
+
+}  // namespace
 
 extern "C" dsp_status dsp_schedule_async(const float* c, const float* c_hist, const float* sps,
                                          int B_max, double tau0, int32_t* len, float* a, int32_t* B,

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256, 4) void draft_pick_kernel(
     const uint16_t* __restrict__ W2,
     const int32_t* __restrict__ anchor, int32_t* __restrict__ tok, float* __restrict__ q,
     double* __restrict__ stats, int R, int gamma, int V, int r, int k, float inv_temp,
-    uint64_t seed, uint32_t round, int n_vt, const Part* __restrict__ part)
+    uint64_t seed, uint32_t round, int n_vt, const Part* __restrict__ part,
+    const uint16_t* __restrict__ S)
 {
     __shared__ PickScratch sh;
     const int n = blockIdx.x;
@@ -96,9 +97,12 @@ __global__ __launch_bounds__(256, 4) void draft_pick_kernel(
         const int v = tsel * kVocabTile + tid;
         const float xb = (v < V) ? Logit<LT>::at(row, v) : -INFINITY;
         if (tid < kRankMax / 8) {
+            // the bias row: E[x_{k-1}] (Markov head) or the state S[n, k]
+            const uint16_t* er = S ? S + ((int64_t)n * gamma + k) * r
+                                   : (prev >= 0 ? E + (int64_t)prev * r : nullptr);
             const int kk = 8 * tid;
             uint4 ev = make_uint4(0, 0, 0, 0);
-            if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
+            if (er && kk < r) ev = *reinterpret_cast<const uint4*>(er + kk);
             *reinterpret_cast<uint4*>(e_row + kk) = ev;
         }
         const float m_t = pp[tsel].m;   // the tile's reference in the partial
@@ -156,10 +160,10 @@ template <typename LT, bool GREEDY, int PER>
 static void launch_pick(const LT* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
                         const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                         int gamma, int V, int r, int k, float it, uint64_t seed, uint32_t round,
-                        int n_vt, const Part* part, hipStream_t s)
+                        int n_vt, const Part* part, const uint16_t* S, hipStream_t s)
 {
     hipLaunchKernelGGL((draft_pick_kernel<LT, GREEDY, PER>), dim3(R), dim3(256), 0, s, base, bs, E, W2,
-                       anchor, tok, q, stats, R, gamma, V, r, k, it, seed, round, n_vt, part);
+                       anchor, tok, q, stats, R, gamma, V, r, k, it, seed, round, n_vt, part, S);
 }
 
 template <typename LT>
@@ -167,14 +171,19 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
                                  const int32_t* anchor, int32_t* tok, float* q, double* stats,
                                  int R, int gamma, int V, int r, int k, float temperature,
                                  uint64_t seed, uint32_t round, void* ws, unsigned* ctl,
-                                 hipStream_t s)
+                                 const uint16_t* S, hipStream_t s)
 {
     const int n_vt = (V + kVocabTile - 1) / kVocabTile;
     Part* part = static_cast<Part*>(ws);
     const bool greedy = (temperature == 0.0f);
     const float it = greedy ? 1.0f : 1.0f / temperature;
     PassArgs a{};
-    a.base = base; a.bs = bs; a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.base = base; a.bs = bs; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    if (S) {   // recurrent head: row n of position k's states
+        a.E = S + (int64_t)k * r; a.e_rs = (int64_t)gamma * r; a.e_rows = R; a.rnn = 1;
+    } else {   // Markov head: row x_{k-1} of the embedding
+        a.E = E; a.e_rs = r; a.e_rows = V; a.rnn = 0;
+    }
     a.R = R; a.gamma = gamma; a.V = V; a.r = r; a.k = k; a.inv_temp = it;
     a.n_vt = n_vt;
     a.req_per_wg = pass_req_per_wg(R, n_vt);
@@ -198,9 +207,9 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     const int per = (n_vt + 255) / 256;
 #define DSP_PICK(P)                                                                              \
     (greedy ? launch_pick<LT, true, P>(base, bs, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, \
-                                       it, seed, round, n_vt, part, s)                           \
+                                       it, seed, round, n_vt, part, S, s)                        \
             : launch_pick<LT, false, P>(base, bs, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, \
-                                        it, seed, round, n_vt, part, s))
+                                        it, seed, round, n_vt, part, S, s))
     if (per <= 1) DSP_PICK(1);
     else if (per <= 2) DSP_PICK(2);
     else if (per <= 4) DSP_PICK(4);
@@ -365,13 +374,96 @@ bool run_geometry(int V, RunGeometry* g)
     return tu > 0;
 }
 
+// ---------------------------------------------------------------------------
+// Recurrent head state of position k: S[n, k] = bf16(tanh(A S[n, k-1] +
+// E[x_{k-1}])), S[n, -1] = 0, the E term dropped for x outside [0, V).  One
+// workgroup per kRnnReq requests; thread i computes element i of each: its row
+// of A in registers, the previous states in LDS, the dot product in fp64 in
+// index order (bf16 x bf16 products are exact), tanh in fp64, then one rounding
+// to the nearest bf16 (ties to even) directly from fp64.
+// ---------------------------------------------------------------------------
+constexpr int kRnnReq = 8;
+
+__device__ __forceinline__ uint16_t bf16_rne_f64(double x)
+{
+    // the two bf16 values around x: the truncation of x's nearest float and the
+    // next one up in magnitude (rounding to float never crosses a bf16 value)
+    const uint32_t u = __float_as_uint((float)x);
+    const uint32_t lo = u & 0xFFFF0000u, hi = lo + 0x10000u;
+    const double dlo = fabs(x - (double)__uint_as_float(lo));
+    const double dhi = fabs((double)__uint_as_float(hi) - x);
+    const uint32_t pick = (dlo < dhi) ? lo : (dhi < dlo) ? hi : (((lo >> 16) & 1u) ? hi : lo);
+    return (uint16_t)(pick >> 16);
+}
+
+__global__ __launch_bounds__(256) void rnn_state_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ E, const int32_t* __restrict__ anchor,
+    const int32_t* __restrict__ tok, uint16_t* __restrict__ S, int R, int gamma, int V, int r, int k)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t sp[kRnnReq][kRankMax];
+    const int n0 = blockIdx.x * kRnnReq;
+    const int t = threadIdx.x;
+    // previous states of the workgroup's requests (zero for position 0)
+    for (int w = t; w < kRnnReq * (kRankMax / 8); w += 256) {
+        const int j = w / (kRankMax / 8), c = 8 * (w % (kRankMax / 8)), n = n0 + j;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k > 0 && n < R && c < r)
+            v = *reinterpret_cast<const uint4*>(S + ((int64_t)n * gamma + (k - 1)) * r + c);
+        *reinterpret_cast<uint4*>(&sp[j][c]) = v;
+    }
+    __syncthreads();
+    if (t >= r) return;
+    uint4 arow[kRankMax / 8];
+#pragma unroll
+    for (int c = 0; c < kRankMax / 8; ++c)
+        arow[c] = (8 * c < r) ? *reinterpret_cast<const uint4*>(A + (int64_t)t * r + 8 * c)
+                              : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kRnnReq; ++j) {
+        const int n = n0 + j;
+        if (n >= R) break;
+        const int x = (k == 0) ? anchor[n] : tok[(int64_t)n * gamma + (k - 1)];
+        double u = 0.0;
+#pragma unroll
+        for (int c = 0; c < kRankMax / 8; ++c) {
+            if (8 * c >= r) break;
+            const uint4 sv = *reinterpret_cast<const uint4*>(&sp[j][8 * c]);
+            const uint32_t aw[4] = {arow[c].x, arow[c].y, arow[c].z, arow[c].w};
+            const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u = fma((double)__uint_as_float(aw[e] << 16), (double)__uint_as_float(sw[e] << 16), u);
+                u = fma((double)__uint_as_float(aw[e] & 0xFFFF0000u),
+                        (double)__uint_as_float(sw[e] & 0xFFFF0000u), u);
+            }
+        }
+        if (x >= 0 && x < V) u += (double)bf16_to_f32(E[(int64_t)x * r + t]);
+        S[((int64_t)n * gamma + k) * r + t] = bf16_rne_f64(tanh(u));
+    }
+}
+
 hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const uint16_t* E,
                              const uint16_t* W2,
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, int n_steps, int path,
                              bool give_up, float temperature, uint64_t seed, uint32_t round,
-                             void* ws, hipStream_t s)
+                             void* ws, hipStream_t s, const uint16_t* A, uint16_t* S)
 {
+    if (S) {   // recurrent head: streaming launches only, each position after its state
+        if (path == kPathPersistent) return hipErrorNotSupported;
+        unsigned* ctl = const_cast<unsigned*>(draft_error_word(ws, R, V));
+        for (int i = 0; i < n_steps; ++i) {
+            hipLaunchKernelGGL(rnn_state_kernel, dim3((unsigned)((R + kRnnReq - 1) / kRnnReq)), dim3(256),
+                               0, s, A, E, anchor, tok, S, R, gamma, V, r, k + i);
+            unsigned* c = (i == 0) ? ctl : nullptr;
+            const hipError_t e =
+                bf16 ? launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,
+                                      R, gamma, V, r, k + i, temperature, seed, round, ws, c, S, s)
+                     : launch_draft_t(static_cast<const float*>(base), bs, E, W2, anchor, tok, q, stats,
+                                      R, gamma, V, r, k + i, temperature, seed, round, ws, c, S, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if (path != kPathStream && bf16) {
         bool launched = false;
         const hipError_t e = try_launch_run(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok,
@@ -386,9 +478,9 @@ hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const u
         unsigned* c = (i == 0) ? ctl : nullptr;
         const hipError_t e =
             bf16 ? launch_draft_t(static_cast<const uint16_t*>(base), bs, E, W2, anchor, tok, q, stats,
-                                  R, gamma, V, r, k + i, temperature, seed, round, ws, c, s)
+                                  R, gamma, V, r, k + i, temperature, seed, round, ws, c, nullptr, s)
                  : launch_draft_t(static_cast<const float*>(base), bs, E, W2, anchor, tok, q, stats,
-                                  R, gamma, V, r, k + i, temperature, seed, round, ws, c, s);
+                                  R, gamma, V, r, k + i, temperature, seed, round, ws, c, nullptr, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -158,23 +158,27 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
     // the raw tokens of this thread's two staging rows in the next block in
     // order (blk), validated where they are used
     int tnext = 0;
+    // (recurrent head: the row of the bias table is the request itself)
     auto prev_raw = [&](int blk, int (&p)[2]) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) p[c] = tsrc[row_live(blk, c) ? tix0[c] + tnext : tlast];
+        for (int c = 0; c < 2; ++c)
+            p[c] = a.rnn ? row0[c] + blk * kPassBlock : tsrc[row_live(blk, c) ? tix0[c] + tnext : tlast];
         tnext += tstep;
     };
     auto prev_ok = [&](int blk, int c, int p) -> bool {
-        return row_live(blk, c) && (unsigned)p < (unsigned)V;
+        return row_live(blk, c) && (unsigned)p < (unsigned)a.e_rows;
     };
+    const int e_rs = (int)a.e_rs;             // bias-table row stride (<= 64 x 256)
     const int kk = 8 * sword;                 // this thread's k-slice of an embedding row
     const int kk_in = (kk < r) ? kk : 0;      // ... clamped into the row
     uint4 eu[2];
     auto load_e = [&](int blk, const int (&p)[2]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            // prev < V <= 2^19 and r <= 256: the row offset fits a 24-bit multiply
+            // a row index below 2^24 and a stride below 2^15 whose product stays
+            // below 2^31 (the library bounds both tables): a 24-bit multiply
             const int prev = prev_ok(blk, c, p[c]) ? p[c] : 0;
-            eu[c] = *reinterpret_cast<const uint4*>(a.E + (__umul24(prev, r) + kk_in));
+            eu[c] = *reinterpret_cast<const uint4*>(a.E + (__umul24(prev, e_rs) + kk_in));
         }
     };
     auto store_e = [&](int b, int blk, const int (&p)[2]) {

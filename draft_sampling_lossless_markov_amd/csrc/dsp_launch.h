@@ -58,7 +58,10 @@ hipError_t launch_draft_step(const void* base, RowStrides bs, bool bf16, const u
                              const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                              int gamma, int V, int r, int k, int n_steps, int path,
                              bool give_up, float temperature, uint64_t seed, uint32_t round,
-                             void* ws, hipStream_t s);
+                             void* ws, hipStream_t s, const uint16_t* A = nullptr,
+                             uint16_t* S = nullptr);
+// (A, S non-null: the recurrent head with matrix A [r, r] and states S [R, gamma, r],
+// streaming launches only.)
 
 hipError_t launch_confidence(const uint16_t* h, const uint16_t* E, const int32_t* anchor,
                              const int32_t* tok, const float* w, const float* T,
@@ -85,7 +88,8 @@ size_t tv_workspace_bytes(int R, int gamma, int V);
 hipError_t launch_tv_accept(const void* target, RowStrides ts, const void* base, RowStrides bs,
                             bool bf16, const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
                             const int32_t* tok, const double* stats, double* alpha, int R, int gamma,
-                            int V, int r, float temperature, void* ws, hipStream_t s);
+                            int V, int r, float temperature, void* ws, hipStream_t s,
+                            const uint16_t* S = nullptr);
 
 hipError_t launch_schedule_async(const float* c, const float* c_hist, const float* sps, int B_max,
                                  uint64_t S0, int32_t* len, float* a, int32_t* B, int32_t* K, int R,
@@ -97,6 +101,12 @@ hipError_t launch_verify(const void* target, RowStrides ts, const void* base, Ro
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
                          float temperature, uint64_t seed, uint32_t round, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const uint16_t* S = nullptr);
+// (S non-null: the recurrent head's states [R, gamma, r] give the draft law at a
+// rejection; the residual draws run the streaming passes.)
+
+// Largest R gamma r for the recurrent head (its state rows are indexed with
+// 32-bit offsets).
+constexpr int64_t kRnnMaxStateElems = ((int64_t)1 << 31) - 1;
 
 }  // namespace dsp

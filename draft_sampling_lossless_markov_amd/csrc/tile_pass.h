@@ -109,7 +109,16 @@ struct PassArgs {
     const void* base;        // [R, gamma, V] draft base logits
     const void* target;      // [R, gamma+1, V] target logits (kResidual)
     RowStrides bs, ts;       // element strides of base and target rows
+    // The table of bias rows (r bf16 values each): row p at E + p * e_rs, valid
+    // for 0 <= p < e_rows.  Markov head: the embedding E, e_rs = r, e_rows = V,
+    // row = the previous token.  Recurrent head: its states S [R, gamma, r];
+    // a draft pass at position k takes E = S + k r, e_rs = gamma r, e_rows = R and
+    // row = the request (rnn = 1); a residual pass takes E = S, e_rs = r,
+    // e_rows = R gamma and the queue's list_prev = n gamma + m.
     const uint16_t* E;
+    int64_t e_rs;
+    int e_rows;
+    int rnn;
     const uint16_t* W2;
     const int32_t* anchor;
     const int32_t* tok;
@@ -298,17 +307,18 @@ __global__ __launch_bounds__(256, (pass_min_blocks<LT, KIND, VEC>())) void bias_
     auto prev_raw = [&](int blk) -> int {
         const int ec = min(n_begin + blk * kPassBlock + srow, n_end - 1);
         if constexpr (RES) return a.list_prev[ec];
+        else if (a.rnn) return ec;
         else return (a.k == 0) ? a.anchor[ec] : a.tok[(int64_t)ec * gamma + (a.k - 1)];
     };
-    // the token selects a Markov row: a live request and a token inside [0, V)
+    // the row index selects a bias row: a live request and a row of the table
     auto prev_ok = [&](int blk, int p) -> bool {
-        return n_begin + blk * kPassBlock + srow < n_end && p >= 0 && p < V;
+        return n_begin + blk * kPassBlock + srow < n_end && (unsigned)p < (unsigned)a.e_rows;
     };
     constexpr int kWords = kRankMax / 8 / 8;   // 16-byte words per thread (4)
     uint4 eu[kWords];
     auto load_e = [&](int blk, int praw) {
         const int prev = prev_ok(blk, praw) ? praw : 0;
-        const uint16_t* rowp = a.E + (int64_t)prev * r;
+        const uint16_t* rowp = a.E + (int64_t)prev * a.e_rs;
 #pragma unroll
         for (int c = 0; c < kWords; ++c) {
             const int kk = (sq * kWords + c) * 8;

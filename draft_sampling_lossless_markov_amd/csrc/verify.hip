@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
     const int32_t* __restrict__ tok, const float* __restrict__ q, const int32_t* __restrict__ len,
     int8_t* __restrict__ accept, int32_t* __restrict__ n_accept, int32_t* __restrict__ y,
     float* __restrict__ p_out, int R, int gamma, float inv_temp, uint64_t seed, uint32_t round,
-    int n_vt, VerifyWs ws, int run_n_t)
+    int n_vt, VerifyWs ws, int run_n_t, int rnn)
 {
     __shared__ int slot_s;
     __shared__ int acc_s[kGammaMax + 1];
@@ -299,9 +299,11 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(
                 slot_s = slot;
                 ws.resid_list[slot] = n;
                 ws.resid_m[slot] = nacc;
-                // the token before the rejection (drafted positions j < l are in tk_s)
+                // the bias row of the rejected position: the token before it
+                // (drafted positions j < l are in tk_s), or for the recurrent
+                // head the state row (n, nacc)
                 const int pv = (nacc == 0) ? anchor_n : tk_s[nacc - 1];
-                ws.resid_prev[slot] = (pv >= 0 && pv < V) ? pv : -1;
+                ws.resid_prev[slot] = rnn ? n * gamma + nacc : (pv >= 0 && pv < V) ? pv : -1;
                 ws.resid_slot[n] = slot;
                 ws.row_m[n] = m_s[nacc];
                 ws.row_z[n] = z_s[nacc];
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256, 4) void verify_pick_kernel(
     const double* __restrict__ stats,
     const int32_t* __restrict__ len, const int32_t* __restrict__ n_accept,
     int32_t* __restrict__ y, int R, int gamma, int V, int r, float inv_temp, uint64_t seed,
-    uint32_t round, int n_vt, VerifyWs ws)
+    uint32_t round, int n_vt, VerifyWs ws, const uint16_t* __restrict__ S)
 {
     __shared__ PickScratch sh;
     __shared__ __attribute__((aligned(16))) uint16_t e_row[kRankMax];
@@ -373,9 +375,12 @@ __global__ __launch_bounds__(256, 4) void verify_pick_kernel(
             const float Mt = ws.row_m[n];
             const float invZt = (float)(1.0 / ws.row_z[n]);
             if (tid < kRankMax / 8) {
+                // the draft law's bias row: E[x_{m-1}] (Markov head) or S[n, m]
+                const uint16_t* er = S ? S + ((int64_t)n * gamma + m) * r
+                                       : (prev >= 0 ? E + (int64_t)prev * r : nullptr);
                 const int kk = 8 * tid;
                 uint4 ev = make_uint4(0, 0, 0, 0);
-                if (prev >= 0 && kk < r) ev = *reinterpret_cast<const uint4*>(E + (int64_t)prev * r + kk);
+                if (er && kk < r) ev = *reinterpret_cast<const uint4*>(er + kk);
                 *reinterpret_cast<uint4*>(e_row + kk) = ev;
             }
             const float zd = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, sh);
@@ -443,14 +448,14 @@ template <bool GREEDY>
 static void launch_accept(const int32_t* anchor, int V, const int32_t* tok, const float* q,
                           const int32_t* len, int8_t* accept, int32_t* n_accept, int32_t* y,
                           float* p, int R, int gamma, float it, uint64_t seed, uint32_t round,
-                          int n_vt, const VerifyWs& ws, hipStream_t s, int run_n_t = 0)
+                          int n_vt, const VerifyWs& ws, hipStream_t s, int run_n_t, int rnn)
 {
     const int np = 4 * ((n_vt + kSpanTiles - 1) / kSpanTiles);
     const int per = (np + kWave - 1) / kWave;     // <= 4 for V <= kVocabMax
 #define DSP_ACCEPT(P)                                                                          \
     hipLaunchKernelGGL((verify_accept_kernel<GREEDY, P>), dim3(R), dim3(256), 0, s, anchor, V, \
                        tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round, n_vt, ws,  \
-                       run_n_t)
+                       run_n_t, rnn)
     if (per <= 1) DSP_ACCEPT(1);
     else if (per <= 2) DSP_ACCEPT(2);
     else if (per <= 4) DSP_ACCEPT(4);
@@ -466,12 +471,12 @@ static void launch_vpick(const LT* target, RowStrides ts, const LT* base, RowStr
                          const int32_t* anchor, const int32_t* tok, const double* stats,
                          const int32_t* len, const int32_t* n_accept, int32_t* y, int R, int gamma,
                          int V, int r, float it, uint64_t seed, uint32_t round, int n_vt,
-                         const VerifyWs& ws, hipStream_t s)
+                         const VerifyWs& ws, const uint16_t* S, hipStream_t s)
 {
     hipLaunchKernelGGL((verify_pick_kernel<LT, PER>), dim3(R), dim3(256), 0, s, target, ts, base, bs,
                        E, W2,
                        anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt,
-                       ws);
+                       ws, S);
 }
 
 template <int TU>
@@ -501,9 +506,10 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
                                   const float* q, const double* stats, const int32_t* len,
                                   int8_t* accept, int32_t* n_accept, int32_t* y, float* p, int R,
                                   int gamma, int V, int r, float temperature, uint64_t seed,
-                                  uint32_t round, void* ws_raw, hipStream_t s)
+                                  uint32_t round, void* ws_raw, const uint16_t* S, hipStream_t s)
 {
     const VerifyWs ws = carve(ws_raw, R, gamma, V, nullptr);
+    const int rnn = S ? 1 : 0;
     const int n_vt = (V + kVocabTile - 1) / kVocabTile;
     const bool greedy = (temperature == 0.0f);
     const float it = greedy ? 1.0f : 1.0f / temperature;
@@ -515,20 +521,21 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
         hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, ts, tok, len,
                            R, gamma, V, it, n_vt, ws, 0u);
         launch_accept<true>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed,
-                            round, n_vt, ws, s);
+                            round, n_vt, ws, s, 0, rnn);
         return hipGetLastError();
     }
-    // the persistent residual launch, where the draft's geometry applies
+    // the persistent residual launch, where the draft's geometry applies (Markov
+    // head only)
     RunGeometry geo{0, 0, 0};
     bool run = false;
     if constexpr (std::is_same<LT, uint16_t>::value)
-        run = path != kPathStream && rows_vec(bs, V, 8) && rows_vec(ts, V, 8) && R <= kRunReqMax &&
+        run = !S && path != kPathStream && rows_vec(bs, V, 8) && rows_vec(ts, V, 8) && R <= kRunReqMax &&
               run_geometry(V, &geo);
     if (path == kPathPersistent && !run) return hipErrorNotSupported;
     hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, ts, tok, len, R,
                        gamma, V, it, n_vt, ws, (run && give_up) ? 1u : 0u);
     launch_accept<false>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round,
-                         n_vt, ws, s, run ? geo.n_t : 0);
+                         n_vt, ws, s, run ? geo.n_t : 0, rnn);
     if constexpr (std::is_same<LT, uint16_t>::value) {
         if (run) {
             ResidArgs ra{};
@@ -557,7 +564,9 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     }
     PassArgs a{};
     a.base = base; a.target = target; a.bs = bs; a.ts = ts;
-    a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    // bias rows of the queued rejections: E[x] or the states S[n, m]
+    a.E = S ? S : E; a.e_rs = r; a.e_rows = S ? R * gamma : V; a.rnn = 0;
     a.list = ws.resid_list; a.list_m = ws.resid_m; a.list_prev = ws.resid_prev;
     a.count = ws.resid_cnt; a.n_accept = n_accept; a.stats = stats;
     a.row_m = ws.row_m; a.row_z = ws.row_z;
@@ -571,10 +580,10 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     else
         hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, false>), g3, dim3(256), 0, s, a);
     const int per = (n_vt + 255) / 256;
-    if (per <= 1) launch_vpick<LT, 1>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
-    else if (per <= 2) launch_vpick<LT, 2>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
-    else if (per <= 4) launch_vpick<LT, 4>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
-    else launch_vpick<LT, 8>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, s);
+    if (per <= 1) launch_vpick<LT, 1>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, S, s);
+    else if (per <= 2) launch_vpick<LT, 2>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, S, s);
+    else if (per <= 4) launch_vpick<LT, 4>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, S, s);
+    else launch_vpick<LT, 8>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, S, s);
     return hipGetLastError();
 }
 
@@ -633,7 +642,7 @@ inline TvWs carve_tv(void* ws, int R, int gamma, int V, size_t* total)
 // one thread per (request, position) entry: the residual pass's queue and the
 // row limit that makes verify_rows stream target rows 0 .. gamma - 1
 __global__ void tv_prep_kernel(const int32_t* __restrict__ anchor, const int32_t* __restrict__ tok,
-                               int R, int gamma, int V, TvWs ws)
+                               int R, int gamma, int V, TvWs ws, int rnn)
 {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t N = (int64_t)R * gamma;
@@ -644,7 +653,8 @@ __global__ void tv_prep_kernel(const int32_t* __restrict__ anchor, const int32_t
     const int p = (k == 0) ? anchor[n] : tok[e - 1];
     ws.list[e] = n;
     ws.list_m[e] = k;
-    ws.list_prev[e] = (p >= 0 && p < V) ? p : -1;
+    // bias row: the token before the position, or the recurrent state row e
+    ws.list_prev[e] = rnn ? (int)e : (p >= 0 && p < V) ? p : -1;
 }
 
 // one wave per entry: the target row's (M, Z) from verify_rows' 8-tile partials
@@ -707,14 +717,15 @@ template <typename LT>
 static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, RowStrides bs,
                               const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
                               const int32_t* tok, const double* stats, double* alpha, int R,
-                              int gamma, int V, int r, float temperature, void* ws_raw, hipStream_t s)
+                              int gamma, int V, int r, float temperature, void* ws_raw,
+                              const uint16_t* S, hipStream_t s)
 {
     const TvWs ws = carve_tv(ws_raw, R, gamma, V, nullptr);
     const int n_vt = (V + kVocabTile - 1) / kVocabTile;
     const float it = 1.0f / temperature;
     const int64_t N = (int64_t)R * gamma;
     hipLaunchKernelGGL(tv_prep_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, anchor, tok,
-                       R, gamma, V, ws);
+                       R, gamma, V, ws, S ? 1 : 0);
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int64_t items = (int64_t)R * spans;
     hipLaunchKernelGGL((verify_rows_kernel<LT, false>), dim3((unsigned)items), dim3(256), 0, s, target,
@@ -732,7 +743,8 @@ static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, R
 #undef DSP_TVROW
     PassArgs a{};
     a.base = base; a.target = target; a.bs = bs; a.ts = ts;
-    a.E = E; a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.W2 = W2; a.anchor = anchor; a.tok = tok;
+    a.E = S ? S : E; a.e_rs = r; a.e_rows = S ? R * gamma : V; a.rnn = 0;
     a.list = ws.list; a.list_m = ws.list_m; a.list_prev = ws.list_prev; a.count = ws.count;
     a.stats = stats; a.row_m = ws.row_m; a.row_z = ws.row_z; a.row_by_entry = 1;
     a.R = R; a.gamma = gamma; a.V = V; a.r = r; a.k = 0; a.inv_temp = it;
@@ -758,13 +770,13 @@ static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, R
 hipError_t launch_tv_accept(const void* target, RowStrides ts, const void* base, RowStrides bs,
                             bool bf16, const uint16_t* E, const uint16_t* W2, const int32_t* anchor,
                             const int32_t* tok, const double* stats, double* alpha, int R, int gamma,
-                            int V, int r, float temperature, void* ws, hipStream_t s)
+                            int V, int r, float temperature, void* ws, hipStream_t s, const uint16_t* S)
 {
     if (bf16)
         return launch_tv_t(static_cast<const uint16_t*>(target), ts, static_cast<const uint16_t*>(base),
-                           bs, E, W2, anchor, tok, stats, alpha, R, gamma, V, r, temperature, ws, s);
+                           bs, E, W2, anchor, tok, stats, alpha, R, gamma, V, r, temperature, ws, S, s);
     return launch_tv_t(static_cast<const float*>(target), ts, static_cast<const float*>(base), bs, E,
-                       W2, anchor, tok, stats, alpha, R, gamma, V, r, temperature, ws, s);
+                       W2, anchor, tok, stats, alpha, R, gamma, V, r, temperature, ws, S, s);
 }
 
 hipError_t launch_verify(const void* target, RowStrides ts, const void* base, RowStrides bs,
@@ -772,17 +784,19 @@ hipError_t launch_verify(const void* target, RowStrides ts, const void* base, Ro
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const float* q, const double* stats, const int32_t* len, int8_t* accept,
                          int32_t* n_accept, int32_t* y, float* p, int R, int gamma, int V, int r,
-                         float temperature, uint64_t seed, uint32_t round, void* ws, hipStream_t s)
+                         float temperature, uint64_t seed, uint32_t round, void* ws, hipStream_t s,
+                         const uint16_t* S)
 {
+    if (S && path == kPathPersistent) return hipErrorNotSupported;
     if (bf16)
         return launch_verify_t(static_cast<const uint16_t*>(target), ts,
                                static_cast<const uint16_t*>(base), bs, path, give_up, E, W2, anchor, tok, q, stats,
                                len, accept, n_accept, y, p, R, gamma, V, r, temperature, seed, round,
-                               ws, s);
+                               ws, S, s);
     return launch_verify_t(static_cast<const float*>(target), ts, static_cast<const float*>(base), bs,
                            path, give_up, E, W2,
                            anchor, tok, q, stats, len, accept, n_accept, y, p, R, gamma, V, r,
-                           temperature, seed, round, ws, s);
+                           temperature, seed, round, ws, S, s);
 }
 
 }  // namespace dsp

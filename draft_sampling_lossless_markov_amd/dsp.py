@@ -29,7 +29,8 @@ DSP_FLAG_TEST_GIVE_UP = 0x100
 EXPORTED = ("dsp_status_string", "dsp_last_error", "dsp_version", "dsp_workspace_size",
             "dsp_workspace_status", "dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence",
             "dsp_schedule", "dsp_schedule_async", "dsp_verify", "dsp_tv_accept",
-            "dsp_confidence_logit", "dsp_sts_fit", "dsp_ece")
+            "dsp_confidence_logit", "dsp_sts_fit", "dsp_ece", "dsp_draft_step_rnn",
+            "dsp_verify_rnn", "dsp_tv_accept_rnn")
 
 _lib = None
 
@@ -76,11 +77,18 @@ def lib():
     L.dsp_schedule_async.argtypes = [P, P, P, I, D, P, P, P, P, I, I, P]
     L.dsp_tv_accept.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, I, I, I, I, F, P, SZ, P]
     L.dsp_confidence_logit.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    L.dsp_draft_step_rnn.argtypes = [P, I, I64, I64, P, P, P, P, P, P, P, P, I, I, I, I, I, I, U32,
+                                     F, U64, U32, P, SZ, P]
+    L.dsp_verify_rnn.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, P, P, P, P, P,
+                                 I, I, I, I, U32, F, U64, U32, P, SZ, P]
+    L.dsp_tv_accept_rnn.argtypes = [P, I64, I64, P, I64, I64, I, P, P, P, P, P, P, P, I, I, I, I, F,
+                                    P, SZ, P]
     L.dsp_sts_fit.argtypes = [P, P, I, I, F, F, P, P, P, SZ, P]
     L.dsp_ece.argtypes = [P, P, P, I, I, I, P, P, SZ, P]
     for f in ("dsp_draft_step", "dsp_draft_step_noalloc", "dsp_confidence", "dsp_schedule",
               "dsp_schedule_async", "dsp_verify", "dsp_tv_accept", "dsp_confidence_logit",
-              "dsp_sts_fit", "dsp_ece"):
+              "dsp_sts_fit", "dsp_ece", "dsp_draft_step_rnn", "dsp_verify_rnn",
+              "dsp_tv_accept_rnn"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -138,6 +146,19 @@ def dsp_draft_step(base, E, W2, anchor, tok, q, stats, k, temperature, seed, rou
                                 _ptr(tok), _ptr(q), _ptr(stats), R, gamma, V, r, int(k),
                                 int(n_steps), int(flags), float(temperature), int(seed), int(round_),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsp_draft_step_rnn(base, E, W2, A, anchor, tok, q, stats, S, k, temperature, seed, round_, ws,
+                       stream=None, n_steps=1, flags=DSP_PATH_AUTO):
+    """dsp_draft_step with the recurrent head: A [r, r] bf16, states S [R, gamma, r] bf16."""
+    R, gamma, V = base.shape
+    r = E.shape[1]
+    rs, ps = _rows(base, "base")
+    _check(lib().dsp_draft_step_rnn(_ptr(base), _dtype(base), rs, ps, _ptr(E), _ptr(W2), _ptr(A),
+                                    _ptr(anchor), _ptr(tok), _ptr(q), _ptr(stats), _ptr(S), R, gamma,
+                                    V, r, int(k), int(n_steps), int(flags), float(temperature),
+                                    int(seed), int(round_), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
 
 
 def dsp_draft_step_noalloc(base, E, W2, anchor, tok, q, stats, k, temperature, seed, round_,
@@ -207,6 +228,38 @@ def dsp_verify(target, base, E, W2, anchor, tok, q, stats, length, accept, n_acc
                             _ptr(accept), _ptr(n_accept), _ptr(y), _ptr(p), R, g1 - 1, V, r,
                             int(flags), float(temperature), int(seed), int(round_), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsp_verify_rnn(target, base, E, W2, S, anchor, tok, q, stats, length, accept, n_accept, y, p,
+                   temperature, seed, round_, ws, stream=None, flags=DSP_PATH_AUTO):
+    """dsp_verify after dsp_draft_step_rnn (S [R, gamma, r] bf16: the draft's states)."""
+    R, g1, V = target.shape
+    r = E.shape[1]
+    trs, tps = _rows(target, "target")
+    brs, bps = _rows(base, "base")
+    if base.dtype != target.dtype:
+        raise TypeError("base and target logits must share a dtype")
+    _check(lib().dsp_verify_rnn(_ptr(target), trs, tps, _ptr(base), brs, bps, _dtype(target),
+                                _ptr(E), _ptr(W2), _ptr(S), _ptr(anchor), _ptr(tok), _ptr(q),
+                                _ptr(stats), _ptr(length), _ptr(accept), _ptr(n_accept), _ptr(y),
+                                _ptr(p), R, g1 - 1, V, r, int(flags), float(temperature), int(seed),
+                                int(round_), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def dsp_tv_accept_rnn(target, base, E, W2, S, anchor, tok, stats, alpha, temperature, ws,
+                      stream=None):
+    """dsp_tv_accept for the recurrent head's draft (S: its states)."""
+    R, g1, V = target.shape
+    r = E.shape[1]
+    trs, tps = _rows(target, "target")
+    brs, bps = _rows(base, "base")
+    if base.dtype != target.dtype:
+        raise TypeError("base and target logits must share a dtype")
+    _check(lib().dsp_tv_accept_rnn(_ptr(target), trs, tps, _ptr(base), brs, bps, _dtype(target),
+                                   _ptr(E), _ptr(W2), _ptr(S), _ptr(anchor), _ptr(tok), _ptr(stats),
+                                   _ptr(alpha), R, g1 - 1, V, r, float(temperature), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dsp_tv_accept(target, base, E, W2, anchor, tok, stats, alpha, temperature, ws, stream=None):

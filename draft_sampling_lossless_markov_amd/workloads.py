@@ -200,3 +200,12 @@ def calibration_set(N: int, gamma: int, seed: int, t_true=None, mu: float = 1.5,
     ok = (u < p).to(torch.int32)
     acc = torch.cumprod(ok, dim=1).sum(dim=1).to(torch.int32)
     return z.to(device), acc.to(device)
+
+
+def rnn_matrix(r: int, seed: int, scale: float = 0.5, device="cpu") -> torch.Tensor:
+    """Recurrent matrix of the recurrent sequential head: [r, r] bf16 with
+    entries ~ N(0, scale^2 / r), so that A s keeps the state's scale for a
+    unit-scale s (spectral radius about `scale`)."""
+    g = torch.Generator().manual_seed(int(seed))
+    A = torch.randn(r, r, generator=g, dtype=torch.float32) * (scale / r ** 0.5)
+    return A.to(torch.bfloat16).to(device)

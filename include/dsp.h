@@ -54,7 +54,10 @@
  * Sizes supported: R >= 1, 1 <= gamma <= 64, 1 <= V <= 524288, 8 <= r <= 256
  * with r % 8 == 0, 0 <= d; the scheduler in mode 1 needs R * gamma <= 16384.
  *
- * ABI version 400: DSP_ERR_TIMEOUT and dsp_workspace_status(); the scheduler's
+ * ABI version 410: the recurrent sequential head (dsp_draft_step_rnn,
+ * dsp_verify_rnn, dsp_tv_accept_rnn), sequential temperature scaling
+ * (dsp_confidence_logit, dsp_sts_fit, dsp_ece).
+ * 400: DSP_ERR_TIMEOUT and dsp_workspace_status(); the scheduler's
  * tau0 is bounded by 2^14.  (300: dsp_draft_step draws n_steps consecutive
  * positions per call; dsp_draft_step and dsp_verify take flags that select their
  * implementation.  200: element strides.)
@@ -182,6 +185,34 @@ dsp_status dsp_draft_step(const void* base, dsp_dtype dtype, int64_t base_rs, in
                           double* stats, int R, int gamma, int V, int r, int k, int n_steps,
                           unsigned flags, float temperature, uint64_t seed, uint32_t round, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * dsp_draft_step_rnn -- dsp_draft_step with the recurrent sequential head.
+ *
+ * Page "DeepSeek联合北大最新文章DSpark", 第二阶段轻量顺序头: besides the Markov head
+ * (previous token only), an RNN head keeps a recurrent state to capture longer
+ * dependencies; the page gives no recurrence.  This library's reading, an
+ * Elman recurrence on the Markov head's rank-r space:
+ *     s[n,-1] = 0
+ *     s[n,k]  = bf16(tanh(A s[n,k-1] + E[x_{k-1}]))   (fp64 sum in index order,
+ *               no E term for x outside [0, V); one rounding to nearest even)
+ *     logit   = base[n,k,:] + s[n,k] . W2^T            (the Markov head's MFMA
+ *                                                       bias with s in place of E[x])
+ * With A = 0 it is the Markov head on the table bf16(tanh(E)).  Sampling,
+ * greedy, Philox counters and outputs as dsp_draft_step.
+ *
+ * A [r, r] bf16, element (i, j) at A[i r + j]; S [R, gamma, r] bf16 (device):
+ * positions k .. k + n_steps - 1 are written, and position k - 1 must hold the
+ * state a previous call wrote when k > 0.  R gamma r <= 2^31 - 1.  Streaming
+ * launches only: DSP_PATH_PERSISTENT returns DSP_ERR_UNSUPPORTED.  Workspace:
+ * dsp_workspace_size(DSP_WS_DRAFT, ...).  Other arguments as dsp_draft_step.
+ */
+dsp_status dsp_draft_step_rnn(const void* base, dsp_dtype dtype, int64_t base_rs, int64_t base_ps,
+                              const uint16_t* E, const uint16_t* W2, const uint16_t* A,
+                              const int32_t* anchor, int32_t* tok, float* q, double* stats,
+                              uint16_t* S, int R, int gamma, int V, int r, int k, int n_steps,
+                              unsigned flags, float temperature, uint64_t seed, uint32_t round,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dsp_draft_step_noalloc -- dsp_draft_step for callers that cannot allocate
@@ -378,6 +409,22 @@ dsp_status dsp_verify(const void* target, int64_t target_rs, int64_t target_ps, 
                       size_t ws_bytes, void* stream);
 
 /*
+ * dsp_verify_rnn -- dsp_verify after dsp_draft_step_rnn: at a rejection the
+ * draft law of position m (whose max(0, p - q) the correction draws from) takes
+ * the state row S[n, m] as its bias row instead of E[x_{m-1}].  S [R, gamma, r]
+ * bf16 as dsp_draft_step_rnn wrote it; R gamma r <= 2^31 - 1; streaming
+ * launches only (DSP_PATH_PERSISTENT: DSP_ERR_UNSUPPORTED).  Other arguments,
+ * workspace and results as dsp_verify.
+ */
+dsp_status dsp_verify_rnn(const void* target, int64_t target_rs, int64_t target_ps, const void* base,
+                          int64_t base_rs, int64_t base_ps, dsp_dtype dtype, const uint16_t* E,
+                          const uint16_t* W2, const uint16_t* S, const int32_t* anchor,
+                          const int32_t* tok, const float* q, const double* stats, const int32_t* len,
+                          int8_t* accept, int32_t* n_accept, int32_t* y, float* p, int R, int gamma,
+                          int V, int r, unsigned flags, float temperature, uint64_t seed,
+                          uint32_t round, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * dsp_tv_accept -- the exact acceptance probability of every draft position.
  *
  * Page "为什么DSpark 可以加速推理？", section on the mathematics of speculative
@@ -402,6 +449,18 @@ dsp_status dsp_tv_accept(const void* target, int64_t target_rs, int64_t target_p
                          const uint16_t* W2, const int32_t* anchor, const int32_t* tok,
                          const double* stats, double* alpha, int R, int gamma, int V, int r,
                          float temperature, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsp_tv_accept_rnn -- dsp_tv_accept for the recurrent head: the draft law of
+ * position k takes the state row S[n, k] (dsp_draft_step_rnn) as its bias row.
+ * R gamma r <= 2^31 - 1; other arguments as dsp_tv_accept.
+ */
+dsp_status dsp_tv_accept_rnn(const void* target, int64_t target_rs, int64_t target_ps,
+                             const void* base, int64_t base_rs, int64_t base_ps, dsp_dtype dtype,
+                             const uint16_t* E, const uint16_t* W2, const uint16_t* S,
+                             const int32_t* anchor, const int32_t* tok, const double* stats,
+                             double* alpha, int R, int gamma, int V, int r, float temperature,
+                             void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

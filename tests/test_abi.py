@@ -260,3 +260,24 @@ def test_sts_and_ece_validation(L):
     assert f(P(FAKE), P(0), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), 4, 4, 16, 32, 8, None) == 1
     assert f(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE + 8), None, P(FAKE), 4, 4, 16, 32, 8,
              None) == 1
+
+
+def test_rnn_entry_validation(L):
+    P = C.c_void_p
+    f = L.dsp_draft_step_rnn
+
+    def draft(A=FAKE, S=FAKE, flags=0, R=4, gamma=4, r=8):
+        return f(P(FAKE), 1, 4 * 32, 32, P(FAKE), P(FAKE), P(A), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                 P(S), R, gamma, 32, r, 0, 1, flags, 1.0, 0, 0, P(FAKE), 1 << 20, None)
+
+    assert draft(A=0) == 1 and b"A or S" in L.dsp_last_error()
+    assert draft(S=0) == 1
+    assert draft(S=FAKE + 8) == 1
+    assert draft(flags=2) == 2 and b"streaming" in L.dsp_last_error()
+    v = L.dsp_verify_rnn
+    args = [P(FAKE), 5 * 32, 32, P(FAKE), 4 * 32, 32, 1, P(FAKE), P(FAKE)]
+    rest = [P(FAKE)] * 9 + [4, 4, 32, 8]
+    assert v(*args, P(0), *rest, 0, 1.0, 0, 0, P(FAKE), 1 << 20, None) == 1
+    assert v(*args, P(FAKE), *rest, 2, 1.0, 0, 0, P(FAKE), 1 << 20, None) == 2
+    t = L.dsp_tv_accept_rnn
+    assert t(*args, P(0), *[P(FAKE)] * 4, 4, 4, 32, 8, 1.0, P(FAKE), 1 << 20, None) == 1

@@ -12,7 +12,10 @@ K rounds times every entry point with HIP events on the launch stream and gives
 the roofline of the dominant one.  Prints one JSON line, with the CPU oracle
 timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--mode greedy]
+
+Besides the headline workload it times the other workloads (per_workload) and the
+entry points outside the round (extended).
 """
 import argparse
 import json
@@ -37,6 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/build.py",
                  "draft_sampling_lossless_markov_amd/csrc/draft.hip",
                  "draft_sampling_lossless_markov_amd/csrc/draft_run.h",
+                 "draft_sampling_lossless_markov_amd/csrc/draft_pass.h",
                  "draft_sampling_lossless_markov_amd/csrc/tile_pass.h",
                  "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_device.h",
@@ -375,7 +379,7 @@ def measure(wl, mode, args, steps, warmup, with_cpu, log_prefix=""):
     traffic = profiled_traffic(wl.name, draft_path)
     kernels = ("run_clear_kernel + draft_run_kernel (one persistent launch, all gamma positions)"
                if draft_path == "persistent" else
-               "bias_pass_kernel + draft_pick_kernel per position")
+               "draft_pass_kernel + draft_pick_kernel per position")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": f"dsp_draft_step, {g} positions: {kernels}",
@@ -430,6 +434,101 @@ def measure(wl, mode, args, steps, warmup, with_cpu, log_prefix=""):
     return result
 
 
+def _time_calls(fn, reps, stream):
+    """Average ms of fn() over reps calls back to back, events on the launch stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_extended(reps=5):
+    """The entry points outside the round, at the large-batch workload's sizes (R 2048,
+    gamma 8, V 262144, r 256, bf16, sampling): the capacity-barrier scheduler, the
+    exact acceptance probability of every draft position, the recurrent head's draft
+    step, and sequential temperature scaling with its calibration error on a held-out
+    set of 65536 samples of 8 positions."""
+    from draft_sampling_lossless_markov_amd.workloads import calibration_set, rnn_matrix
+    wl = WORKLOADS[4]
+    inp = make_inputs(wl, 0, device="cuda", layout=BENCH_LAYOUT)
+    R, g, V, r = inp["R"], inp["gamma"], inp["V"], inp["r"]
+    rd = Round(R, g, V, r)
+    stream = torch.cuda.current_stream()
+    temp, seed = wl.temperature, 0
+    out = {"workload": wl.name, "mode": "sampling"}
+    rd.draft(inp, temp, seed, 0)
+    rd.confidence(inp)
+    c_hist = rd.c.roll(1, dims=0).contiguous()   # another round's confidences
+    torch.cuda.synchronize()
+
+    # prefix schedulers (latency-bound: one workgroup sorts R gamma candidates)
+    t_sync = _time_calls(lambda: rd.schedule(inp), 20, stream)
+    t_async = _time_calls(lambda: rd.schedule_async(inp, c_hist), 20, stream)
+    out["schedule_us"] = round(t_sync * 1e3, 2)
+    out["schedule_async_us"] = round(t_async * 1e3, 2)
+
+    # exact acceptance probability: target rows 0..gamma-1 and the draft rows
+    # streamed once, W2 once, the per-entry outputs
+    alpha = torch.zeros(R, g, dtype=torch.float64, device="cuda")
+    ws_tv = torch.zeros(dsp.dsp_workspace_size(dsp.DSP_WS_TV, R, g, V, r), dtype=torch.uint8,
+                        device="cuda")
+    t_tv = _time_calls(lambda: dsp.dsp_tv_accept(inp["target"], inp["base"], inp["E"], inp["W2"],
+                                                 inp["anchor"], rd.tok, rd.stats, alpha, temp,
+                                                 ws_tv), reps, stream)
+    tv_bytes = 2 * (2 * R * g * V) + 2 * r * V + 8 * R * g
+    out["tv_accept"] = {"us": round(t_tv * 1e3, 1), "algorithmic_bytes": tv_bytes,
+                        "achieved_GBs": round(tv_bytes / (t_tv * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(tv_bytes / (t_tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del ws_tv, alpha
+
+    # recurrent head: the Markov draft call against the recurrent one
+    A = rnn_matrix(r, 0).cuda()
+    S = torch.zeros(R, g, r, dtype=torch.bfloat16, device="cuda")
+    t_markov = _time_calls(lambda: dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"],
+                                                      rd.tok, rd.q, rd.stats, 0, temp, seed, 0,
+                                                      rd.ws_draft, n_steps=g,
+                                                      flags=dsp.DSP_PATH_STREAMING), reps, stream)
+    t_rnn = _time_calls(lambda: dsp.dsp_draft_step_rnn(inp["base"], inp["E"], inp["W2"], A,
+                                                       inp["anchor"], rd.tok, rd.q, rd.stats, S, 0,
+                                                       temp, seed, 0, rd.ws_draft, n_steps=g),
+                        reps, stream)
+    rnn_bytes = draft_call_bytes(inp) + 2 * r * r + 2 * (2 * R * g * r)
+    out["rnn_draft"] = {"us": round(t_rnn * 1e3, 1), "markov_streaming_us": round(t_markov * 1e3, 1),
+                        "overhead": round(t_rnn / t_markov - 1.0, 4),
+                        "achieved_GBs": round(rnn_bytes / (t_rnn * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(rnn_bytes / (t_rnn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del S, A, rd, inp
+    torch.cuda.empty_cache()
+
+    # sequential temperature scaling: 2 grid stages x 256 candidates x N samples
+    # per position, each a cumulative-survival cross-entropy in fp64
+    N, gc = 65536, 8
+    z, acc = calibration_set(N, gc, 0, device="cuda")
+    T = torch.zeros(gc, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(dsp.dsp_workspace_size(dsp.DSP_WS_STS, N, gc, 1, 1), dtype=torch.uint8,
+                     device="cuda")
+    t_fit = _time_calls(lambda: dsp.dsp_sts_fit(z, acc, 1.0 / 16, 16.0, T, None, ws), 3, stream)
+    ece = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws_e = torch.zeros(dsp.dsp_workspace_size(dsp.DSP_WS_ECE, 0, 0, 0, 0), dtype=torch.uint8,
+                       device="cuda")
+    t_ece = _time_calls(lambda: dsp.dsp_ece(z, acc, T, 15, ece, ws_e), 10, stream)
+    ece_after = float(ece.item())
+    dsp.dsp_ece(z, acc, None, 15, ece, ws_e)
+    evals = N * gc * 2 * 256
+    out["sts_fit"] = {"N": N, "gamma": gc, "ms": round(t_fit, 3),
+                      "loss_evaluations_per_s": round(evals / (t_fit * 1e-3), 1),
+                      "ece_us": round(t_ece * 1e3, 2),
+                      "ece_before": round(float(ece.item()), 5), "ece_after": round(ece_after, 5),
+                      "T": [round(float(x), 4) for x in T.cpu()]}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -442,6 +541,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-workload", action="store_true",
                     help="time only the headline workload")
+    ap.add_argument("--no-extended", action="store_true",
+                    help="skip the entry points outside the round (async scheduler, exact "
+                         "acceptance, recurrent head, temperature scaling)")
     ap.add_argument("--eager", action="store_true",
                     help="time the rounds as eager launches instead of graph replays")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -481,6 +583,9 @@ def main():
                 "entry_points_us", "verified_per_round", "round_us_percentiles")}
             per[f"{w2.name}/{m}"]["draft_path"] = r2["config"]["draft_path"]
         result["per_workload"] = per
+    if not args.no_extended and args.workload == HEADLINE_WORKLOAD and args.mode is None:
+        log("entry points outside the round")
+        result["extended"] = measure_extended()
     copy_gbs = copy_bandwidth()
     A = result["round_roofline"]["algorithmic_bytes"]
     result["copy_bandwidth"] = {"GBs": round(copy_gbs, 1),

@@ -62,8 +62,9 @@ __device__ __forceinline__ int dp_slot(int rho, int c) { return c ^ ((rho & 15) 
 // The A fragments of wave w: W2 rows v0 + 32 w + dp_arow(i), k-steps 0..15.  Each
 // 64-row quarter of the 256-row tile is read contiguously into LDS; waves 2 q
 // and 2 q + 1 then read their fragments from quarter q.
+template <class Lds>   // an LDS union whose member w2 is [2][64][kRankMax / 8] words
 __device__ __forceinline__ void dp_stage_w2(const uint16_t* __restrict__ W2, int V, int r, int v0,
-                                            DraftPassLds& L, bf16x8 (&a)[kKSteps])
+                                            Lds& L, bf16x8 (&a)[kKSteps])
 {
     constexpr int kWordsRow = kRankMax / 8;                  // 32 words of 16 bytes
     constexpr int kPer = 64 * kWordsRow / kDpThreads;        // 4 words per quarter

@@ -23,6 +23,7 @@
 #include "bias_tile.h"
 #include "dsp_device.h"
 #include "dsp_launch.h"
+#include "resid_pass.h"
 #include "resid_run.h"
 #include "tile_pass.h"
 
@@ -49,6 +50,9 @@ struct VerifyWs {
     Part* resid_part;    // [R, n_vt]
     uint64_t* run_slots; // [R, n_t] residual mass of the persistent residual launch
     unsigned* run_ctl;   // its error word
+    int64_t* resid_roff; // [R, 2] records of the queued entries for resid_pass_kernel
+    int* resid_erow;     // [R]
+    float4* resid_rst;   // [R]
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -74,6 +78,9 @@ inline VerifyWs carve(void* ws, int R, int gamma, int V, size_t* total)
     const size_t n_run = std::min<size_t>((size_t)((V + 31) / 32), (size_t)kRunTilesMax);
     w.run_slots = reinterpret_cast<uint64_t*>(p + off); off += align256((size_t)R * n_run * sizeof(uint64_t));
     w.run_ctl = reinterpret_cast<unsigned*>(p + off); off += 256;
+    w.resid_roff = reinterpret_cast<int64_t*>(p + off); off += align256((size_t)R * 2 * sizeof(int64_t));
+    w.resid_erow = reinterpret_cast<int*>(p + off);   off += align256((size_t)R * sizeof(int));
+    w.resid_rst = reinterpret_cast<float4*>(p + off); off += align256((size_t)R * sizeof(float4));
     if (total) *total = off;
     return w;
 }
@@ -575,10 +582,18 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     a.req_per_wg = pass_req_per_wg(R, n_vt);
     a.part = ws.resid_part;
     const dim3 g3(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
-    if (rows_vec(bs, V, 8) && rows_vec(ts, V, 8))
+    const bool vec = rows_vec(bs, V, 8) && rows_vec(ts, V, 8);
+    if (std::is_same<LT, uint16_t>::value && vec) {   // bf16 rows of 16-byte words
+        hipLaunchKernelGGL(resid_prep_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+                           ws.resid_list, ws.resid_m, ws.resid_prev, ws.resid_cnt, stats, ws.row_m,
+                           ws.row_z, 0, bs, ts, gamma, ws.resid_roff, ws.resid_erow, ws.resid_rst);
+        hipLaunchKernelGGL(resid_pass_kernel, g3, dim3(kDpThreads), 0, s, a,
+                           ResidRecs{ws.resid_roff, ws.resid_erow, ws.resid_rst});
+    } else if (vec) {
         hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, true>), g3, dim3(256), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, false>), g3, dim3(256), 0, s, a);
+    }
     const int per = (n_vt + 255) / 256;
     if (per <= 1) launch_vpick<LT, 1>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, S, s);
     else if (per <= 2) launch_vpick<LT, 2>(target, ts, base, bs, E, W2, anchor, tok, stats, len, n_accept, y, R, gamma, V, r, it, seed, round, n_vt, ws, S, s);
@@ -610,6 +625,9 @@ struct TvWs {
     float* row_m;        // [R gamma] target row maximum
     double* row_z;       // [R gamma] target row normaliser
     Part* part;          // [R gamma, n_vt] residual mass per tile
+    int64_t* roff;       // [R gamma, 2] records for resid_pass_kernel
+    int* erow;           // [R gamma]
+    float4* rst;         // [R gamma]
 };
 
 inline TvWs carve_tv(void* ws, int R, int gamma, int V, size_t* total)
@@ -633,6 +651,9 @@ inline TvWs carve_tv(void* ws, int R, int gamma, int V, size_t* total)
     w.row_m = reinterpret_cast<float*>(p + off);     off += align256(N * sizeof(float));
     w.row_z = reinterpret_cast<double*>(p + off);    off += align256(N * sizeof(double));
     w.part = reinterpret_cast<Part*>(p + off);       off += align256(N * n_vt * sizeof(Part));
+    w.roff = reinterpret_cast<int64_t*>(p + off);    off += align256(N * 2 * sizeof(int64_t));
+    w.erow = reinterpret_cast<int*>(p + off);        off += align256(N * sizeof(int));
+    w.rst = reinterpret_cast<float4*>(p + off);      off += align256(N * sizeof(float4));
     if (total) *total = off;
     return w;
 }
@@ -752,10 +773,18 @@ static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, R
     a.req_per_wg = pass_req_per_wg((int)N, n_vt);
     a.part = ws.part;
     const dim3 g3(n_vt, (unsigned)((N + a.req_per_wg - 1) / a.req_per_wg));
-    if (rows_vec(bs, V, 8) && rows_vec(ts, V, 8))
+    const bool vec = rows_vec(bs, V, 8) && rows_vec(ts, V, 8);
+    if (std::is_same<LT, uint16_t>::value && vec) {   // bf16 rows of 16-byte words
+        hipLaunchKernelGGL(resid_prep_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                           ws.list, ws.list_m, ws.list_prev, ws.count, stats, ws.row_m, ws.row_z, 1,
+                           bs, ts, gamma, ws.roff, ws.erow, ws.rst);
+        hipLaunchKernelGGL(resid_pass_kernel, g3, dim3(kDpThreads), 0, s, a,
+                           ResidRecs{ws.roff, ws.erow, ws.rst});
+    } else if (vec) {
         hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, true>), g3, dim3(256), 0, s, a);
-    else
+    } else {
         hipLaunchKernelGGL((bias_pass_kernel<LT, kResidual, false>), g3, dim3(256), 0, s, a);
+    }
     const int pc = (n_vt + kWave - 1) / kWave;
 #define DSP_TVC(P) hipLaunchKernelGGL((tv_combine_kernel<P>), gw, dim3(256), 0, s, R, gamma, n_vt, ws, alpha)
     if (pc <= 1) DSP_TVC(1);

@@ -191,9 +191,12 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     a.ctl = ctl;
     const dim3 g1(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
     const bool vec = rows_vec(bs, V, 8);
-    if (sizeof(LT) == 2 && vec) {   // bf16 rows of 16-byte words: the software-pipelined pass
-        if (greedy) hipLaunchKernelGGL((draft_pass_kernel<true>), g1, dim3(kDpThreads), 0, s, a);
-        else hipLaunchKernelGGL((draft_pass_kernel<false>), g1, dim3(kDpThreads), 0, s, a);
+    if (sizeof(LT) == 2 && vec && dp_offsets_fit(bs, a.e_rows, a.e_rs, r)) {
+        // bf16 rows of 16-byte words: the software-pipelined pass
+#define DSP_DP(G, H) hipLaunchKernelGGL((draft_pass_kernel<G, H>), g1, dim3(kDpThreads), 0, s, a)
+        if (greedy) { if (S) DSP_DP(true, true); else DSP_DP(true, false); }
+        else { if (S) DSP_DP(false, true); else DSP_DP(false, false); }
+#undef DSP_DP
     } else if (greedy && vec)
         hipLaunchKernelGGL((bias_pass_kernel<LT, kGreedy, true>), g1, dim3(256), 0, s, a);
     else if (greedy)

@@ -101,7 +101,51 @@ __device__ __forceinline__ void dp_stage_w2(const uint16_t* __restrict__ W2, int
     lds_barrier();   // the buffers are reused for the embedding tiles
 }
 
-template <bool GREEDY>
+// Raw buffer resources: a base in scalar registers, a 32-bit byte offset per
+// lane and a range the hardware checks -- a load at or past the range returns
+// zeros, a store there is dropped.  Rows past the end, bias rows that select
+// none and idle lanes thus take offsets out of range instead of address masks
+// and branches, and the per-block address arithmetic of the logit words is
+// scalar.  Every range here stays below 2^31 bytes (dp_offsets_fit), so
+// kBufOut lies outside all of them.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kBufWord3 = 0x00020000;       // raw access, 32-bit data format
+constexpr uint32_t kBufOut = 0x80000000u;
+
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufWord3);
+}
+
+// 16-byte loads: kBufNt streams (the logit words, read once)
+constexpr int kBufNt = 2;
+template <int AUX>
+__device__ __forceinline__ uint4 buf_load16(BufRsrc r, uint32_t off)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// the maximum of three values without the quieting of signalling NaNs that
+// fmaxf adds to operands it did not compute itself (values read back from LDS)
+__device__ __forceinline__ float max3_lds(float a, float b, float c)
+{
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
+// Whether a call's tensors fit the pass's 32-bit offsets: the 32 rows of a
+// block of logit words, and the bias table (whose row index also has to fit
+// the 24-bit multiply).
+__host__ __device__ inline bool dp_offsets_fit(RowStrides bs, int64_t e_rows, int64_t e_rs, int r)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    return bs.rs >= 0 && bs.ps >= 0 && (kPassBlock * bs.rs + kVocabTile) * 2 < lim &&
+           e_rows < ((int64_t)1 << 24) && ((e_rows - 1) * e_rs + r) * 2 < lim;
+}
+
+template <bool GREEDY, bool RNN>
 __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
 {
     __shared__ DraftPassLds L;
@@ -120,10 +164,6 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
     const int h = lane >> 5, c32 = lane & 31;
     const int V = a.V, r = a.r, gamma = a.gamma;
     const int v_lane = vt * kVocabTile + 32 * wave + 16 * h;   // first of this lane's 16 columns
-    // the partial of request n_begin + 4 w + l of block 0 (lanes l < 4 of wave w)
-    Part* __restrict__ pnext = a.part + (int64_t)(n_begin + 4 * wave + (lane & 3)) * a.n_vt + vt;
-    const int64_t pstep = (int64_t)kPassBlock * a.n_vt;
-    const uint16_t* __restrict__ base = static_cast<const uint16_t*>(a.base);
     const Itl itL = fold_itl(a.inv_temp);
 
     bf16x8 afrag[kKSteps];
@@ -133,83 +173,104 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
     // whole row segment per half-wave (lanes 32 g .. 32 g + 31 read the 32
     // consecutive 16-byte words of one row), so that an instruction reads two
     // rows' full cache lines.  Thread t handles rows 4 w + 2 c + (l / 32) of a
-    // block, c = 0, 1, word l % 32.
+    // block, c = 0, 1, word l % 32.  Rows past the end (the last block of the
+    // last chunk, and the blocks requested ahead past it) read zeros and their
+    // results are never stored: a request's partial depends on its own row only.
     const int sword = lane & 31;
     auto srow_of = [&](int c) { return 4 * wave + 2 * c + h; };
-    // Per staging row c of the thread, its request in block 0, the index of its
-    // previous token and the offset of its logit word.  The token and logit
-    // requests go out block by block in order, so each adds a workgroup-uniform
-    // running offset (no per-lane multiply in the loop).  Rows past the end read
-    // the last request's token and the -inf words.
-    const int vcol = vt * kVocabTile + 8 * sword;   // first column of this thread's word
-    const bool col_in = vcol + 8 <= V;
-    const int32_t* __restrict__ tsrc = (a.k == 0) ? a.anchor : a.tok;
-    const int tstep = kPassBlock * ((a.k == 0) ? 1 : gamma);            // R * gamma < 2^30
-    const int tlast = (a.k == 0) ? n_end - 1 : (n_end - 1) * gamma + (a.k - 1);
-    const int64_t lstep = (int64_t)kPassBlock * a.bs.rs;
-    int row0[2], tix0[2];
-    int64_t lof0[2];
+    const int kk = 8 * sword;                         // this thread's k-slice of a bias row
+    const int cols = min(kVocabTile, V - vt * kVocabTile);   // columns of this tile
+
+    // previous tokens: byte offsets of this thread's rows' tokens in block 0,
+    // advanced a block at a time (rows past the end fall past the array)
+    const int32_t* tsrc = (a.k == 0) ? a.anchor : a.tok;
+    const BufRsrc tok_rs = buf_rsrc(tsrc, (uint32_t)(a.R * ((a.k == 0) ? 1 : gamma)) * 4u);
+    const uint32_t tstep = (uint32_t)(kPassBlock * ((a.k == 0) ? 1 : gamma)) * 4u;   // R gamma < 2^30
+    uint32_t toff[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        row0[c] = n_begin + srow_of(c);
-        tix0[c] = (a.k == 0) ? row0[c] : row0[c] * gamma + (a.k - 1);
-        lof0[c] = (int64_t)row0[c] * a.bs.rs + (int64_t)a.k * a.bs.ps + vcol;
+        const int row = n_begin + srow_of(c);
+        toff[c] = (uint32_t)((a.k == 0) ? row : row * gamma + (a.k - 1)) * 4u;
     }
-    auto row_live = [&](int blk, int c) { return row0[c] + blk * kPassBlock < n_end; };
-    // the raw tokens of this thread's two staging rows in the next block in
-    // order (blk), validated where they are used
-    int tnext = 0;
-    // (recurrent head: the row of the bias table is the request itself)
-    auto prev_raw = [&](int blk, int (&p)[2]) {
+    auto prev_raw = [&](int (&p)[2]) {
+        if constexpr (!RNN) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-            p[c] = a.rnn ? row0[c] + blk * kPassBlock : tsrc[row_live(blk, c) ? tix0[c] + tnext : tlast];
-        tnext += tstep;
+            for (int c = 0; c < 2; ++c) {
+                p[c] = (int)__builtin_amdgcn_raw_buffer_load_b32(tok_rs, toff[c], 0, 0);
+                toff[c] += tstep;
+            }
+        }
     };
-    auto prev_ok = [&](int blk, int c, int p) -> bool {
-        return row_live(blk, c) && (unsigned)p < (unsigned)a.e_rows;
-    };
-    const int e_rs = (int)a.e_rs;             // bias-table row stride (<= 64 x 256)
-    const int kk = 8 * sword;                 // this thread's k-slice of an embedding row
-    const int kk_in = (kk < r) ? kk : 0;      // ... clamped into the row
+
+    // bias rows: row p of the table at p e_rs (the previous token; the request
+    // itself for the recurrent head); a row outside the table, or a k-slice
+    // past r, reads zeros
+    const BufRsrc e_rsc = buf_rsrc(a.E, (uint32_t)((((int64_t)a.e_rows - 1) * a.e_rs + r) * 2));
+    const uint32_t e_rs2 = (uint32_t)a.e_rs * 2u, kk2 = 2u * (uint32_t)kk;
+    const bool kk_ok = kk < r;
     uint4 eu[2];
     auto load_e = [&](int blk, const int (&p)[2]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            // a row index below 2^24 and a stride below 2^15 whose product stays
-            // below 2^31 (the library bounds both tables): a 24-bit multiply
-            const int prev = prev_ok(blk, c, p[c]) ? p[c] : 0;
-            eu[c] = *reinterpret_cast<const uint4*>(a.E + (__umul24(prev, e_rs) + kk_in));
+            const int row = RNN ? n_begin + blk * kPassBlock + srow_of(c) : p[c];
+            // row < 2^24 and e_rs2 < 2^16: a 24-bit multiply (product < 2^31)
+            const uint32_t off = ((unsigned)row < (unsigned)a.e_rows && kk_ok)
+                                     ? __umul24((uint32_t)row, e_rs2) + kk2 : kBufOut;
+            eu[c] = buf_load16<0>(e_rsc, off);
         }
     };
-    auto store_e = [&](int b, int blk, const int (&p)[2]) {
+    auto store_e = [&](int b) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            // a dead row or a k-slice past r stores zeros (masked, branch-free)
-            const uint32_t mk = (prev_ok(blk, c, p[c]) && kk < r) ? 0xFFFFFFFFu : 0u;
-            const uint4 v = eu[c];
-            *reinterpret_cast<uint4*>(&e_tile[b][srow_of(c)][kk]) =
-                make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
-        }
+        for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&e_tile[b][srow_of(c)][kk]) = eu[c];
     };
 
     // base logit words of a block (its rows' 256 columns of the tile) into ring
-    // slot sl; rows past the end and words past V read the -inf words
+    // slot sl (a compile-time index: the ring stays in registers).  The block's rows are one buffer based at its first row: each
+    // thread's offset is fixed and the range ends with the block's last live
+    // row, so that rows past the end read zeros; words past V (a last, partial
+    // tile) read whatever lies there and are replaced by -inf words when staged.
+    const uint16_t* __restrict__ base = static_cast<const uint16_t*>(a.base);
+    uint32_t loff[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) loff[c] = (uint32_t)(srow_of(c) * a.bs.rs + kk) * 2u;
+    const uint16_t* lblk = base + (int64_t)n_begin * a.bs.rs + (int64_t)a.k * a.bs.ps + vt * kVocabTile;
+    const int64_t lstep = (int64_t)kPassBlock * a.bs.rs;
+    int lfirst = n_begin;   // first request of the next block in order
     uint4 rs[kDpRing][2];
-    const uint16_t* neg = reinterpret_cast<const uint16_t*>(kNegInfWords);
-    int64_t lnext = 0;   // offset of the next block in order (blk)
-    auto load_raw = [&](int blk, int sl) {
+    auto load_raw = [&](auto SLc) {
+        constexpr int sl = decltype(SLc)::value;
+        const int live = min(kPassBlock, n_end - lfirst);   // <= 0 past the end
+        const uint32_t bytes = (live > 0) ? (uint32_t)(((int64_t)(live - 1) * a.bs.rs + cols) * 2) : 0u;
+        const BufRsrc rb = buf_rsrc(lblk, bytes);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint16_t* p = (row_live(blk, c) && col_in) ? base + (lof0[c] + lnext) : neg;
-            rs[sl][c] = load_nt16(p);
+        for (int c = 0; c < 2; ++c) rs[sl][c] = buf_load16<kBufNt>(rb, loff[c]);
+        lblk += lstep;
+        lfirst += kPassBlock;
+    };
+    const bool col_in = kk < cols;
+    auto store_lg = [&](auto SLc) {
+        constexpr int sl = decltype(SLc)::value, b = sl;
+        if (cols < kVocabTile) {   // a partial tile (workgroup-uniform)
+            // a blend with a mask: a select of whole words would become a load
+            // through a selected address and move the ring to scratch memory
+            constexpr uint32_t kNinf2 = 0xFF80FF80u;   // two bf16 -inf
+            const uint32_t keep = col_in ? 0xFFFFFFFFu : 0u, put = kNinf2 & ~keep;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                uint4& v = rs[sl][c];
+                v = make_uint4((v.x & keep) | put, (v.y & keep) | put, (v.z & keep) | put, (v.w & keep) | put);
+            }
         }
-        lnext += lstep;
-    };
-    auto store_lg = [&](int b, int sl) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&L.s.lg[b][srow_of(c)][8 * sword]) = rs[sl][c];
+        for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&L.s.lg[b][srow_of(c)][kk]) = rs[sl][c];
     };
+
+    // partials: lanes 0..3 of wave w store requests 4 w .. 4 w + 3 of a block
+    // (every lane merges request 4 w + l % 4; the others store out of range, as
+    // do rows past the end)
+    const uint32_t poff = (lane < 4) ? (uint32_t)((4 * wave + lane) * a.n_vt) * 16u : kBufOut;
+    Part* pblk = a.part + (int64_t)n_begin * a.n_vt + vt;
+    const int64_t pstep = (int64_t)kPassBlock * a.n_vt;
 
     // logits of a block from its staged base logits and bias, and their lane
     // maximum
@@ -236,8 +297,8 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
             float mw[kDpWaves];
 #pragma unroll
             for (int w = 0; w < kDpWaves; ++w) mw[w] = mx[b][w][c32];
-            mt = fmaxf(fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3])),
-                       fmaxf(fmaxf(mw[4], mw[5]), fmaxf(mw[6], mw[7])));
+            mt = max3_lds(max3_lds(mw[0], mw[1], mw[2]), max3_lds(mw[3], mw[4], mw[5]),
+                          fmaxf(mw[6], mw[7]));
             mref = (mt == -INFINITY) ? 0.0f : mt;   // an all-masked tile
         }
     };
@@ -245,25 +306,33 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
     // prologue: blocks 0 and 1 staged (embedding rows and logits), block 0's
     // logits formed and its tile maximum taken; block 2's embedding rows,
     // block 3's tokens and the logit words of blocks 2 and 3 in flight
+    constexpr std::integral_constant<int, 0> kSl0{};
+    constexpr std::integral_constant<int, 1> kSl1{};
     floatx16 acc;
-    int p2[2], p3[2];   // raw tokens of blocks i + 2 and i + 3
+    int p3[2] = {0, 0};   // raw tokens of block i + 3 (the Markov head)
     {
-        int p0[2], p1[2];
-        prev_raw(0, p0);
-        prev_raw(1, p1);
-        prev_raw(2, p2);
+        int p0[2] = {0, 0}, p1[2] = {0, 0}, p2[2] = {0, 0};
+        prev_raw(p0);
+        prev_raw(p1);
+        prev_raw(p2);
         load_e(0, p0);
-        load_raw(0, 0);
-        load_raw(1, 1);
-        store_e(0, 0, p0);
+        load_raw(kSl0);
+        load_raw(kSl1);
+        store_e(0);
         load_e(1, p1);
-        store_lg(0, 0);
-        store_lg(1, 1);
-        load_raw(2, 0);
-        load_raw(3, 1);
-        store_e(1, 1, p1);
+        store_lg(kSl0);
+        store_lg(kSl1);
+        store_e(1);
+        // the last requests in the order an iteration makes them (words, then
+        // embedding rows, tokens, words of the next block), so that the loop is
+        // entered with the same loads in flight as it carries round
+        load_raw(kSl0);   // block 2
+        __builtin_amdgcn_sched_barrier(0);
         load_e(2, p2);
-        prev_raw(3, p3);
+        prev_raw(p3);
+        __builtin_amdgcn_sched_barrier(0);
+        load_raw(kSl1);   // block 3
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         const uint16_t* eb = &e_tile[0][c32][8 * h];
         acc = floatx16{};
@@ -335,24 +404,22 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
         } else {
             res = Part{mt, 0, xsum<32>(c)};
         }
-        store_e(b, i + 2, p2);   // rows past the end store zeros
-        store_lg(b, sl);         // block i + 2's logits
+        store_e(b);              // block i + 2's embedding rows
+        store_lg(SL);            // block i + 2's logits
         if (h == 0) red[b][wave][c32] = res;
         if (more) logits(b ^ 1, acc);
         lds_barrier();
 
         // [C]
         load_e(i + 3, p3);       // block i + 3's embedding rows
-        p2[0] = p3[0];
-        p2[1] = p3[1];
-        prev_raw(i + 4, p3);     // block i + 4's tokens
+        prev_raw(p3);            // block i + 4's tokens
         // the loads above are due before the logit words below: keep them ahead
         // in issue order (the load counter is in-order)
         __builtin_amdgcn_sched_barrier(0);
-        load_raw(i + 4, sl);     // block i + 4's logit words
-        // lanes 0..3 of wave w merge requests 4 w .. 4 w + 3 of the block
-        const int j = 4 * wave + lane;
-        if (lane < 4 && n0 + j < n_end) {
+        load_raw(SL);            // block i + 4's logit words
+        // every lane merges request 4 w + l % 4 of the block; lanes 0..3 store it
+        {
+            const int j = 4 * wave + (lane & 3);
             Part p = red[b][0][j];
 #pragma unroll
             for (int w = 1; w < kDpWaves; ++w) {
@@ -365,15 +432,25 @@ __global__ __launch_bounds__(kDpThreads, 1) void draft_pass_kernel(PassArgs a)
                     p.s += q.s;   // one reference (the tile maximum) throughout
                 }
             }
-            *pnext = p;
+            const int live = min(kPassBlock, n_end - n0);
+            const BufRsrc rp = buf_rsrc(pblk, (uint32_t)(((int64_t)(live - 1) * a.n_vt + 1) * sizeof(Part)));
+            const uint64_t sb = (uint64_t)__double_as_longlong(p.s);
+            const u32x4 pw = {__float_as_uint(p.m), (uint32_t)p.idx, (uint32_t)sb, (uint32_t)(sb >> 32)};
+            __builtin_amdgcn_raw_buffer_store_b128(pw, rp, poff, 0, 0);
         }
-        pnext += pstep;
+        pblk += pstep;
         if (more) tile_max(b ^ 1);
     };
-    for (int i = 0; i < n_blk; i += 2) {
+    // Whole pairs in the loop and an odd last block after it: with the second
+    // half conditional inside the loop, the compiler also sees a path from the
+    // first half straight back to the loop head, where the words that half has
+    // just requested would be consumed, and waits for every load in flight.
+    int i = 0;
+    for (; i + 1 < n_blk; i += 2) {
         iter(i, std::integral_constant<int, 0>{});
-        if (i + 1 < n_blk) iter(i + 1, std::integral_constant<int, 1>{});
+        iter(i + 1, std::integral_constant<int, 1>{});
     }
+    if (i < n_blk) iter(i, std::integral_constant<int, 0>{});
 }
 
 }  // namespace dsp

@@ -169,27 +169,32 @@ __global__ __launch_bounds__(kDpThreads, 1) void resid_pass_kernel(PassArgs a, R
 
     // prologue: blocks 0 and 1 staged, block 0's logits formed; the records of
     // blocks 2 and 3, block 2's bias rows and words, the statistics of blocks 0
-    // and 1 loaded
+    // and 1 requested
     floatx16 acc;
     {
         // (the row offsets hold one block: each block's records are loaded right
         // before its words are requested)
-        load_st(0, 0);
-        load_st(1, 1);
         load_meta(0, 0);
         load_e(0, 0);
         load_raw(0);
+        load_meta(1, 1);
         store_e(0, 0, 0);
         store_lg(0);
-        load_meta(1, 1);
         load_e(1, 1);
         load_raw(1);
+        load_st(0, 0);
+        load_meta(2, 0);
         store_e(1, 1, 1);
         store_lg(1);
-        load_meta(2, 0);
-        load_raw(2);
+        // the last requests in the order an iteration makes them, so that the
+        // loop is entered with the same loads in flight as it carries round
+        __builtin_amdgcn_sched_barrier(0);
         load_e(2, 0);
+        load_raw(2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_st(1, 1);
         load_meta(3, 1);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         const uint16_t* eb = &e_tile[0][c32][8 * h];
         acc = floatx16{};
@@ -263,10 +268,15 @@ __global__ __launch_bounds__(kDpThreads, 1) void resid_pass_kernel(PassArgs a, R
             a.part[(int64_t)(n0 + j) * a.n_vt + vt] = p;
         }
     };
-    for (int i = 0; i < n_blk; i += 2) {
+    // whole pairs in the loop and an odd last block after it (a conditional
+    // second half would give the compiler a path back to the loop head on which
+    // it waits for every load in flight)
+    int i = 0;
+    for (; i + 1 < n_blk; i += 2) {
         iter(i, std::integral_constant<int, 0>{});
-        if (i + 1 < n_blk) iter(i + 1, std::integral_constant<int, 1>{});
+        iter(i + 1, std::integral_constant<int, 1>{});
     }
+    if (i < n_blk) iter(i, std::integral_constant<int, 0>{});
 }
 
 }  // namespace dsp

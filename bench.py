@@ -41,6 +41,7 @@ DRAFT_SOURCES = ("draft_sampling_lossless_markov_amd/build.py",
                  "draft_sampling_lossless_markov_amd/csrc/draft.hip",
                  "draft_sampling_lossless_markov_amd/csrc/draft_run.h",
                  "draft_sampling_lossless_markov_amd/csrc/draft_pass.h",
+                 "draft_sampling_lossless_markov_amd/csrc/draft_pass_wide.h",
                  "draft_sampling_lossless_markov_amd/csrc/tile_pass.h",
                  "draft_sampling_lossless_markov_amd/csrc/bias_tile.h",
                  "draft_sampling_lossless_markov_amd/csrc/dsp_device.h",
@@ -379,7 +380,7 @@ def measure(wl, mode, args, steps, warmup, with_cpu, log_prefix=""):
     traffic = profiled_traffic(wl.name, draft_path)
     kernels = ("run_clear_kernel + draft_run_kernel (one persistent launch, all gamma positions)"
                if draft_path == "persistent" else
-               "draft_pass_kernel + draft_pick_kernel per position")
+               "draft_pass_wide_kernel + draft_pick_kernel per position")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": f"dsp_draft_step, {g} positions: {kernels}",

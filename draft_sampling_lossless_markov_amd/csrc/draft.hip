@@ -19,6 +19,7 @@
 
 #include "bias_tile.h"
 #include "draft_pass.h"
+#include "draft_pass_wide.h"
 #include "draft_run.h"
 #include "dsp_device.h"
 #include "dsp_launch.h"
@@ -193,7 +194,7 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     const bool vec = rows_vec(bs, V, 8);
     if (sizeof(LT) == 2 && vec && dp_offsets_fit(bs, a.e_rows, a.e_rs, r)) {
         // bf16 rows of 16-byte words: the software-pipelined pass
-#define DSP_DP(G, H) hipLaunchKernelGGL((draft_pass_kernel<G, H>), g1, dim3(kDpThreads), 0, s, a)
+#define DSP_DP(G, H) hipLaunchKernelGGL((draft_pass_wide_kernel<G, H>), g1, dim3(kDwThreads), 0, s, a)
         if (greedy) { if (S) DSP_DP(true, true); else DSP_DP(true, false); }
         else { if (S) DSP_DP(false, true); else DSP_DP(false, false); }
 #undef DSP_DP

@@ -134,7 +134,7 @@ dsp_status dsp_workspace_status(dsp_ws_kind which, const void* ws, size_t ws_byt
  * "DeepSeek DSpark 技术解析" section 四: only the token id is passed forward).
  *
  * For each request n:
- *   prev     = anchor[n] if k == 0 else tok[n, k-1]   (prev < 0: no bias)
+ *   prev     = anchor[n] if k == 0 else tok[n, k-1]   (prev outside [0, V): no bias)
  *   logit_v  = base[n, k, v] + sum_i E[prev, i] * W2[v, i]   (fp32)
  *   greedy (temperature == 0): tok[n,k] = argmax_v logit_v (lowest index on
  *     ties), q[n,k] = 1, stats[n,k] = (max logit, 0)
@@ -244,7 +244,8 @@ dsp_status dsp_draft_step_noalloc(const void* base, dsp_dtype dtype, int64_t bas
  *
  *   y       = sum_{i<d} w[i] h[n,k,i] + sum_{i<r} w[d+i] E[prev,i]   (fp64)
  *   c[n,k]  = 1 / (1 + exp(-(y + offset[n]) / T[k]))   rounded to fp32
- * prev = anchor[n] for k = 0, tok[n, k-1] otherwise (prev < 0 drops the E term).
+ * prev = anchor[n] for k = 0, tok[n, k-1] otherwise (prev outside [0, V) drops the
+ * E term).
  *
  * h [R, gamma, d] bf16; E [V, r] bf16; anchor [R]; tok [R, gamma];
  * w [d + r] f32; T [gamma] f32 (> 0); offset [R] f32 or NULL; c [R, gamma] f32.

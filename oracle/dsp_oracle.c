@@ -115,7 +115,8 @@ static double ulp32(float x)
 /* Markov head [P4-SEQ], [P2-SA]: biased logits of one draft row.            */
 /*   bias_v  = sum_i E[prev, i] * W2(i, v)   (exact-order fp64, one rounding) */
 /*   logit_v = fl32(base_v + fl32(bias_v))                                    */
-/* W2(i, v) is stored at W2[v * r + i].  prev < 0 means "no Markov bias".    */
+/* W2(i, v) is stored at W2[v * r + i].  A prev outside [0, V) (-1 before   */
+/* any token) selects no embedding row: "no Markov bias".                    */
 /* absdot[v] (optional) receives sum_i |E[prev,i] * W2(i,v)|, the magnitude   */
 /* that bounds any fp32 summation-order difference of the bias.              */
 /* ------------------------------------------------------------------------- */
@@ -127,7 +128,7 @@ int orc_markov_logits(int V, int r, const void* base_row, int dtype,
     if (V <= 0 || r <= 0) return 1;
     for (int v = 0; v < V; ++v) {
         double s = 0.0, sa = 0.0;
-        if (prev >= 0) {
+        if (prev >= 0 && prev < V) {
             for (int i = 0; i < r; ++i) {
                 const double t = (double)bf16_to_float(E[(size_t)prev * r + i]) *
                                  (double)bf16_to_float(W2[(size_t)v * r + i]);
@@ -368,7 +369,8 @@ int orc_draft(int n, int gamma, int V, int r,
 /* Confidence head + sequential temperature scaling [P4-2.1].                */
 /*   y   = sum_{i<d} w_i h[k,i] + sum_{i<r} w_{d+i} E[prev,i]   (fp64)        */
 /*   c_k = 1 / (1 + exp(-(y + offset) / T_k))                                */
-/* prev = anchor for k = 0, else x_{k-1}; prev < 0 drops the E term.         */
+/* prev = anchor for k = 0, else x_{k-1}; prev outside [0, V) drops the E   */
+/* term.                                                                     */
 /* flag = 1 when c lies within 1e-12 (relative) of an fp32 rounding          */
 /* midpoint, i.e. fp32 rounding of a differently ordered sum may differ.     */
 /* ------------------------------------------------------------------------- */
@@ -387,7 +389,7 @@ int orc_confidence(int n, int gamma, int d, int V, int r,
             double y = 0.0;
             for (int t = 0; t < d; ++t)
                 y += (double)w[t] * (double)bf16_to_float(h[ik * (size_t)d + t]);
-            if (prev >= 0)
+            if (prev >= 0 && prev < V)
                 for (int t = 0; t < r; ++t)
                     y += (double)w[d + t] * (double)bf16_to_float(E[(size_t)prev * r + t]);
             if (offset) y += (double)offset[i];
@@ -707,7 +709,7 @@ int orc_confidence_logit(int n, int gamma, int d, int V, int r,
             double y = 0.0;
             for (int t = 0; t < d; ++t)
                 y += (double)w[t] * (double)bf16_to_float(h[ik * (size_t)d + t]);
-            if (prev >= 0)
+            if (prev >= 0 && prev < V)
                 for (int t = 0; t < r; ++t)
                     y += (double)w[d + t] * (double)bf16_to_float(E[(size_t)prev * r + t]);
             if (offset) y += (double)offset[i];

@@ -301,6 +301,40 @@ def test_no_markov_bias_and_zero_lengths():
     assert np.all(g["len"] == 0) and g["B"][0] == 40
 
 
+def test_streaming_pass_previous_tokens_outside_the_vocabulary():
+    """Anchors of -1 and at or past V select no bias row: the streaming pass (range
+    checks of its buffer loads) and the persistent launch agree with the oracle,
+    on a ragged request block, a partial last tile and r < 256."""
+    R, gamma, V, r = 70, 3, 1000, 24
+    wl = custom(R, gamma, V, r, 8, torch.bfloat16)
+    inp_cpu = make_inputs(wl, 0, layout="position")
+    anchor = inp_cpu["anchor"].clone()
+    anchor[0::5] = -1
+    anchor[1::5] = V
+    anchor[2::5] = V + 5
+    anchor[3::7] = 2 ** 30
+    inp_cpu["anchor"] = anchor
+    inp = to_dev(inp_cpu)
+    for temp in (0.9, 0.0):
+        _say(f"previous tokens outside the vocabulary, T={temp}")
+        rd = Round(R, gamma, V, r)
+        S = np.arange(R, dtype=np.int32)
+        o_tok, o_q, o_stats, o_flag = orc.draft(orc.host_logits(inp_cpu["base"]),
+                                                orc.bf16_bits(inp_cpu["E"]),
+                                                orc.bf16_bits(inp_cpu["W2"]),
+                                                np_(inp_cpu["anchor"]), S, temp, SEED, 0)
+        for flags in (dsp.DSP_PATH_STREAMING, dsp.DSP_PATH_PERSISTENT):
+            tok, q, st = _draft_all(inp, rd, temp, 0, flags=flags)
+            t, _ = compare_draft(tok, q, st, o_tok, o_q, o_stats, o_flag, temp == 0.0, S)
+            assert t.ok(), (flags, t.summary())
+            if temp == 0.0:
+                assert t.diverged == 0, (flags, t.summary())
+            else:
+                AGG.add(Tally(decisions=t.decisions, flagged=t.flagged, diverged=t.diverged))
+        del rd
+    torch.cuda.empty_cache()
+
+
 def test_determinism_and_replay():
     wl = custom(70, 5, 1000, 24, 100, torch.bfloat16)
     inp = to_dev(make_inputs(wl, 1))

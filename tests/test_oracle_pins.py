@@ -194,6 +194,23 @@ def test_markov_bias_is_rank_r_contraction(orc):
         np.testing.assert_array_equal(lg, expect)
 
 
+def test_markov_out_of_vocabulary_prev_is_no_bias(orc):
+    """A previous token outside [0, V) selects no embedding row: its logits are the
+    base logits, bit for bit, as for prev = -1 (and the confidence head drops the
+    E term); a valid prev does add its bias."""
+    rng = np.random.default_rng(2)
+    V, r = 9, 8
+    E = bf16(rng.normal(0, 0.5, (V, r)))
+    W2 = bf16(rng.normal(0, 0.5, (V, r)))
+    base = rng.normal(0, 1, V).astype(np.float32)
+    for prev in (-1, -7, V, V + 3, 2 ** 30):
+        lg, ad = orc.markov_logits(base, E, W2, prev=prev)
+        np.testing.assert_array_equal(lg, base)
+        assert np.all(ad == 0.0)
+    lg, _ = orc.markov_logits(base, E, W2, prev=V - 1)
+    assert not np.array_equal(lg, base)
+
+
 # ---------------------------------------------------------------------------
 # Token selection: reductions to library routines
 # ---------------------------------------------------------------------------

@@ -35,14 +35,14 @@ namespace dsp {
 // and the embedding row are requested before the W2 fetch so their latencies
 // overlap.
 // ---------------------------------------------------------------------------
-template <typename LT, bool GREEDY, int PER>
+template <typename LT, bool GREEDY, int PER, bool SUB>
 __global__ __launch_bounds__(256, 4) void draft_pick_kernel(
     const LT* __restrict__ base, RowStrides bs, const uint16_t* __restrict__ E,
     const uint16_t* __restrict__ W2,
     const int32_t* __restrict__ anchor, int32_t* __restrict__ tok, float* __restrict__ q,
     double* __restrict__ stats, int R, int gamma, int V, int r, int k, float inv_temp,
     uint64_t seed, uint32_t round, int n_vt, const Part* __restrict__ part,
-    const uint16_t* __restrict__ S)
+    const float4* __restrict__ sub, const uint16_t* __restrict__ S)
 {
     __shared__ PickScratch sh;
     const int n = blockIdx.x;
@@ -93,10 +93,44 @@ __global__ __launch_bounds__(256, 4) void draft_pick_kernel(
         double before;
         const int tsel = block_locate<PER>(w, target, &before, sh, 0);
 
-        // rebuild the chosen tile's 256 logits (thread t: column tsel * 256 + t)
+        const float m_t = pp[tsel].m;   // the tile's reference in the partial
+        const double f = rescale64(m_t, M, inv_temp);
+        // SUB: the quarter of the tile whose cumulative mass crosses the target,
+        // from the pass's four 64-column sums (the first with positive mass that
+        // crosses, else the last with positive mass); only it is rebuilt
+        int v0 = tsel * kVocabTile, width = kVocabTile;
+        double before_t = before;
+        if constexpr (SUB) {
+            const float4 sw = sub[(int64_t)tsel * R + n];   // tile-major
+            const float sv[4] = {sw.x, sw.y, sw.z, sw.w};
+            int js = -1, jl = 0;
+            double cum = before, cj = before, cl = before;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double wj = (double)sv[j] * f;
+                if (js < 0 && wj > 0.0 && cum + wj > target) {
+                    js = j;
+                    cj = cum;
+                }
+                if (wj > 0.0) {
+                    jl = j;
+                    cl = cum;
+                }
+                cum += wj;
+            }
+            if (js < 0) {
+                js = jl;
+                cj = cl;
+            }
+            v0 += 64 * js;
+            width = 64;
+            before_t = cj;
+        }
+        // rebuild the chosen columns' logits (thread t: column v0 + t, t < width)
         const LT* row = base + (int64_t)n * bs.rs + (int64_t)k * bs.ps;
-        const int v = tsel * kVocabTile + tid;
-        const float xb = (v < V) ? Logit<LT>::at(row, v) : -INFINITY;
+        const int v = v0 + tid;
+        const bool in_tile = tid < width;
+        const float xb = (v < V && in_tile) ? Logit<LT>::at(row, v) : -INFINITY;
         if (tid < kRankMax / 8) {
             // the bias row: E[x_{k-1}] (Markov head) or the state S[n, k]
             const uint16_t* er = S ? S + ((int64_t)n * gamma + k) * r
@@ -106,17 +140,16 @@ __global__ __launch_bounds__(256, 4) void draft_pick_kernel(
             if (er && kk < r) ev = *reinterpret_cast<const uint4*>(er + kk);
             *reinterpret_cast<uint4*>(e_row + kk) = ev;
         }
-        const float m_t = pp[tsel].m;   // the tile's reference in the partial
-        const float z = tile_logit(W2, V, r, tsel * kVocabTile, e_row, xb, sh);
+        const float z = SUB ? sub_logit(W2, V, r, v0, e_row, xb, sh)
+                            : tile_logit(W2, V, r, v0, e_row, xb, sh);
         // the pass's own weights: relative to the tile maximum, moved onto the
         // row's reference by the partials' fp64 factor
         const float mref = (m_t == -INFINITY) ? 0.0f : m_t;
-        double e1[1] = {(v < V) ? (double)wexp(z - mref, fold_itl(inv_temp)) * rescale64(m_t, M, inv_temp)
-                                : 0.0};
+        double e1[1] = {(v < V && in_tile) ? (double)wexp(z - mref, fold_itl(inv_temp)) * f : 0.0};
         double b2;
-        const int loc = block_locate<1>(e1, target - before, &b2, sh, 1);
+        const int loc = block_locate<1>(e1, target - before_t, &b2, sh, 1);
         if (tid == loc) {
-            tok[out] = tsel * kVocabTile + loc;
+            tok[out] = v0 + loc;
             q[out] = (float)(e1[0] / Z);
             stats[2 * out] = M;
             stats[2 * out + 1] = Z;
@@ -130,13 +163,15 @@ __global__ __launch_bounds__(256, 4) void draft_pick_kernel(
 constexpr size_t kRunCtlBytes = 256;
 
 // partials of either path (the streaming path's 256-column tiles, 16 bytes each,
-// or a persistent run's tiles: two positions' slots of two 8-byte words), then
-// the error word
+// then the pipelined pass's four 64-column sums per tile, 16 bytes each; or a
+// persistent run's tiles: two positions' slots of two 8-byte words), then the
+// error word
 static size_t draft_part_bytes(int R, int V)
 {
     const size_t n_vt = (size_t)((V + kVocabTile - 1) / kVocabTile);
     const size_t n_run = std::min<size_t>((size_t)((V + 31) / 32), (size_t)kRunTilesMax);
-    const size_t b = (size_t)R * std::max(n_vt * sizeof(Part), n_run * 4 * sizeof(uint64_t));
+    const size_t b = (size_t)R * std::max(n_vt * (sizeof(Part) + sizeof(float4)),
+                                          n_run * 4 * sizeof(uint64_t));
     return (b + 255) / 256 * 256;
 }
 
@@ -161,10 +196,17 @@ template <typename LT, bool GREEDY, int PER>
 static void launch_pick(const LT* base, RowStrides bs, const uint16_t* E, const uint16_t* W2,
                         const int32_t* anchor, int32_t* tok, float* q, double* stats, int R,
                         int gamma, int V, int r, int k, float it, uint64_t seed, uint32_t round,
-                        int n_vt, const Part* part, const uint16_t* S, hipStream_t s)
+                        int n_vt, const Part* part, const float4* sub, const uint16_t* S,
+                        hipStream_t s)
 {
-    hipLaunchKernelGGL((draft_pick_kernel<LT, GREEDY, PER>), dim3(R), dim3(256), 0, s, base, bs, E, W2,
-                       anchor, tok, q, stats, R, gamma, V, r, k, it, seed, round, n_vt, part, S);
+    if (sub)
+        hipLaunchKernelGGL((draft_pick_kernel<LT, GREEDY, PER, true>), dim3(R), dim3(256), 0, s, base, bs,
+                           E, W2, anchor, tok, q, stats, R, gamma, V, r, k, it, seed, round, n_vt, part,
+                           sub, S);
+    else
+        hipLaunchKernelGGL((draft_pick_kernel<LT, GREEDY, PER, false>), dim3(R), dim3(256), 0, s, base, bs,
+                           E, W2, anchor, tok, q, stats, R, gamma, V, r, k, it, seed, round, n_vt, part,
+                           sub, S);
 }
 
 template <typename LT>
@@ -192,7 +234,13 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     a.ctl = ctl;
     const dim3 g1(n_vt, (R + a.req_per_wg - 1) / a.req_per_wg);
     const bool vec = rows_vec(bs, V, 8);
-    if (sizeof(LT) == 2 && vec && dp_offsets_fit(bs, a.e_rows, a.e_rs, r)) {
+    const bool piped = sizeof(LT) == 2 && vec && dp_offsets_fit(bs, a.e_rows, a.e_rs, r);
+    // the pipelined pass's 64-column sums (sampling, tile-major [n_vt, R]), after
+    // the partials
+    float4* sub = (piped && !greedy)
+                      ? reinterpret_cast<float4*>(part + (size_t)R * n_vt) : nullptr;
+    a.sub = sub;
+    if (piped) {
         // bf16 rows of 16-byte words: the software-pipelined pass
 #define DSP_DP(G, H) hipLaunchKernelGGL((draft_pass_wide_kernel<G, H>), g1, dim3(kDwThreads), 0, s, a)
         if (greedy) { if (S) DSP_DP(true, true); else DSP_DP(true, false); }
@@ -211,9 +259,9 @@ static hipError_t launch_draft_t(const LT* base, RowStrides bs, const uint16_t* 
     const int per = (n_vt + 255) / 256;
 #define DSP_PICK(P)                                                                              \
     (greedy ? launch_pick<LT, true, P>(base, bs, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, \
-                                       it, seed, round, n_vt, part, S, s)                        \
+                                       it, seed, round, n_vt, part, sub, S, s)                   \
             : launch_pick<LT, false, P>(base, bs, E, W2, anchor, tok, q, stats, R, gamma, V, r, k, \
-                                        it, seed, round, n_vt, part, S, s))
+                                        it, seed, round, n_vt, part, sub, S, s))
     if (per <= 1) DSP_PICK(1);
     else if (per <= 2) DSP_PICK(2);
     else if (per <= 4) DSP_PICK(4);

@@ -196,6 +196,7 @@ __global__ __launch_bounds__(kDwThreads, 1) void draft_pass_wide_kernel(PassArgs
 
     // partials: lanes 0..7 of wave w store requests 8 w .. 8 w + 7 of a block
     const uint32_t poff = (lane < 8) ? (uint32_t)((8 * wave + lane) * a.n_vt) * 16u : kBufOut;
+    const uint32_t qoff = (lane < 8) ? (uint32_t)(8 * wave + lane) * 16u : kBufOut;
     Part* pblk = a.part + (int64_t)n_begin * a.n_vt + vt;
     const int64_t pstep = (int64_t)kPassBlock * a.n_vt;
 
@@ -370,9 +371,13 @@ __global__ __launch_bounds__(kDwThreads, 1) void draft_pass_wide_kernel(PassArgs
         __builtin_amdgcn_sched_barrier(0);
         load_raw(SL);            // block i + 4's logit words
         // every lane merges request 8 w + l % 8 of the block; lanes 0..7 store it
+        // and (sampling) the four waves' 64-column sums, which let the pick
+        // rebuild one 64-column quarter of the chosen tile instead of all of it
         {
             const int j = 8 * wave + (lane & 7);
             Part p = red[b][0][j];
+            float sq[kDwWaves];
+            sq[0] = (float)p.s;
 #pragma unroll
             for (int w = 1; w < kDwWaves; ++w) {
                 const Part q = red[b][w][j];
@@ -382,13 +387,25 @@ __global__ __launch_bounds__(kDwThreads, 1) void draft_pass_wide_kernel(PassArgs
                     p.idx = am.i;
                 } else {
                     p.s += q.s;   // one reference (the tile maximum) throughout
+                    sq[w] = (float)q.s;
                 }
             }
             const int live = min(kPassBlock, n_end - n0);
-            const BufRsrc rp = buf_rsrc(pblk, (uint32_t)(((int64_t)(live - 1) * a.n_vt + 1) * sizeof(Part)));
+            const uint32_t pbytes = (uint32_t)(((int64_t)(live - 1) * a.n_vt + 1) * sizeof(Part));
+            const BufRsrc rp = buf_rsrc(pblk, pbytes);
             const uint64_t sb = (uint64_t)__double_as_longlong(p.s);
             const u32x4 pw = {__float_as_uint(p.m), (uint32_t)p.idx, (uint32_t)sb, (uint32_t)(sb >> 32)};
             __builtin_amdgcn_raw_buffer_store_b128(pw, rp, poff, 0, 0);
+            if constexpr (!GREEDY) {
+                // the sums tile-major (sub[vt R + n]): a block's 32 requests are
+                // one contiguous 512-byte run; a null array is a zero range
+                // (every store dropped)
+                const BufRsrc rq = a.sub ? buf_rsrc(a.sub + (int64_t)vt * a.R + n0, (uint32_t)live * 16u)
+                                         : buf_rsrc(pblk, 0u);
+                const u32x4 qw = {__float_as_uint(sq[0]), __float_as_uint(sq[1]), __float_as_uint(sq[2]),
+                                  __float_as_uint(sq[3])};
+                __builtin_amdgcn_raw_buffer_store_b128(qw, rq, qoff, 0, 0);
+            }
         }
         pblk += pstep;
         if (more) tile_max(b ^ 1);

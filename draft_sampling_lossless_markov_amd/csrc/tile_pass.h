@@ -136,6 +136,8 @@ struct PassArgs {
     float inv_temp;
     int n_vt, req_per_wg;
     Part* part;              // [R, n_vt] (kResidual: [queue slot, n_vt])
+    float4* sub;             // [n_vt, R] or null: a sampling tile's four 64-column sums
+                             // (fp32, relative to the tile maximum), for the pick
     unsigned* ctl;           // error word of the call's workspace, set to 0 by the
                              // first pass of a call (nullptr: left alone)
     int row_by_entry;        // kResidual: row_m / row_z indexed by queue slot (else by request)
@@ -690,6 +692,54 @@ __device__ __forceinline__ float tile_logit(const uint16_t* __restrict__ W2, int
     }
     lds_barrier();
     return xb + sh.lg[threadIdx.x];
+}
+
+// One request's logits over the 64 columns at v0 (thread t < 64: column v0 + t),
+// bit-identical to tile_logit and the passes (each column the same MFMA sequence):
+// waves 0 and 1 run M-tiles 0 and 1 of the 64-block (the rows a_row_voff
+// places), waves 2 and 3 only meet the barriers.  Same conventions as
+// tile_logit; threads 64.. get the logit of column v0 + t % 64.
+__device__ __forceinline__ float sub_logit(const uint16_t* __restrict__ W2, int V, int r, int v0,
+                                           const uint16_t* e_row, float xb, PickScratch& sh)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = lane >> 5, c32 = lane & 31;
+    constexpr int kHalf = kKSteps / 2;
+    const bool live = wave < 2;   // wave-uniform
+    const uint16_t* wrow = W2 + (int64_t)min(v0 + a_row_voff(wave & 1, c32), V - 1) * r;
+    uint4 af[kHalf];
+    auto fetch = [&](int half) {
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i)
+            af[i] = *reinterpret_cast<const uint4*>(wrow + min((half * kHalf + i) * kKStep + 8 * h, r - 8));
+    };
+    if (live) fetch(0);
+    lds_barrier();   // e_row is written
+    if (live) {
+        floatx16 acc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (half == 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(1);
+            }
+#pragma unroll
+            for (int i = 0; i < kHalf; ++i) {
+                const int ks = half * kHalf + i;
+                uint4 u = make_uint4(0, 0, 0, 0);
+                if (c32 == 0) u = *reinterpret_cast<const uint4*>(e_row + ks * kKStep + 8 * h);
+                acc = mfma32_bf16(as_bf16x8(af[i]), as_bf16x8(u), acc);
+            }
+        }
+        if (c32 == 0) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sh.lg[32 * h + 16 * wave + j] = acc[j];
+        }
+    }
+    lds_barrier();
+    return xb + sh.lg[threadIdx.x & 63];
 }
 
 }  // namespace dsp

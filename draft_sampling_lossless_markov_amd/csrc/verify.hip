@@ -99,8 +99,13 @@ __device__ __forceinline__ int clamp_len(const int32_t* len, int n, int gamma)
 // row is reduced.  Wave w covers tiles [32 sp + 8 w, +8): lanes 8i .. 8i+7 own
 // tile i of the wave, 32 values each (load k reads columns k*64 + 8*(l%8) .. +7
 // of the tile, so each load instruction moves eight whole 128-byte runs).
+// VEC (rows of whole 16-byte words): every load is one unconditional 16-byte
+// load from the row or, past V, from the -inf words, so the compiler keeps the
+// next row's loads in flight while the current row is reduced; a load behind a
+// branch (the per-element path, or the drafted token's logit) made it wait for
+// them before every reduction.
 // ---------------------------------------------------------------------------
-template <typename LT, bool GREEDY>
+template <typename LT, bool GREEDY, bool VEC>
 __global__ __launch_bounds__(256) void verify_rows_kernel(
     const LT* __restrict__ target, RowStrides ts, const int32_t* __restrict__ tok,
     const int32_t* __restrict__ len, int R, int gamma, int V, float inv_temp, int n_vt,
@@ -116,19 +121,49 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
         ws.run_ctl[0] = ctl0;
     }
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
-    const bool vec_ok = rows_vec(ts, V, Logit<LT>::kVecAlign);
     const int n = blockIdx.x / spans;
     const int sp = blockIdx.x - n * spans;
     const int l = clamp_len(len, n, gamma);
     const int t = sp * kSpanTiles + wave * 8 + (lane >> 3);
     const int sub = lane & 7;
 
+    // VEC: row j through a buffer resource of the whole row (a row past l has a
+    // zero range: the loads are still issued, read nothing and return zeros),
+    // each lane at fixed offsets; words past V read zeros and become -inf words
+    // in the last span
+    const bool tail_span = (sp + 1) * kSpanTiles * kVocabTile > V;   // workgroup-uniform
     auto load_row = [&](int j, uint4 (&raw)[4][RW]) {
-        const LT* row = target + (int64_t)n * ts.rs + (int64_t)j * ts.ps;
+        if constexpr (VEC) {
+            const LT* row = target + (int64_t)n * ts.rs + (int64_t)min(j, l) * ts.ps;
+            const BufRsrc rr = buf_rsrc(row, (j <= l) ? (uint32_t)V * (uint32_t)sizeof(LT) : 0u);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int v0 = t * kVocabTile + k * 64 + sub * 8;
-            Logit<LT>::load8_raw(row, min(v0, V), V, vec_ok && v0 + 8 <= V, raw[k]);
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t off = (uint32_t)(t * kVocabTile + k * 64 + sub * 8) * (uint32_t)sizeof(LT);
+#pragma unroll
+                for (int w = 0; w < RW; ++w) raw[k][w] = buf_load16<kBufNt>(rr, off + 16u * w);
+            }
+        } else {
+            const LT* row = target + (int64_t)n * ts.rs + (int64_t)j * ts.ps;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int v0 = t * kVocabTile + k * 64 + sub * 8;
+                Logit<LT>::load8_raw(row, min(v0, V), V, false, raw[k]);
+            }
+        }
+    };
+    auto mask_tail = [&](uint4 (&raw)[4][RW]) {
+        if (VEC && tail_span) {
+            const uint32_t ninf = (sizeof(LT) == 2) ? 0xFF80FF80u : 0xFF800000u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool in = t * kVocabTile + k * 64 + sub * 8 < V;   // whole words: in or past V
+                const uint32_t keep = in ? 0xFFFFFFFFu : 0u, put = ninf & ~keep;
+#pragma unroll
+                for (int w = 0; w < RW; ++w) {
+                    uint4& u = raw[k][w];
+                    u = make_uint4((u.x & keep) | put, (u.y & keep) | put, (u.z & keep) | put, (u.w & keep) | put);
+                }
+            }
         }
     };
     auto reduce_row = [&](int j, const uint4 (&raw)[4][RW]) {
@@ -149,12 +184,13 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
                 b.i = __shfl_xor(am.i, o, kWave);
                 am = argmax_merge(am, b);
             }
-            if (sub == 0 && t < n_vt) out[t] = Part{am.v, am.i, 0.0};
+            const Part pt{am.v, am.i, 0.0};
             // the wave's 8 tiles (lane groups) combined: one partial per wave
             ArgMax b8;
             b8.v = __shfl_xor(am.v, 8, kWave);
             b8.i = __shfl_xor(am.i, 8, kWave);
             am = xargmax<32>(xargmax<16>(argmax_merge(am, b8)));
+            if (sub == 0 && t < n_vt) out[t] = pt;
             if (lane == 0)
                 ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{am.v, am.i, 0.0};
         } else {
@@ -176,7 +212,7 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
             double s = sum_w64(x, mref, itL);
 #pragma unroll
             for (int o = 1; o < 8; o <<= 1) s += __shfl_xor(s, o, kWave);
-            if (sub == 0 && t < n_vt) out[t] = Part{m, 0, s};
+            const Part pt{m, 0, s};
             // the wave's 8 tiles (lane groups) rescaled to their max and summed:
             // one partial per wave (an fp32 factor: these partials only give each
             // row's normaliser, to ~1e-7; the draws use the tile partials and rescans)
@@ -185,25 +221,36 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
             double sw = (m == -INFINITY) ? 0.0 : s * (double)wexp(m - mw, itL);
             sw += __shfl_xor(sw, 8, kWave);
             sw = xsum<32>(xsum<16>(sw));
+            // (ordinary exec-masked stores: a buffer store whose every lane falls out
+            // of range -- a wave of tiles past V -- upset the in-order load
+            // counter the compiler's waits assume, measured as wrong row sums)
+            if (sub == 0 && t < n_vt) out[t] = pt;
             if (lane == 0)
                 ws.spanpart[(((int64_t)n * (gamma + 1) + j) * spans + sp) * 4 + wave] = Part{mw, 0, sw};
-            if (tid == 0 && j < l) {
-                const int xj = tok[(int64_t)n * gamma + j];
-                const int lo = sp * kSpanTiles * kVocabTile;
-                if (xj >= lo && xj < min(V, lo + kSpanTiles * kVocabTile))
-                    ws.zx[(int64_t)n * gamma + j] =
-                        Logit<LT>::at(target + (int64_t)n * ts.rs + (int64_t)j * ts.ps, xj);
-            }
         }
     };
     uint4 ra[4][RW], rb[4][RW];
     load_row(0, ra);
     for (int j = 0; j <= l; j += 2) {
-        if (j + 1 <= l) load_row(j + 1, rb);
+        // VEC: unconditional requests (a row past l reads nothing)
+        if (VEC || j + 1 <= l) load_row(j + 1, rb);
+        mask_tail(ra);
         reduce_row(j, ra);
         if (j + 1 > l) break;
-        if (j + 2 <= l) load_row(j + 2, ra);
+        if (VEC || j + 2 <= l) load_row(j + 2, ra);
+        mask_tail(rb);
         reduce_row(j + 1, rb);
+    }
+    // sampling: the target logit at each drafted token of this span (thread j,
+    // row j), for the accept test
+    if constexpr (!GREEDY) {
+        const int j = tid;
+        if (j < l) {
+            const int xj = tok[(int64_t)n * gamma + j];
+            const int lo = sp * kSpanTiles * kVocabTile;
+            if (xj >= lo && xj < min(V, lo + kSpanTiles * kVocabTile))
+                ws.zx[(int64_t)n * gamma + j] = Logit<LT>::at(target + (int64_t)n * ts.rs + (int64_t)j * ts.ps, xj);
+        }
     }
 }
 
@@ -525,8 +572,12 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
     const dim3 g1((unsigned)items);
     if (path == kPathPersistent && !std::is_same<LT, uint16_t>::value) return hipErrorNotSupported;
     if (greedy) {
-        hipLaunchKernelGGL((verify_rows_kernel<LT, true>), g1, dim3(256), 0, s, target, ts, tok, len,
-                           R, gamma, V, it, n_vt, ws, 0u);
+        if (rows_vec(ts, V, Logit<LT>::kVecAlign))
+            hipLaunchKernelGGL((verify_rows_kernel<LT, true, true>), g1, dim3(256), 0, s, target, ts, tok, len,
+                               R, gamma, V, it, n_vt, ws, 0u);
+        else
+            hipLaunchKernelGGL((verify_rows_kernel<LT, true, false>), g1, dim3(256), 0, s, target, ts, tok,
+                               len, R, gamma, V, it, n_vt, ws, 0u);
         launch_accept<true>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed,
                             round, n_vt, ws, s, 0, rnn);
         return hipGetLastError();
@@ -539,8 +590,12 @@ static hipError_t launch_verify_t(const LT* target, RowStrides ts, const LT* bas
         run = !S && path != kPathStream && rows_vec(bs, V, 8) && rows_vec(ts, V, 8) && R <= kRunReqMax &&
               run_geometry(V, &geo);
     if (path == kPathPersistent && !run) return hipErrorNotSupported;
-    hipLaunchKernelGGL((verify_rows_kernel<LT, false>), g1, dim3(256), 0, s, target, ts, tok, len, R,
-                       gamma, V, it, n_vt, ws, (run && give_up) ? 1u : 0u);
+    if (rows_vec(ts, V, Logit<LT>::kVecAlign))
+        hipLaunchKernelGGL((verify_rows_kernel<LT, false, true>), g1, dim3(256), 0, s, target, ts, tok, len,
+                           R, gamma, V, it, n_vt, ws, (run && give_up) ? 1u : 0u);
+    else
+        hipLaunchKernelGGL((verify_rows_kernel<LT, false, false>), g1, dim3(256), 0, s, target, ts, tok, len,
+                           R, gamma, V, it, n_vt, ws, (run && give_up) ? 1u : 0u);
     launch_accept<false>(anchor, V, tok, q, len, accept, n_accept, y, p, R, gamma, it, seed, round,
                          n_vt, ws, s, run ? geo.n_t : 0, rnn);
     if constexpr (std::is_same<LT, uint16_t>::value) {
@@ -749,8 +804,12 @@ static hipError_t launch_tv_t(const LT* target, RowStrides ts, const LT* base, R
                        R, gamma, V, ws, S ? 1 : 0);
     const int spans = (n_vt + kSpanTiles - 1) / kSpanTiles;
     const int64_t items = (int64_t)R * spans;
-    hipLaunchKernelGGL((verify_rows_kernel<LT, false>), dim3((unsigned)items), dim3(256), 0, s, target,
-                       ts, tok, ws.lens, R, gamma, V, it, n_vt, ws.v, 0u);
+    if (rows_vec(ts, V, Logit<LT>::kVecAlign))
+        hipLaunchKernelGGL((verify_rows_kernel<LT, false, true>), dim3((unsigned)items), dim3(256), 0, s,
+                           target, ts, tok, ws.lens, R, gamma, V, it, n_vt, ws.v, 0u);
+    else
+        hipLaunchKernelGGL((verify_rows_kernel<LT, false, false>), dim3((unsigned)items), dim3(256), 0, s,
+                           target, ts, tok, ws.lens, R, gamma, V, it, n_vt, ws.v, 0u);
     const int np = 4 * spans;
     const int per = (np + kWave - 1) / kWave;
     const dim3 gw((unsigned)((N + 3) / 4));

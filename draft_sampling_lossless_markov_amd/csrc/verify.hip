@@ -763,7 +763,8 @@ __global__ __launch_bounds__(256) void tv_rowstats_kernel(int R, int gamma, int 
     }
 }
 
-// one wave per entry: alpha = 1 - (sum of the tiles' residual mass)
+// one wave per entry: alpha = 1 - (sum of the tiles' residual mass); lane l adds
+// tiles l, l + 64, ..., so that each load reads 64 consecutive partials
 template <int PER>
 __global__ __launch_bounds__(256) void tv_combine_kernel(int R, int gamma, int n_vt, TvWs ws,
                                                          double* __restrict__ alpha)
@@ -775,7 +776,7 @@ __global__ __launch_bounds__(256) void tv_combine_kernel(int R, int gamma, int n
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int t = lane * PER + i;
+        const int t = i * kWave + lane;
         if (t < n_vt) s += pp[t].s;
     }
     s = wave_sum_d(s);

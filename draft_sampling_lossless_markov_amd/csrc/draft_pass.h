@@ -1,8 +1,8 @@
 // draft_pass.h -- shared pieces of the software-pipelined streaming passes (gfx950):
 // the W2 fragment layout and its staging through swizzled LDS, raw buffer
 // resources with hardware range checks, and the launch-time check that a call
-// fits their 32-bit offsets.  The draft pass (draft_pass_wide.h, one wave per
-// SIMD) and the residual pass (resid_pass.h, eight waves) build on them.
+// fits their 32-bit offsets.  The draft pass (draft_pass_wide.h, two workgroups
+// per CU) and the residual pass (resid_pass.h, eight waves) build on them.
 //
 // A pass holds its workgroup's W2 tile in registers as MFMA A fragments and
 // streams request blocks of 32: a block's base logits and embedding rows are
@@ -110,13 +110,14 @@ __device__ __forceinline__ float max3_lds(float a, float b, float c)
 }
 
 // Whether a call's tensors fit the pass's 32-bit offsets: the 32 rows of a
-// block of logit words, and the bias table (whose row index also has to fit
-// the 24-bit multiply).
+// block of logit words, and the bias table, whose row index and row stride in
+// bytes also have to fit the 24-bit multiply and whose offsets (row e_rows
+// included, the out-of-range row) stay below 2^31 bytes.
 __host__ __device__ inline bool dp_offsets_fit(RowStrides bs, int64_t e_rows, int64_t e_rs, int r)
 {
-    const int64_t lim = (int64_t)1 << 31;
+    const int64_t lim = (int64_t)1 << 31, lim24 = (int64_t)1 << 24;
     return bs.rs >= 0 && bs.ps >= 0 && (kPassBlock * bs.rs + kVocabTile) * 2 < lim &&
-           e_rows < ((int64_t)1 << 24) && ((e_rows - 1) * e_rs + r) * 2 < lim;
+           e_rows < lim24 && e_rs >= r && e_rs * 2 < lim24 && e_rows * e_rs * 2 < lim;
 }
 
 }  // namespace dsp

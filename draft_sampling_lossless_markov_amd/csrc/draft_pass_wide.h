@@ -246,6 +246,12 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
         constexpr int b = decltype(Bc)::value;
         const uint16_t* eb = &e_tile[b][c32][8 * h];
         floatx16 acc0 = floatx16{}, acc1 = floatx16{};
+        // from here to the merge after the barrier the wave runs at raised issue
+        // priority (the weights drop it): the other workgroup's wave on the SIMD
+        // then fills its own weights into this wave's gaps rather than holding
+        // back the chain, logits and maxima that all four waves of this
+        // workgroup wait for at the barrier
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < kKSteps; ++ks) {
             const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(eb + ks * kKStep));
@@ -351,6 +357,7 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
         load_e(i + 2, p);        // block i + 2's embedding rows
         prev_raw(p);             // block i + 3's tokens
         merge(i - 1, pr);
+        __builtin_amdgcn_s_setprio(0);
         block_part(Bc, mw);
     };
     // whole pairs in the loop and an odd last block after it

@@ -17,10 +17,11 @@
 // Lane l holds request l % 32 of a block and, in tile t, the 16 contiguous
 // columns [64 w + 32 t + 16 (l / 32), +16) (dp_arow maps MFMA rows to columns
 // as for one 32-column tile).  Iteration i, one barrier: block i + 1's staged
-// rows to LDS, block i + 2's logit words requested, block i's MFMA chain,
+// rows to LDS, block i + 2's logit words requested, block i's MFMA chain
+// (sampling: block i - 1's last 16 weights among it, then its partial),
 // logits, lane and wave maxima; barrier; block i + 2's embedding rows and block
 // i + 3's tokens requested, block i - 1's partials merged and stored, block i's
-// tile maximum taken and its weights summed.  All global traffic uses raw
+// tile maximum taken and its first 16 weights summed.  All global traffic uses raw
 // buffer instructions (draft_pass.h): rows past the end, bias rows that select
 // none and idle lanes take out-of-range offsets, and a block's logit-word
 // addresses are scalar.  Every logit is the same MFMA sequence (k-steps 0..15
@@ -239,10 +240,30 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
         }
     };
 
-    // one block: its MFMA chain over e_tile[b], its logits (slot s: tile s / 16,
-    // column s % 16) and lane maximum, and (sampling) the wave maximum to mx[b]
+    // Sampling: a block's weights are summed in two halves -- slots 0..15 after
+    // the barrier that publishes its maxima, slots 16..31 among the next block's
+    // MFMAs, whose chain otherwise leaves the wave's VALU idle -- in two fp64
+    // chains (even and odd slots, each in slot order).  Carried from one block
+    // to the next: the last 16 logits, the reference, the tile maximum and the
+    // two chains' sums.
+    float zh[16], mh = 0.0f, mth = -INFINITY;
+    double hc0 = 0.0, hc1 = 0.0;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) zh[s] = -INFINITY;
+    // the previous block's partial, once its second half is summed
+    auto put_part = [&](auto Pc) {
+        if constexpr (!GREEDY) {
+            const Part res{mth, 0, xsum<32>(hc0 + hc1)};
+            if (h == 0) red[decltype(Pc)::value][wave][c32] = res;
+        }
+    };
+
+    // one block: its MFMA chain over e_tile[b] (sampling: the previous block's
+    // second half of weights among it, its partial to red[Pc]), its logits (slot
+    // s: tile s / 16, column s % 16) and lane maximum, and (sampling) the wave
+    // maximum to mx[b]
     float z[32], m = -INFINITY;
-    auto block_logits = [&](auto Bc) {
+    auto block_logits = [&](auto Bc, auto Pc) {
         constexpr int b = decltype(Bc)::value;
         const uint16_t* eb = &e_tile[b][c32][8 * h];
         floatx16 acc0 = floatx16{}, acc1 = floatx16{};
@@ -256,8 +277,24 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
         for (int ks = 0; ks < kKSteps; ++ks) {
             const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(eb + ks * kKStep));
             acc0 = mfma32_bf16(afrag[0][ks], bf, acc0);
+            if constexpr (!GREEDY) {
+                const double w = (double)wexp(zh[ks] - mh, itL);   // slot 16 + ks
+                if (ks & 1) hc1 += w; else hc0 += w;
+            }
             acc1 = mfma32_bf16(afrag[1][ks], bf, acc1);
         }
+        if constexpr (!GREEDY) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (ks + 1 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
+        }
+        put_part(Pc);
         uint4 lw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -295,24 +332,28 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
             ArgMax am{m, v < V ? v : 0x7fffffff};
             am = xargmax<32>(am);
             res = Part{am.v, am.i, 0.0};
+            if (h == 0) red[b][wave][c32] = res;
         } else {
+            // the first half of the weights (the second is summed among the next
+            // block's MFMAs), in groups of eight kept apart for the scheduler
             const float mt = fmaxf(max3_lds(mw[0], mw[1], mw[2]), mw[3]);
             const float mref = (mt == -INFINITY) ? 0.0f : mt;
-            // the weights in groups of eight kept apart for the scheduler, summed
-            // in fp64 in two chains (even and odd slots)
-            double c0 = 0.0, c1 = 0.0;
+            hc0 = 0.0;
+            hc1 = 0.0;
 #pragma unroll
-            for (int g = 0; g < 32; g += 8) {
+            for (int g = 0; g < 16; g += 8) {
 #pragma unroll
                 for (int s = g; s < g + 8; s += 2) {
-                    c0 += (double)wexp(z[s] - mref, itL);
-                    c1 += (double)wexp(z[s + 1] - mref, itL);
+                    hc0 += (double)wexp(z[s] - mref, itL);
+                    hc1 += (double)wexp(z[s + 1] - mref, itL);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            res = Part{mt, 0, xsum<32>(c0 + c1)};
+#pragma unroll
+            for (int s = 0; s < 16; ++s) zh[s] = z[16 + s];
+            mh = mref;
+            mth = mt;
         }
-        if (h == 0) red[b][wave][c32] = res;
     };
 
     constexpr std::integral_constant<int, 0> kB0{};
@@ -344,7 +385,7 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
         store_lg(Nc);            // last read before the previous barrier
         load_raw();              // block i + 2's logit words
         __builtin_amdgcn_sched_barrier(0);
-        block_logits(Bc);
+        block_logits(Bc, Nc);
         lds_barrier();
         // this block's wave maxima and the last block's partials, read together
         float mw[kDwWaves] = {};
@@ -367,6 +408,14 @@ __global__ __launch_bounds__(kDwThreads, 2) void draft_pass_wide_kernel(PassArgs
         iter(i + 1, kB1, kB0);
     }
     auto last_merge = [&](int j, auto Bc) {
+        if constexpr (!GREEDY) {   // the last block's second half of weights
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const double w = (double)wexp(zh[s] - mh, itL);
+                if (s & 1) hc1 += w; else hc0 += w;
+            }
+            put_part(Bc);
+        }
         lds_barrier();
         Part pr[kDwWaves];
 #pragma unroll

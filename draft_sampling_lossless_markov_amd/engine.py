@@ -1,8 +1,12 @@
 """One DSpark decode round on the GPU: gamma draft steps, the confidence head,
-the prefix scheduler and verification, issued back to back on one stream.
+the prefix scheduler and verification.
 
 The Round object owns the output tensors and the two workspaces (allocated once,
 reused every round) and calls the C-ABI in order; it does no arithmetic itself.
+With overlap, the confidence head and the scheduler run on a second stream while
+the last position is drafted: the head at position k reads the draft token of
+position k - 1 only, so the last position's token is first read by verification,
+and the outputs are those of the calls in order.
 """
 from __future__ import annotations
 
@@ -35,10 +39,11 @@ class Round:
         self.ws_verify = torch.zeros(max(1, dsp.dsp_workspace_size(dsp.DSP_WS_VERIFY, R, gamma, V, r)),
                                      dtype=torch.uint8, device=dev)
 
-    def draft(self, inp, temperature, seed, rnd, stream=None):
+    def draft(self, inp, temperature, seed, rnd, stream=None, k=0, n_steps=None):
+        n_steps = self.gamma - k if n_steps is None else n_steps
         dsp.dsp_draft_step(inp["base"], inp["E"], inp["W2"], inp["anchor"], self.tok, self.q,
-                           self.stats, 0, temperature, seed, rnd, self.ws_draft, stream,
-                           n_steps=self.gamma)
+                           self.stats, k, temperature, seed, rnd, self.ws_draft, stream,
+                           n_steps=n_steps)
 
     def confidence(self, inp, stream=None):
         dsp.dsp_confidence(inp["h"], inp["E"], inp["anchor"], self.tok, inp["w"], inp["T"],
@@ -69,9 +74,23 @@ class Round:
         dsp.dsp_workspace_status(dsp.DSP_WS_DRAFT, self.ws_draft, *args, stream=stream)
         dsp.dsp_workspace_status(dsp.DSP_WS_VERIFY, self.ws_verify, *args, stream=stream)
 
-    def run(self, inp, temperature, seed, rnd, mode=None, tau0=None, stream=None):
-        self.draft(inp, temperature, seed, rnd, stream)
-        self.confidence(inp, stream)
-        self.schedule(inp, mode, tau0, stream)
+    def run(self, inp, temperature, seed, rnd, mode=None, tau0=None, stream=None, overlap=False):
+        if not overlap or self.gamma < 2:
+            self.draft(inp, temperature, seed, rnd, stream)
+            self.confidence(inp, stream)
+            self.schedule(inp, mode, tau0, stream)
+        else:
+            s = torch.cuda.current_stream() if stream is None else stream
+            if not hasattr(self, "side"):
+                self.side = torch.cuda.Stream(device=self.tok.device)
+                self.fork, self.join = torch.cuda.Event(), torch.cuda.Event()
+            self.draft(inp, temperature, seed, rnd, s, k=0, n_steps=self.gamma - 1)
+            self.fork.record(s)
+            self.side.wait_event(self.fork)
+            self.confidence(inp, self.side)
+            self.schedule(inp, mode, tau0, self.side)
+            self.draft(inp, temperature, seed, rnd, s, k=self.gamma - 1, n_steps=1)
+            self.join.record(self.side)
+            s.wait_event(self.join)
         self.verify(inp, temperature, seed, rnd, stream)
         return self

@@ -372,6 +372,39 @@ def test_graph_capture_replays_match_eager(temp):
             assert np.array_equal(np_(getattr(rd, k)), ref[k]), (rep, k)
 
 
+@pytest.mark.parametrize("temp", [1.0, 0.0])
+@pytest.mark.parametrize("shape", [(70, 5, 1000, 24), (300, 4, 70000, 256)])
+def test_overlapped_round_matches_serial(temp, shape):
+    """The round with the confidence head and the scheduler on a second stream while
+    the last position is drafted (persistent and streaming draft paths): eagerly, and
+    captured in a graph and replayed between other rounds, it reproduces the calls in
+    order bit for bit."""
+    R, g, V, r = shape
+    wl = custom(R, g, V, r, 100, torch.bfloat16)
+    inp = to_dev(make_inputs(wl, 3))
+    rd = Round(R, g, V, r)
+    keys = ("tok", "q", "stats", "c", "len", "a", "B", "accept", "n_accept", "y", "p")
+    rd.run(inp, temp, 7, 11)
+    torch.cuda.synchronize()
+    ref = {k: np_(getattr(rd, k)).copy() for k in keys}
+    rd.run(inp, temp, 7, 30)                    # other outputs in the buffers
+    rd.run(inp, temp, 7, 11, overlap=True)
+    torch.cuda.synchronize()
+    for k in keys:
+        assert np.array_equal(np_(getattr(rd, k)), ref[k]), ("eager", k)
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        rd.run(inp, temp, 7, 11, stream=cap, overlap=True)
+    for rep in range(3):
+        rd.run(inp, temp, 7, 40 + rep, overlap=True)   # different work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert np.array_equal(np_(getattr(rd, k)), ref[k]), (rep, k)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, stage by stage on sampled requests
 # ---------------------------------------------------------------------------

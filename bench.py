@@ -2,8 +2,9 @@
 
 One step = one decode round over a batch of synthetic inputs already resident in
 HBM: dsp_draft_step (all gamma positions), dsp_confidence, dsp_schedule, dsp_verify, as
-Round.run issues them: dsp_confidence and dsp_schedule on a second stream while the last
-position is drafted (they read no token of it), the rest in order on one stream.  A workload without scheduling (every position verified)
+Round.run issues them: with the streaming draft, dsp_confidence and dsp_schedule on a
+second stream while the last position is drafted (they read no token of it), the rest in
+order on one stream.  A workload without scheduling (every position verified)
 has no consumer for the confidence head: its round is dsp_draft_step + dsp_verify with
 l_r = gamma set once, and dsp_confidence and dsp_schedule are timed in a loop of their
 own for the per-entry-point breakdown.  The throughput (`value`) times K rounds replayed
@@ -296,15 +297,18 @@ def measure(wl, mode, args, steps, warmup, with_cpu, log_prefix=""):
         timing = "eager launches"
         round_ms = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(K)])
     else:
-        # the round as Round.run issues it: with the scheduler on, the confidence
-        # head and the scheduler on a second stream while the last position is
-        # drafted (outputs identical to the calls in order)
+        # the round as Round.run issues it: with the scheduler on and the streaming
+        # draft, the confidence head and the scheduler on a second stream while the
+        # last position is drafted (outputs identical to the calls in order; the
+        # persistent draft runs all positions in one launch, and splitting it
+        # costs more than the overlap saves)
+        overlap = scheduled and draft_path == "streaming"
         cap = torch.cuda.Stream()
         graphs = []
         for i in range(K):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr, stream=cap):
-                if scheduled:
+                if overlap:
                     rd.run(sets[(warmup + i) % len(sets)], temp, seed, warmup + i, stream=cap,
                            overlap=True)
                 else:
@@ -323,7 +327,7 @@ def measure(wl, mode, args, steps, warmup, with_cpu, log_prefix=""):
         round_ms = np.array([t_ev[i].elapsed_time(t_ev[i + 1]) for i in range(K)])
         timing = ("HIP graph replay, one graph per round" +
                   ("; confidence and scheduler on a second stream during the last draft position"
-                   if scheduled else ""))
+                   if overlap else ""))
         rd.check()
         del graphs
 

@@ -6,7 +6,9 @@ reused every round) and calls the C-ABI in order; it does no arithmetic itself.
 With overlap, the confidence head and the scheduler run on a second stream while
 the last position is drafted: the head at position k reads the draft token of
 position k - 1 only, so the last position's token is first read by verification,
-and the outputs are those of the calls in order.
+and the outputs are those of the calls in order.  It pays with the streaming draft
+(one launch pair per position); the persistent draft runs every position in one
+launch, and splitting that launch costs more than the overlap saves.
 """
 from __future__ import annotations
 

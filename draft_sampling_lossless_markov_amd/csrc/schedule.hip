@@ -24,7 +24,6 @@ namespace dsp {
 namespace {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / kWave;
-constexpr int kSchedItems = kSchedMaxCand / kSchedThreads;   // largest chunk of a thread
 constexpr int kRadixBits = 8;
 constexpr int kBuckets = 1 << kRadixBits;
 
@@ -42,18 +41,11 @@ struct SortLds {
 
 // Stable LSD radix sort (4 passes of 8 bits) of candidate indices idx[cur][0..N)
 // by the key ~bits(a[idx]): a descending, then index ascending.  Wave w owns a
-// contiguous segment of the current order and takes it 64 elements a round; a
-// lane's rank among the round's lanes of its digit comes from ballots, and the
-// last lane of each digit advances the wave's count for it, so every element
-// learns its offset within (digit, wave) without atomics (survival values near
-// one share their high digits, and LDS atomics on one bucket serialise).  The
-// offsets of (digit, wave) are laid out digit-major, wave-minor, which keeps
-// segment order; the scatter adds them to the offsets kept in registers.
-// Deterministic.  Returns the buffer holding the sorted order.  Called by the
-// whole workgroup.
+// contiguous segment of the current order; offsets are laid out (digit, wave) so
+// segment order is kept; ranks inside a wave come from ballots (deterministic).
+// Returns the buffer holding the sorted order.  Called by the whole workgroup.
 __device__ int sort_desc(const float* a_s, uint16_t (&idx_s)[2][kSchedMaxCand], int N, SortLds& L)
 {
-    constexpr int kRounds = kSchedMaxCand / kSchedThreads;   // rounds of 64 per wave, at most
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int seg = ((N + kSchedWaves - 1) / kSchedWaves + kWave - 1) / kWave * kWave;
     const int seg_begin = min(N, wave * seg);
@@ -61,29 +53,11 @@ __device__ int sort_desc(const float* a_s, uint16_t (&idx_s)[2][kSchedMaxCand], 
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int cur = 0;
     for (int shift = 0; shift < 32; shift += kRadixBits) {
-        // (the previous pass's last reads of this wave's row were its own)
         for (int b = lane; b < kBuckets; b += kWave) L.hist[wave][b] = 0;
-        uint32_t loc[kRounds];   // offset within (digit, wave) | digit << 16
-        uint16_t ids[kRounds];
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-            const int e = seg_begin + k * kWave + lane;
-            if (seg_begin + k * kWave >= seg_end) break;   // wave-uniform
-            const bool valid = e < seg_end;
-            const uint16_t id = valid ? idx_s[cur][e] : 0;
-            const uint32_t dgt = valid ? (sort_key(a_s[id]) >> shift) & (kBuckets - 1) : 0;
-            uint64_t same = __ballot(valid);
-#pragma unroll
-            for (int bit = 0; bit < kRadixBits; ++bit) {
-                const uint64_t bb = __ballot((dgt >> bit) & 1u);
-                same &= ((dgt >> bit) & 1u) ? bb : ~bb;
-            }
-            const uint32_t rank = (uint32_t)__popcll(same & lanes_below);
-            const uint32_t cnt = (uint32_t)__popcll(same);
-            const uint32_t base = valid ? L.hist[wave][dgt] : 0u;
-            if (valid && rank + 1 == cnt) L.hist[wave][dgt] = base + cnt;
-            loc[k] = (base + rank) | (dgt << 16);
-            ids[k] = id;
+        __syncthreads();
+        for (int e = seg_begin + lane; e < seg_end; e += kWave) {
+            const uint32_t dgt = (sort_key(a_s[idx_s[cur][e]]) >> shift) & (kBuckets - 1);
+            atomicAdd(&L.hist[wave][dgt], 1u);
         }
         __syncthreads();
         if (tid < kBuckets) {
@@ -112,15 +86,29 @@ __device__ int sort_desc(const float* a_s, uint16_t (&idx_s)[2][kSchedMaxCand], 
             for (int e = 0; e < 4; ++e) { L.digit_tot[4 * lane + e] = run; run += v[e]; }
         }
         __syncthreads();
-        // scatter: (digit, wave) start = digit start + the waves' counts before
+        if (tid < kBuckets) {
+            const uint32_t b = L.digit_tot[tid];
+            for (int w = 0; w < kSchedWaves; ++w) L.hist[w][tid] += b;
+        }
+        __syncthreads();
+        // scatter, one 64-element round at a time in segment order
+        for (int e0 = seg_begin; e0 < seg_end; e0 += kWave) {
+            const int e = e0 + lane;
+            const bool valid = e < seg_end;
+            const uint16_t id = valid ? idx_s[cur][e] : 0;
+            const uint32_t dgt = valid ? (sort_key(a_s[id]) >> shift) & (kBuckets - 1) : 0;
+            uint64_t same = __ballot(valid);
 #pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-            const int e = seg_begin + k * kWave + lane;
-            if (seg_begin + k * kWave >= seg_end) break;   // wave-uniform
-            if (e < seg_end) {
-                const uint32_t dgt = loc[k] >> 16;
-                idx_s[cur ^ 1][L.digit_tot[dgt] + L.hist[wave][dgt] + (loc[k] & 0xFFFFu)] = ids[k];
+            for (int bit = 0; bit < kRadixBits; ++bit) {
+                const uint64_t bb = __ballot((dgt >> bit) & 1u);
+                same &= ((dgt >> bit) & 1u) ? bb : ~bb;
             }
+            const uint32_t rank = (uint32_t)__popcll(same & lanes_below);
+            const uint32_t cnt = (uint32_t)__popcll(same);
+            uint32_t base = 0;
+            if (valid) base = L.hist[wave][dgt];
+            if (valid) idx_s[cur ^ 1][base + rank] = id;
+            if (valid && rank + 1 == cnt) L.hist[wave][dgt] = base + cnt;
         }
         __syncthreads();
         cur ^= 1;
@@ -196,25 +184,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     // 3-4. Q48 prefix sums in sorted order and the first non-rising Theta
     const int items = (N + kSchedThreads - 1) / kSchedThreads;
     const int p0 = tid * items;
-    // the SPS values of the chunk's comparisons (sps[R + p - 1], p = p0 .. p0 +
-    // items), requested together before the prefix sums rather than one round trip
-    // per step of the scan
-    float sp[kSchedItems + 1];
-#pragma unroll
-    for (int k = 0; k <= kSchedItems; ++k) {
-        const int q = R + p0 + k - 1;
-        sp[k] = (k <= items && q < B_max) ? sps[q] : 0.0f;
-    }
     uint64_t S = chunk_prefix(a_s, idx_s[cur], N, S0, p0, items, wave_tot);
     const double inv_scale = 1.0 / 281474976710656.0;
-#pragma unroll
-    for (int k = 0; k < kSchedItems; ++k) {
-        const int p = p0 + k;
-        if (k >= items || p >= N) break;
+    for (int p = p0; p < min(N, p0 + items); ++p) {
         if (R + p + 1 > B_max) { atomicMin(&stop_at, p); break; }
         const uint64_t S_next = S + q48(a_s[idx_s[cur][p]]);
-        const double th_prev = ((double)S * inv_scale) * (double)sp[k];
-        const double th = ((double)S_next * inv_scale) * (double)sp[k + 1];
+        const double th_prev = ((double)S * inv_scale) * (double)sps[R + p - 1];
+        const double th = ((double)S_next * inv_scale) * (double)sps[R + p];
         if (!(th > th_prev)) { atomicMin(&stop_at, p); break; }
         S = S_next;
     }
@@ -280,20 +256,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_async_kernel(
     int cur = sort_desc(a_s, idx_s, N, sl);
     const int items = (N + kSchedThreads - 1) / kSchedThreads;
     const int p0 = tid * items;
-    // the chunk's SPS values (sps[R + p], p = p0 .. p0 + items - 1), requested together
-    float sp[kSchedItems];
-#pragma unroll
-    for (int k = 0; k < kSchedItems; ++k) sp[k] = (k < items && p0 + k < n_max) ? sps[R + p0 + k] : 0.0f;
     uint64_t S = chunk_prefix(a_s, idx_s[cur], N, S0, p0, items, wave_tot);
     // Theta_0 (nothing admitted) on thread 0, then Theta_n for n = p + 1 of the chunk
     ThetaBest b{-1.0, 0x7fffffff};
     if (tid == 0) b = ThetaBest{((double)S0 * inv_scale) * (double)sps[R - 1], 0};
-#pragma unroll
-    for (int k = 0; k < kSchedItems; ++k) {
-        const int p = p0 + k;
-        if (k >= items || p >= n_max) break;
+    for (int p = p0; p < min(n_max, p0 + items); ++p) {
         S += q48(a_s[idx_s[cur][p]]);
-        b = theta_better(b, ThetaBest{((double)S * inv_scale) * (double)sp[k], p + 1});
+        b = theta_better(b, ThetaBest{((double)S * inv_scale) * (double)sps[R + p], p + 1});
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {

@@ -227,6 +227,32 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
         const int k = a.k0 + s;
         uint64_t* slots = a.slots + (int64_t)(k & 1) * R * n_t * 2;
 
+        // base words of this lane's request: its two 8-column words of each unit.
+        // Ordinary cached loads: the two lanes of a request read 32 bytes of a row
+        // per instruction and the next instruction the rest of its 64-byte
+        // segment, which a streaming (non-temporal) load would fetch again.  The
+        // words do not depend on the tokens, so the first block's are requested
+        // before the wait for them.  (V is a multiple of 8 here: a word lies
+        // wholly inside the row or wholly past it and then reads as -inf.)
+        constexpr int RING = (TU >= 5) ? 1 : 2;
+        uint4 bw[RING][TU][2];
+        auto load_base = [&](int n0, auto SL) {
+            constexpr int sl = decltype(SL)::value % RING;
+            const int n = n0 + c32;
+            const bool nok = n < R;
+            const uint16_t* row = a.base + (int64_t)(nok ? n : 0) * a.bs.rs + (int64_t)k * a.bs.ps;
+#pragma unroll
+            for (int u = 0; u < TU; ++u)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
+                    const bool in = nok && v0 + 8 <= V;
+                    const uint16_t* p = in ? row + v0 : reinterpret_cast<const uint16_t*>(kNegInfWords);
+                    bw[sl][u][c] = *reinterpret_cast<const uint4*>(p);
+                }
+        };
+        load_base(0, std::integral_constant<int, 0>{});
+
         // ---- the previous token of every request (drawn in this launch: wait
         // for it; the anchor or an earlier call's token: read it)
         lds_barrier();   // the previous position's readers of tokl are done
@@ -252,24 +278,7 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                                         : make_uint4(0, 0, 0, 0);
             }
         };
-        // base words of this lane's request: its two 8-column words of each unit
-        constexpr int RING = (TU >= 5) ? 1 : 2;
-        uint4 bw[RING][TU][2];
-        auto load_base = [&](int n0, auto SL) {
-            constexpr int sl = decltype(SL)::value % RING;
-            const int n = n0 + c32;
-            const bool nok = n < R;
-            const uint16_t* row = a.base + (int64_t)(nok ? n : 0) * a.bs.rs + (int64_t)k * a.bs.ps;
-#pragma unroll
-            for (int u = 0; u < TU; ++u)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
-                    load8_any<uint16_t, true>(row, v0, V, nok, v0 + 8 <= V, &bw[sl][u][c]);
-                }
-        };
         load_e(0);
-        load_base(0, std::integral_constant<int, 0>{});
 
         // one request block; SL (block parity) is the base-word ring slot
         auto block = [&](int b, auto SL) {
@@ -317,6 +326,11 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
 #pragma unroll
                     for (int j = 0; j < 16; ++j)
                         acc[u][j] = Logit<uint16_t>::raw_at(&bw[sl][u0 + u][j >> 3], j & 7) + acc[u][j];
+                // with one ring slot, the next block's words as soon as the last
+                // group has read this block's
+                if constexpr (RING == 1 && u1 == TU) {
+                    if (b + 1 < RB) load_base(n0 + kPassBlock, std::integral_constant<int, 0>{});
+                }
                 float m = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < nu; ++u)
@@ -383,9 +397,6 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 uint64_t* sp = slots + 2 * ((int64_t)n * n_t + tw);
                 dev_store_u64(sp, word);
                 dev_store_u64(sp + 1, word2);
-            }
-            if constexpr (RING == 1) {
-                if (b + 1 < RB) load_base(n0 + kPassBlock, std::integral_constant<int, 0>{});
             }
         };
         for (int b = 0; b < RB; b += 2) {

@@ -108,7 +108,10 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
     // this lane's target and draft words, its row statistics: two slots of each
     // up to four units per wave; at five the registers hold two slots of target
     // words but one of draft words, so the next block's draft words are requested
-    // after this block's epilogue
+    // after this block's epilogue.  Ordinary cached loads: the two lanes of a
+    // request read 32 bytes of a row per instruction and the next instruction the
+    // rest of its 64-byte segment, which a streaming load would fetch again (the
+    // words are whole 16-byte words of the row or read as -inf: V % 8 == 0 here)
     constexpr int RING = 2;                      // target words, statistics
     constexpr int RING_D = (TU >= 5) ? 1 : 2;    // draft words
     uint4 dw[RING_D][TU][2], xw[RING][TU][2];
@@ -122,7 +125,8 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
-                load8_any<uint16_t, true>(trow, v0, V, ok, v0 + 8 <= V, &xw[sl][u][c]);
+                const bool in = ok && v0 + 8 <= V;
+                xw[sl][u][c] = *reinterpret_cast<const uint4*>(in ? trow + v0 : reinterpret_cast<const uint16_t*>(kNegInfWords));
             }
         Md[sl] = ok ? (float)a.stats[2 * ((int64_t)n * gamma + m)] : 0.0f;
         invZd[sl] = ok ? (float)(1.0 / a.stats[2 * ((int64_t)n * gamma + m) + 1]) : 0.0f;
@@ -138,7 +142,8 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int v0 = v_tile + 32 * u + 16 * c + 8 * h;
-                load8_any<uint16_t, true>(drow, v0, V, ok, v0 + 8 <= V, &dw[sl][u][c]);
+                const bool in = ok && v0 + 8 <= V;
+                dw[sl][u][c] = *reinterpret_cast<const uint4*>(in ? drow + v0 : reinterpret_cast<const uint16_t*>(kNegInfWords));
             }
     };
     auto load_rows = [&](int n0, int n, int m, auto SL) {

@@ -307,18 +307,39 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 for (int u = 0; u < nu; ++u)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) acc[u][j] = 0.0f;
+                // LDS operands (the embedding fragment; the W2 fragments of LDS
+                // units) requested D k-steps ahead of their MFMAs and the order
+                // pinned per k-step: at one wave per SIMD nothing else hides an LDS
+                // read, and left to itself the compiler issues each one right before
+                // its MFMA.  The register units' fragments stay in AGPRs, read there
+                // by the MFMAs (no copies into VGPRs), which leaves the VGPRs for the
+                // prefetch (D = 2 would spill at five units).
+                constexpr bool kLds = u0 >= NR;
+                constexpr int D = (kLds && TU < 5) ? 2 : 1, S = D + 1;
+                uint4 pb[S];
+                uint4 pa[S][kLds ? nu : 1];
+                auto fetch = [&](int ks, int slot) {
+                    pb[slot] = *reinterpret_cast<const uint4*>(&L.e[c32][ks * kKStep + 8 * h]);
+                    if constexpr (kLds) {
+#pragma unroll
+                        for (int u = 0; u < nu; ++u)
+                            pa[slot][u] = L.w2[wave][u0 + u >= NR ? u0 + u - NR : 0][prow][w2_slot(prow, 2 * ks + h)];
+                    }
+                };
+#pragma unroll
+                for (int ks = 0; ks < D; ++ks) fetch(ks, ks);
 #pragma unroll
                 for (int ks = 0; ks < kKSteps; ++ks) {
-                    const bf16x8 bv =
-                        as_bf16x8(*reinterpret_cast<const uint4*>(&L.e[c32][ks * kKStep + 8 * h]));
+                    if (ks + D < kKSteps) fetch(ks + D, (ks + D) % S);
+                    const bf16x8 bv = as_bf16x8(pb[ks % S]);
 #pragma unroll
                     for (int u = 0; u < nu; ++u) {
                         const int uu = u0 + u;
-                        const bf16x8 av = (u0 < NR) ? afrag[uu < NR ? uu : 0][ks]
-                                                    : as_bf16x8(L.w2[wave][uu >= NR ? uu - NR : 0][prow]
-                                                                     [w2_slot(prow, 2 * ks + h)]);
+                        if constexpr (!kLds) asm volatile("" : "+a"(afrag[uu < NR ? uu : 0][ks]));
+                        const bf16x8 av = kLds ? as_bf16x8(pa[ks % S][kLds ? u : 0]) : afrag[uu < NR ? uu : 0][ks];
                         acc[u] = mfma32_bf16(av, bv, acc[u]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 // logits of the group's columns for this lane's request
 #pragma unroll

@@ -185,15 +185,33 @@ __global__ __launch_bounds__(256, 1) void resid_run_kernel(ResidArgs a)
         for (int u = 0; u < TU; ++u)
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[u][j] = 0.0f;
+        // LDS operands requested two k-steps ahead of their MFMAs and the order
+        // pinned per k-step (one wave per SIMD: nothing else hides an LDS read);
+        // the register units' fragments are read by the MFMAs from AGPRs
+        {
+            constexpr int NLU = TU - NR > 0 ? TU - NR : 1;
+            constexpr int D = 2, S = D + 1;
+            uint4 pb[S];
+            uint4 pa[S][NLU];
+            auto fetch = [&](int ks, int slot) {
+                pb[slot] = *reinterpret_cast<const uint4*>(&L.e[c32][ks * kKStep + 8 * h]);
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-            const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(&L.e[c32][ks * kKStep + 8 * h]));
+                for (int u = NR; u < TU; ++u)
+                    pa[slot][u - NR < NLU ? u - NR : 0] = L.w2[wave][u >= NR ? u - NR : 0][prow][w2_slot(prow, 2 * ks + h)];
+            };
 #pragma unroll
-            for (int u = 0; u < TU; ++u) {
-                const bf16x8 av = (u < NR) ? afrag[u < NR ? u : 0][ks]
-                                           : as_bf16x8(L.w2[wave][u >= NR ? u - NR : 0][prow]
-                                                            [w2_slot(prow, 2 * ks + h)]);
-                acc[u] = mfma32_bf16(av, bv, acc[u]);
+            for (int ks = 0; ks < D; ++ks) fetch(ks, ks);
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) {
+                if (ks + D < kKSteps) fetch(ks + D, (ks + D) % S);
+                const bf16x8 bv = as_bf16x8(pb[ks % S]);
+#pragma unroll
+                for (int u = 0; u < TU; ++u) {
+                    if (u < NR) asm volatile("" : "+a"(afrag[u < NR ? u : 0][ks]));
+                    const bf16x8 av = (u < NR) ? afrag[u < NR ? u : 0][ks] : as_bf16x8(pa[ks % S][u >= NR ? u - NR : 0]);
+                    acc[u] = mfma32_bf16(av, bv, acc[u]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // max(0, p - q) per column with the arithmetic of the streaming residual

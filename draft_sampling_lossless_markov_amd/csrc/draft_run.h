@@ -487,17 +487,13 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                     M = fmaxf(M, mt[i]);
                 }
                 M = block_max256(M, L.sh);
-                double ls = 0.0;
 #pragma unroll
-                for (int i = 0; i < PER; ++i) {
-                    sw[i] = sw[i] * rescale64(mt[i], M, a.inv_temp);
-                    ls += sw[i];
-                }
-                const double Z = block_sum256(ls, L.sh);
+                for (int i = 0; i < PER; ++i) sw[i] = sw[i] * rescale64(mt[i], M, a.inv_temp);
+                // the row total from the locating scan itself (target = u Z)
                 const double u = uniform24(a.seed, a.round, (uint32_t)n, (uint32_t)k, 0u);
+                double before, Z;
+                const int tsel = block_locate_u<PER>(sw, u, &Z, &before, L.sh, 0);
                 const double target = u * Z;
-                double before;
-                const int tsel = block_locate<PER>(sw, target, &before, L.sh, 0);
 
                 // rebuild the tile's 32 TU logits (thread t: column vt0 + t); the
                 // embedding row, the base logit and this wave's W2 fragments

@@ -570,9 +570,11 @@ __device__ __forceinline__ double block_sum256(double v, PickScratch& sh)
 // w[] holds the thread's weights (zeros past the end).  Returns the item and
 // the cumulative mass before it; falls back to the last positive item when
 // rounding leaves the target beyond the total.  slot: 0 or 1, one per call.
-template <int PER>
-__device__ __forceinline__ int block_locate(const double (&w)[PER], double target, double* before,
-                                            PickScratch& sh, int slot)
+// FROM_U: the target is u times the total, the total taken from the scan's own
+// wave sums (one block reduction fewer than summing first) and returned in *total.
+template <int PER, bool FROM_U>
+__device__ __forceinline__ int block_locate_impl(const double (&w)[PER], double target, double* before,
+                                                 PickScratch& sh, int slot, double* total)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     double ls = 0.0;
@@ -581,6 +583,11 @@ __device__ __forceinline__ int block_locate(const double (&w)[PER], double targe
     const double incl = wave_scan_d(ls);
     if (lane == kWave - 1) sh.scan[slot][wave] = incl;
     lds_barrier();
+    if constexpr (FROM_U) {
+        const double z = (sh.scan[slot][0] + sh.scan[slot][1]) + (sh.scan[slot][2] + sh.scan[slot][3]);
+        *total = z;
+        target *= z;
+    }
     double off = 0.0;
     for (int w2 = 0; w2 < wave; ++w2) off += sh.scan[slot][w2];
     const double c0 = off + incl - ls;
@@ -628,6 +635,21 @@ __device__ __forceinline__ int block_locate(const double (&w)[PER], double targe
     lds_barrier();
     *before = (l >= 0) ? sh.fb[slot] : 0.0;
     return l < 0 ? 0 : l;
+}
+
+template <int PER>
+__device__ __forceinline__ int block_locate(const double (&w)[PER], double target, double* before,
+                                            PickScratch& sh, int slot)
+{
+    return block_locate_impl<PER, false>(w, target, before, sh, slot, nullptr);
+}
+
+// The same with the target u * Z, Z the weights' total (returned in *Z).
+template <int PER>
+__device__ __forceinline__ int block_locate_u(const double (&w)[PER], double u, double* Z, double* before,
+                                              PickScratch& sh, int slot)
+{
+    return block_locate_impl<PER, true>(w, u, before, sh, slot, Z);
 }
 
 

@@ -138,6 +138,7 @@ struct RunLds {
     uint16_t e_row[kRankMax];                          // the picked request's embedding row
     int32_t tokl[kRunReqMax];                          // previous tokens of every request
     PickScratch sh;
+    uint64_t pw[2][kPassBlock][4][2];   // a block's words per (request, wave), stored by the workgroup
 };
 
 // The wave's W2 units (the 32 TU columns from v_tile): units 0 .. NR-1 into
@@ -280,11 +281,28 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
         };
         load_e(0);
 
+        // A block's words are staged in LDS by each wave and stored by the
+        // workgroup after the next barrier: thread t writes request n0 + t / 4's
+        // pair of tile 4 blockIdx.x + t % 4, so that a request's four tiles (64
+        // contiguous bytes) leave together instead of as four scattered 16-byte
+        // stores (each written through at a whole segment's cost)
+        auto store_words = [&](int n0, int par) {
+            if (tid < 4 * kPassBlock) {
+                const int nl = tid >> 2, j = tid & 3;
+                const int n = n0 + nl, t = 4 * (int)blockIdx.x + j;
+                if (n < R && t < n_t) {
+                    uint64_t* sp = slots + 2 * ((int64_t)n * n_t + t);
+                    dev_store_u64(sp, L.pw[par][nl][j][0]);
+                    dev_store_u64(sp + 1, L.pw[par][nl][j][1]);
+                }
+            }
+        };
         // one request block; SL (block parity) is the base-word ring slot
         auto block = [&](int b, auto SL) {
             constexpr int sl = decltype(SL)::value % RING;
             const int n0 = b * kPassBlock;
             lds_barrier();   // the previous block's embedding tile is read
+            if (b > 0) store_words(n0 - kPassBlock, (b - 1) & 1);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 *reinterpret_cast<uint4*>(&L.e[srow][(sq * 4 + c) * 8]) = eu[c];
@@ -413,17 +431,17 @@ __global__ __launch_bounds__(256, 1) void draft_run_kernel(RunArgs a)
                 word = pack2(m, 0u);
                 word2 = (uint64_t)__double_as_longlong(sum);
             }
-            const int n = n0 + c32;
-            if (h == 0 && n < R && tw < n_t) {
-                uint64_t* sp = slots + 2 * ((int64_t)n * n_t + tw);
-                dev_store_u64(sp, word);
-                dev_store_u64(sp + 1, word2);
+            if (h == 0) {
+                L.pw[b & 1][c32][wave][0] = word;
+                L.pw[b & 1][c32][wave][1] = word2;
             }
         };
         for (int b = 0; b < RB; b += 2) {
             block(b, std::integral_constant<int, 0>{});
             if (b + 1 < RB) block(b + 1, std::integral_constant<int, 1>{});
         }
+        lds_barrier();
+        store_words((RB - 1) * kPassBlock, (RB - 1) & 1);
 
         // ================= phase 2: one workgroup per request ==================
         for (int n = blockIdx.x; n < R; n += G) {

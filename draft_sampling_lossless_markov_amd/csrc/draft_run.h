@@ -6,7 +6,7 @@
 // every position dominates the traffic of a small batch, so this kernel reads it
 // once per call: one workgroup per CU (all resident at once: the grid has at most
 // one per CU and the kernel's registers and LDS admit exactly one), each
-// holding its slice of W2 on chip -- three 32-column units per wave in VGPRs as
+// holding its slice of W2 on chip -- three 32-column units per wave in registers as
 // MFMA fragments and up to two in LDS.  Per position:
 //   phase 1 (every workgroup): the previous tokens of all requests, then per
 //     32-request block the bias by MFMA from the resident slice plus the base
@@ -40,7 +40,7 @@
 namespace dsp {
 
 constexpr int kRunUnitsMax = 5;      // 32-column units per wave (one tile per wave)
-constexpr int kRunRegUnits = 3;      // units held in VGPRs; the rest in LDS
+constexpr int kRunRegUnits = 3;      // units held in registers (AGPRs); the rest in LDS
 constexpr int kRunTilesMax = 1024;   // tiles of one launch (four per workgroup)
 constexpr int kRunReqMax = 2048;     // requests of one launch (their tokens sit in LDS)
 constexpr unsigned kRunSpinLimit = 1u << 22;
